@@ -1,0 +1,388 @@
+"""Plain CPU oracle for the forward pass of a top-k routed MoE layer.
+
+This is test infrastructure only. The tests, the smoke check and the
+benchmark's CPU-baseline leg may use it. The GPU path never imports or calls
+it, and it imports nothing from the GPU path.
+
+Everything is computed in numpy float64. Inputs that are bf16 or fp32 in
+storage are upcast exactly by the caller. Each function states the passage
+it follows. The main source is the layer in "混合专家 MoE" (anrans
+ai-infra handbook):
+
+* section "结构": structure and the output formula;
+* section "实现：逐 token 与按专家分组": ``moe.py``, with ``route``,
+  ``forward_naive`` and ``forward_grouped``;
+* section "负载均衡": ``aux_loss`` and the bias used only for selection.
+
+Capacity dropping follows the notes "混合专家模型 (MoE)：大规模稀疏条件计算的
+架构与工程实践", section 三.1 "容量因子 (Capacity Factor) 与 Token 丢弃策略".
+
+Readings where the pages are silent:
+
+* top-k order: larger score first; equal scores go to the lower expert index;
+* capacity: copies compete in copy order c = t*k + j;
+* the bf16 rounding point: only the SwiGLU intermediate h, and only for bf16
+  layers.
+
+What pins each function (in tests/test_oracle_*.py):
+
+* softmax: row sums, the E=1 and equal-logit closed forms, and
+  scipy.special.softmax;
+* top-k: brute force from the counting definition on small inputs with
+  planted ties;
+* renormalise: sums to 1, k=1 gives 1, k=E gives p, and the printed
+  0.62/0.38 figure;
+* grouping: bincount and numpy's stable sort; a per-copy brute force of
+  capacity; the C >= N*k and C = 0 special cases;
+* experts: the per-token form equals the grouped form; E=1, k=1 equals a
+  dense SwiGLU FFN built from torch.nn.functional;
+* balance statistic: uniform gives 1, one-hot gives E, and the handbook's
+  skewed case gives exactly 4;
+* bf16_round: nearest-value brute force over every bf16 pattern, and torch's
+  fp32 -> bf16 cast.
+
+Parity unpinned: y on general random inputs has no printed value on any page.
+It rests on the special cases above and on the per-token and grouped forms
+agreeing.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Callable, Optional, Sequence
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ---------------------------------------------------------------- rounding
+
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def bf16_round(a) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits. The smallest normal is 2^-126, and
+    below it the spacing is fixed at 2^-133. Values that round past the
+    largest finite bf16 become +-inf. The result is returned as float64.
+    """
+    a = np.asarray(a, dtype=F64)
+    _, e = np.frexp(a)                  # a = m * 2^e with 0.5 <= |m| < 1
+    e = np.maximum(e, -125)             # fixed spacing in the subnormal range
+    q = np.rint(np.ldexp(a, 8 - e))     # integer count of spacings; rint ties to even
+    r = np.ldexp(q, e - 8)
+    big = np.abs(r) > _BF16_MAX
+    if np.any(big):
+        r = np.where(big, np.copysign(np.inf, a), r)
+    return r
+
+
+# ---------------------------------------------------------------- router
+
+def softmax(logits: np.ndarray) -> np.ndarray:
+    """Row softmax in float64: p_e = exp(l_e - max) / sum_e' exp(l_e' - max).
+
+    This is ``probs = self.router(x).softmax(dim=-1)`` in ``route`` ("实现"
+    section). Subtracting the row maximum changes no value mathematically.
+    """
+    l = np.asarray(logits, dtype=F64)
+    z = np.exp(l - l.max(axis=-1, keepdims=True))
+    return z / z.sum(axis=-1, keepdims=True)
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray,
+                  logit_bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """l[t, e] = x[t] . W_r[e] (+ logit_bias[e]).
+
+    The router is ``nn.Linear(d, E, bias=False)``, so y = x W_r^T. The
+    optional additive bias is the gate ``nn.Linear(input_dim, num_experts)``
+    (with bias) in MoEGating on the cloud.baidu.com overview of MoE. It also
+    carries the Zipf-like skew of the capacity workload.
+    """
+    l = np.asarray(x, dtype=F64) @ np.asarray(w_router, dtype=F64).T
+    if logit_bias is not None:
+        l = l + np.asarray(logit_bias, dtype=F64)[None, :]
+    return l
+
+
+def topk_order(scores: np.ndarray, k: int) -> np.ndarray:
+    """idx[t, :k]: the k largest scores of row t, largest first.
+
+    Order: a larger score ranks first, and equal scores rank the lower expert
+    index first. A stable sort of -s gives exactly this order (library sort
+    as one step).
+    """
+    s = np.asarray(scores, dtype=F64)
+    order = np.argsort(-s, axis=-1, kind="stable")
+    return order[..., :k].astype(np.int64)
+
+
+@dataclass
+class Routing:
+    idx: np.ndarray       # [N, k] int64, expert ids, best first
+    w: np.ndarray         # [N, k] float64 combine weights
+    probs: np.ndarray     # [N, E] float64 softmax (without the selection bias)
+    gap: np.ndarray       # [N] float64: s_(k) - s_(k+1) (inf when k == E)
+
+
+def route(x, w_router, k: int, logit_bias=None, select_bias=None,
+          renormalize: bool = True) -> Routing:
+    """Router of the layer: linear, softmax, (selection bias), top-k, renormalise.
+
+    Follows ``route`` ("实现" section): ``probs = softmax(router(x))``,
+    ``weights, idx = probs.topk(k)``, ``weights /= weights.sum()``.
+
+    The selection-only bias comes from the aux-loss-free balancing bullet of
+    the "负载均衡" section: the bias is added to the scores used to choose the
+    top-k and does not change the weights. So the weights are always taken
+    from the unbiased p.
+    """
+    p = softmax(router_logits(x, w_router, logit_bias))
+    s = p if select_bias is None else p + np.asarray(select_bias, dtype=F64)[None, :]
+    idx = topk_order(s, k)
+    w = np.take_along_axis(p, idx, axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    E = p.shape[1]
+    if k < E:
+        srt = -np.sort(-s, axis=1)
+        gap = srt[:, k - 1] - srt[:, k]
+    else:
+        gap = np.full(p.shape[0], np.inf)
+    return Routing(idx=idx, w=w, probs=p, gap=gap)
+
+
+# ---------------------------------------------------------------- grouping
+
+def expert_counts(idx: np.ndarray, n_experts: int) -> np.ndarray:
+    """counts[e] = number of (token, slot) copies routed to e, before capacity.
+
+    ``torch.bincount(flat_expert, minlength=E)`` in ``forward_grouped``.
+    """
+    counts = np.zeros(n_experts, dtype=np.int64)
+    for e in np.asarray(idx).reshape(-1):
+        counts[int(e)] += 1
+    return counts
+
+
+def capacity_keep(idx: np.ndarray, n_experts: int, capacity: int) -> np.ndarray:
+    """keep[c] for every copy c = t*k + j: does it fit in its expert's buffer?
+
+    Follows the token-dropping rule in section 三.1 of the notes: each expert
+    has a static buffer of ``capacity`` rows, and the copies beyond it skip
+    every expert branch. The pages do not say which copies overflow. Here
+    copies take their places in copy order, so a copy is kept iff fewer than
+    C earlier copies went to the same expert. capacity <= 0 means no limit.
+    """
+    flat = np.asarray(idx).reshape(-1)
+    keep = np.ones(flat.shape[0], dtype=bool)
+    if capacity <= 0:
+        return keep
+    fill = np.zeros(n_experts, dtype=np.int64)
+    for c, e in enumerate(flat):
+        e = int(e)
+        if fill[e] < capacity:
+            fill[e] += 1
+        else:
+            keep[c] = False
+    return keep
+
+
+@dataclass
+class Grouping:
+    counts: np.ndarray    # [E] routed copies per expert (before capacity)
+    kept: np.ndarray      # [E] copies that fit the capacity
+    offsets: np.ndarray   # [E+1] exclusive prefix sum of kept
+    perm: np.ndarray      # [sum kept] copy ids grouped by expert, increasing within a group
+    slot_pos: np.ndarray  # [N*k] row of each copy in perm, -1 if dropped
+
+
+def group(idx: np.ndarray, n_experts: int, capacity: int = 0) -> Grouping:
+    """Sort the token copies by expert: count, capacity, prefix sum, permutation.
+
+    ``forward_grouped`` ("实现" section) flattens idx, takes a stable argsort
+    by expert, and walks the segments with a running start. That section
+    also names the histogram and the prefix sum of starts. Dropped copies are
+    left out of their segment.
+    """
+    flat = np.asarray(idx).reshape(-1).astype(np.int64)
+    counts = expert_counts(idx, n_experts)
+    keep = capacity_keep(idx, n_experts, capacity)
+    order = np.argsort(flat, kind="stable")           # copies sorted by (expert, copy id)
+    perm = order[keep[order]]
+    kept = np.zeros(n_experts, dtype=np.int64)
+    for c in perm:
+        kept[flat[c]] += 1
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    slot_pos = np.full(flat.shape[0], -1, dtype=np.int64)
+    slot_pos[perm] = np.arange(perm.shape[0])
+    return Grouping(counts=counts, kept=kept, offsets=offsets, perm=perm, slot_pos=slot_pos)
+
+
+# ---------------------------------------------------------------- experts
+
+def silu(z) -> np.ndarray:
+    """silu(z) = z / (1 + exp(-z)) (``F.silu`` in the Expert module)."""
+    z = np.asarray(z, dtype=F64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(X, w_gate, w_up, w_down, round_h: bool) -> np.ndarray:
+    """Expert(x) = down(silu(gate(x)) * up(x)) for the rows of X.
+
+    This is ``Expert.forward`` ("实现" section). gate_proj and up_proj are
+    ``nn.Linear(d, d_ff)``, so their weights are [d_ff, d]. down_proj is
+    ``nn.Linear(d_ff, d)``, with weight [d, d_ff]. In bf16 layers the
+    intermediate h is rounded to bf16 before the down projection.
+    """
+    X = np.atleast_2d(np.asarray(X, dtype=F64))
+    g = X @ np.asarray(w_gate, dtype=F64).T
+    u = X @ np.asarray(w_up, dtype=F64).T
+    h = silu(g) * u
+    if round_h:
+        h = bf16_round(h)
+    return h @ np.asarray(w_down, dtype=F64).T
+
+
+WeightSet = Sequence  # indexable by expert id -> 2-D array (converted to float64 on use)
+
+
+def forward_per_token(x, idx, w, keep, w_gate: WeightSet, w_up: WeightSet, w_down: WeightSet,
+                      shared=None, round_h: bool = False, rows=None) -> np.ndarray:
+    """The per-token form: y_t = sum_j w[t,j] Expert_{idx[t,j]}(x_t) + sum_s Shared_s(x_t).
+
+    Follows ``forward_naive`` ("实现" section) and the output formula in
+    section "结构". Each kept copy is one matrix-vector expert application on
+    one token row. A dropped copy adds nothing. The layer returns no residual:
+    section 三.1 of the notes sends dropped tokens through the residual path,
+    which lies outside the layer. Shared experts have no gate and weight 1 on
+    every token ("结构", DeepSeekMoE's second point).
+
+    ``shared`` is None or a tuple (s_gate, s_up, s_down) of weight sets.
+    ``rows`` restricts the output to those token rows (all rows if None).
+    """
+    x = np.asarray(x, dtype=F64)
+    N = x.shape[0]
+    k = idx.shape[1]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    keep = np.asarray(keep).reshape(N, k)
+    cache = {}
+
+    def weights(e):
+        if e not in cache:
+            cache[e] = (np.asarray(w_gate[e], dtype=F64), np.asarray(w_up[e], dtype=F64),
+                        np.asarray(w_down[e], dtype=F64))
+        return cache[e]
+
+    out = np.zeros((rows.shape[0], x.shape[1]), dtype=F64)
+    for i, t in enumerate(rows):
+        for j in range(k):
+            if not keep[t, j]:
+                continue
+            e = int(idx[t, j])
+            out[i] += w[t, j] * swiglu_expert(x[t], *weights(e), round_h=round_h)[0]
+        if shared is not None:
+            sg, su, sd = shared
+            for s in range(len(sg)):
+                out[i] += swiglu_expert(x[t], sg[s], su[s], sd[s], round_h=round_h)[0]
+    return out
+
+
+def forward_grouped(x, idx, w, grouping: Grouping, w_gate: WeightSet, w_up: WeightSet,
+                    w_down: WeightSet, shared=None, round_h: bool = False) -> np.ndarray:
+    """The grouped form: one matrix product per expert over its segment.
+
+    Follows ``forward_grouped`` ("实现" section). The segment of expert e is
+    ``perm[offsets[e]:offsets[e+1]]``, and its token ids are c // k. Each
+    segment with at least one row runs the expert once over all of its rows.
+    The result is added back at the tokens, scaled by their weights. Empty
+    segments are skipped, as that section's second exercise requires.
+    """
+    x = np.asarray(x, dtype=F64)
+    N, k = idx.shape
+    out = np.zeros_like(x)
+    wf = np.asarray(w, dtype=F64).reshape(-1)
+    E = grouping.offsets.shape[0] - 1
+    for e in range(E):
+        a, b = int(grouping.offsets[e]), int(grouping.offsets[e + 1])
+        if a == b:
+            continue
+        sel = grouping.perm[a:b]
+        tok = sel // k
+        y = swiglu_expert(x[tok], w_gate[e], w_up[e], w_down[e], round_h=round_h)
+        np.add.at(out, tok, y * wf[sel][:, None])
+    if shared is not None:
+        sg, su, sd = shared
+        for s in range(len(sg)):
+            out += swiglu_expert(x, sg[s], su[s], sd[s], round_h=round_h)
+    return out
+
+
+# ---------------------------------------------------------------- statistic
+
+def balance_stat(counts, prob_sum, n_tokens: int, top_k: int) -> float:
+    """E * sum_e f_e P_e, the load-balancing statistic.
+
+    This is ``aux_loss`` ("负载均衡" section), written there as
+    E * sum_i f_i P_i:
+
+    * f_e = counts_e / (N*k), the share of the copies; ``idx.numel()`` is N*k;
+    * P_e = prob_sum_e / N, the mean router probability.
+
+    counts are the routed copies before capacity.
+    """
+    counts = np.asarray(counts, dtype=F64)
+    prob_sum = np.asarray(prob_sum, dtype=F64)
+    E = counts.shape[0]
+    f = counts / float(n_tokens * top_k)
+    P = prob_sum / float(n_tokens)
+    return float(E * np.sum(f * P))
+
+
+# ---------------------------------------------------------------- whole layer
+
+@dataclass
+class LayerResult:
+    routing: Routing
+    grouping: Grouping
+    prob_sum: np.ndarray
+    stat: float
+    y: Optional[np.ndarray]
+
+
+def moe_layer(x, w_router, w_gate, w_up, w_down, k: int, *, shared=None, logit_bias=None,
+              select_bias=None, capacity: int = 0, renormalize: bool = True,
+              round_h: bool = False, form: str = "per_token", rows=None,
+              forced_idx: Optional[np.ndarray] = None) -> LayerResult:
+    """Route, group, run the experts and combine, in the pages' order.
+
+    With ``forced_idx`` set, routing still computes p, but the expert choice
+    comes from the given idx. The weights are then p at those experts,
+    renormalised the same way. This forced-routing mode lets each later step
+    be checked on a given choice of experts. ``form`` is "per_token" (the
+    authority), "grouped", or "none" to skip the experts.
+    """
+    r = route(x, w_router, k, logit_bias, select_bias, renormalize)
+    if forced_idx is not None:
+        idx = np.asarray(forced_idx, dtype=np.int64)
+        wv = np.take_along_axis(r.probs, idx, axis=1)
+        if renormalize:
+            wv = wv / wv.sum(axis=1, keepdims=True)
+        r = Routing(idx=idx, w=wv, probs=r.probs, gap=r.gap)
+    E = r.probs.shape[1]
+    g = group(r.idx, E, capacity)
+    prob_sum = r.probs.sum(axis=0)
+    stat = balance_stat(g.counts, prob_sum, r.idx.shape[0], k)
+    y = None
+    if form == "per_token":
+        y = forward_per_token(x, r.idx, r.w, g.slot_pos >= 0, w_gate, w_up, w_down,
+                              shared=shared, round_h=round_h, rows=rows)
+    elif form == "grouped":
+        y = forward_grouped(x, r.idx, r.w, g, w_gate, w_up, w_down, shared=shared,
+                            round_h=round_h)
+        if rows is not None:
+            y = y[np.asarray(rows)]
+    return LayerResult(routing=r, grouping=g, prob_sum=prob_sum, stat=stat, y=y)

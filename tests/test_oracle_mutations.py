@@ -1,0 +1,114 @@
+"""Plant plausible mistakes in the oracle and check that a pin catches each one.
+
+Every mutation is applied to the CPU oracle only, with monkeypatch, and
+undone after the test.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+import test_oracle_pins as pins
+
+F64 = np.float64
+
+
+def _fails(fn):
+    with pytest.raises(AssertionError):
+        fn()
+
+
+def test_tie_break_to_higher_index_is_caught(monkeypatch):
+    def bad(scores, k):
+        s = np.asarray(scores, dtype=F64)
+        E = s.shape[-1]
+        rev = np.argsort(-s[..., ::-1], axis=-1, kind="stable")  # ties -> higher index
+        return (E - 1 - rev)[..., :k]
+    monkeypatch.setattr(O, "topk_order", bad)
+    _fails(pins.test_topk_bruteforce_exhaustive_with_ties)
+
+
+def test_gate_up_swapped_is_caught(monkeypatch):
+    orig = O.swiglu_expert
+    monkeypatch.setattr(O, "swiglu_expert", lambda X, g, u, d, round_h: orig(X, u, g, d, round_h))
+    _fails(pins.test_e1_k1_is_dense_swiglu_ffn)
+
+
+def test_transposed_down_is_caught(monkeypatch):
+    def bad(X, g, u, d, round_h):
+        X = np.atleast_2d(np.asarray(X, dtype=F64))
+        h = O.silu(X @ np.asarray(g, F64).T) * (X @ np.asarray(u, F64).T)
+        dd = np.asarray(d, F64)
+        return h @ (dd if dd.shape[0] == dd.shape[1] else dd.T)  # wrong when square
+    monkeypatch.setattr(O, "swiglu_expert", bad)
+
+    def square_case():
+        rng = np.random.default_rng(0)
+        x = rng.standard_normal((9, 16))
+        wg, wu, wd, _ = pins.rand_layer(rng, 1, 16, 16)
+        y = O.moe_layer(x, rng.standard_normal((1, 16)), wg, wu, wd, 1).y
+        np.testing.assert_allclose(y, pins.torch_swiglu(x, wg[0], wu[0], wd[0]), rtol=1e-12)
+    _fails(square_case)
+
+
+def test_fraction_over_tokens_is_caught(monkeypatch):
+    def bad(counts, prob_sum, n_tokens, top_k):
+        c, p = np.asarray(counts, F64), np.asarray(prob_sum, F64)
+        return float(c.shape[0] * np.sum(c / n_tokens * p / n_tokens))
+    monkeypatch.setattr(O, "balance_stat", bad)
+    _fails(pins.test_balance_stat_uniform_probs_is_one)
+
+
+def test_dropped_shared_term_is_caught(monkeypatch):
+    orig = O.forward_per_token
+    monkeypatch.setattr(O, "forward_per_token",
+                        lambda *a, shared=None, **kw: orig(*a, shared=None, **kw))
+    _fails(pins.test_shared_expert_adds_dense_ffn)
+
+
+def test_missing_renormalisation_is_caught(monkeypatch):
+    orig = O.route
+    monkeypatch.setattr(O, "route", lambda x, W, k, logit_bias=None, select_bias=None, renormalize=True:
+                        orig(x, W, k, logit_bias, select_bias, False))
+    _fails(pins.test_renormalised_weights_sum_to_one_and_special_k)
+
+
+def test_capacity_keeping_last_copies_is_caught(monkeypatch):
+    def bad(idx, E, C):
+        flat = np.asarray(idx).reshape(-1)
+        keep = np.ones(flat.shape[0], dtype=bool)
+        if C <= 0:
+            return keep
+        for e in range(E):
+            where = np.nonzero(flat == e)[0]
+            keep[where[: max(0, len(where) - C)]] = False  # keeps the last C
+        return keep
+    monkeypatch.setattr(O, "capacity_keep", bad)
+    _fails(lambda: pins.test_capacity_bruteforce(2))
+
+
+def test_softmax_without_exp_is_caught(monkeypatch):
+    def bad(l):
+        l = np.asarray(l, F64) - np.min(l, axis=-1, keepdims=True)
+        return l / l.sum(axis=-1, keepdims=True)
+    monkeypatch.setattr(O, "softmax", bad)
+    _fails(pins.test_softmax_matches_scipy_and_sums_to_one)
+
+
+def test_weights_from_biased_scores_is_caught(monkeypatch):
+    def bad(x, W, k, logit_bias=None, select_bias=None, renormalize=True):
+        p = O.softmax(O.router_logits(x, W, logit_bias))
+        s = p if select_bias is None else p + np.asarray(select_bias)[None, :]
+        idx = O.topk_order(s, k)
+        w = np.take_along_axis(s, idx, axis=1)  # weights from the biased score: wrong
+        return O.Routing(idx=idx, w=w, probs=p, gap=np.zeros(p.shape[0]))
+    monkeypatch.setattr(O, "route", bad)
+    _fails(pins.test_selection_bias_picks_but_does_not_weight)
+
+
+def test_bf16_truncation_is_caught(monkeypatch):
+    def bad(a):
+        a = np.asarray(a, F64)
+        m, e = np.frexp(a)
+        return np.ldexp(np.trunc(m * 256) / 256, e)
+    monkeypatch.setattr(O, "bf16_round", bad)
+    _fails(pins.test_bf16_round_matches_torch_on_fp32)

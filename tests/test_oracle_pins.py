@@ -1,0 +1,379 @@
+"""Pins of the CPU oracle against what the MoE pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a value
+the pages print, a closed form, an invariant, a library routine for a
+special case, or brute force on tiny inputs. Section names refer to
+"混合专家 MoE" (anrans ai-infra handbook) unless stated otherwise.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                key, v = line.split("=")
+                vals[key] = float(v)
+    return vals
+
+
+def rand_layer(rng, E, d, f, S=0):
+    wg = rng.standard_normal((E, f, d)) / math.sqrt(d)
+    wu = rng.standard_normal((E, f, d)) / math.sqrt(d)
+    wd = rng.standard_normal((E, d, f)) / math.sqrt(f)
+    shared = None
+    if S:
+        shared = (rng.standard_normal((S, f, d)) / math.sqrt(d),
+                  rng.standard_normal((S, f, d)) / math.sqrt(d),
+                  rng.standard_normal((S, d, f)) / math.sqrt(f))
+    return wg, wu, wd, shared
+
+
+# ------------------------------------------------------------------ softmax
+
+def test_softmax_matches_scipy_and_sums_to_one():
+    rng = np.random.default_rng(1)
+    l = rng.standard_normal((40, 13)) * 5
+    p = O.softmax(l)
+    np.testing.assert_allclose(p, scipy.special.softmax(l, axis=1), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+
+
+def test_softmax_closed_forms():
+    # E = 1: p = 1 exactly. Equal logits: p = 1/E (exact for E a power of two).
+    assert np.all(O.softmax(np.array([[3.7], [-2.0]])) == 1.0)
+    for E in (2, 8, 256):
+        p = O.softmax(np.zeros((3, E)))
+        assert np.all(p == 1.0 / E)
+    # a zero router gives equal logits
+    x = np.random.default_rng(0).standard_normal((5, 16))
+    assert np.all(O.softmax(O.router_logits(x, np.zeros((8, 16)))) == 1.0 / 8)
+
+
+def test_router_logits_is_linear_layer():
+    # nn.Linear(d, E, bias=False) gives x W^T; the optional bias enters additively
+    rng = np.random.default_rng(2)
+    x, W, b = rng.standard_normal((7, 12)), rng.standard_normal((5, 12)), rng.standard_normal(5)
+    ref = torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(W), torch.from_numpy(b))
+    np.testing.assert_allclose(O.router_logits(x, W, b), ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------ top-k
+
+def topk_bruteforce(s, k):
+    """The counting definition: rank_e = #{e': s_e' > s_e or (s_e' == s_e and e' < e)}."""
+    E = len(s)
+    rank = [sum(1 for f in range(E) if s[f] > s[e] or (s[f] == s[e] and f < e)) for e in range(E)]
+    chosen = sorted((r, e) for e, r in enumerate(rank) if r < k)
+    return [e for _, e in chosen]
+
+
+def test_topk_bruteforce_exhaustive_with_ties():
+    # every score vector over a 3-level alphabet for E <= 5 (exact ties planted), all k
+    levels = [0.0, 0.25, 0.5]
+    for E in range(1, 6):
+        rows = np.array(list(itertools.product(levels, repeat=E)))
+        for k in range(1, E + 1):
+            got = O.topk_order(rows, k)
+            for r, g in zip(rows, got):
+                assert list(g) == topk_bruteforce(list(r), k)
+
+
+def test_topk_random_e8_k3():
+    rng = np.random.default_rng(3)
+    s = rng.integers(0, 4, size=(500, 8)).astype(float) / 4  # many ties
+    got = O.topk_order(s, 3)
+    for r, g in zip(s, got):
+        assert list(g) == topk_bruteforce(list(r), 3)
+
+
+def test_selection_bias_picks_but_does_not_weight():
+    # "负载均衡": the bias only changes which experts are chosen, not their weights
+    rng = np.random.default_rng(4)
+    x, W = rng.standard_normal((30, 16)), rng.standard_normal((8, 16)) * 0.2
+    b = np.zeros(8)
+    b[7] = 10.0  # expert 7 always chosen
+    r = O.route(x, W, 2, select_bias=b, renormalize=False)
+    assert np.all(r.idx[:, 0] == 7)
+    p = O.softmax(O.router_logits(x, W))
+    np.testing.assert_array_equal(r.w[:, 0], p[:, 7])
+
+
+# ------------------------------------------------------------------ weights
+
+def test_renormalised_weights_sum_to_one_and_special_k():
+    rng = np.random.default_rng(5)
+    x, W = rng.standard_normal((64, 32)), rng.standard_normal((8, 32))
+    for k in (1, 2, 3, 8):
+        r = O.route(x, W, k)
+        np.testing.assert_allclose(r.w.sum(axis=1), 1.0, rtol=0, atol=4e-16)
+        if k == 1:
+            assert np.all(r.w == 1.0)
+        if k == 8:  # dense-output mixture: all experts, weights = p
+            np.testing.assert_allclose(np.take_along_axis(r.probs, r.idx, 1), r.w, rtol=1e-15)
+            np.testing.assert_allclose(np.sort(r.idx, axis=1), np.tile(np.arange(8), (64, 1)))
+
+
+def test_router_figure_weights():
+    g = read_golden("router_figure.txt")
+    E = int(g["n_experts"])
+    p = np.array([0.31, 0.05, 0.07, 0.19, 0.08, 0.1, 0.12, 0.08])  # two selected carry 0.31 : 0.19
+    r = O.route(np.ones((1, 1)), np.log(p)[:, None], int(g["top_k"]))  # logits = log p
+    assert list(r.idx[0]) == [0, 3]
+    np.testing.assert_allclose(r.w[0], [g["w0"], g["w1"]], rtol=1e-14)
+
+
+# ------------------------------------------------------------------ grouping / capacity
+
+def test_counts_perm_offsets_against_library_sort():
+    rng = np.random.default_rng(6)
+    N, k, E = 200, 3, 11
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(N)])
+    g = O.group(idx, E, 0)
+    np.testing.assert_array_equal(g.counts, np.bincount(idx.ravel(), minlength=E))
+    assert g.counts.sum() == N * k
+    np.testing.assert_array_equal(g.perm, np.argsort(idx.ravel(), kind="mergesort"))
+    np.testing.assert_array_equal(g.offsets, np.concatenate([[0], np.cumsum(g.counts)]))
+    assert np.all(g.slot_pos[g.perm] == np.arange(N * k))
+
+
+def capacity_bruteforce(idx, E, C):
+    """keep copy c iff #{c' < c : expert(c') == expert(c)} < C."""
+    flat = idx.ravel()
+    return np.array([np.sum(flat[:c] == flat[c]) < C for c in range(len(flat))])
+
+
+@pytest.mark.parametrize("C", [1, 2, 5, 17])
+def test_capacity_bruteforce(C):
+    rng = np.random.default_rng(7 + C)
+    N, k, E = 60, 2, 5
+    p = np.array([0.5, 0.2, 0.15, 0.1, 0.05])
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(N)])
+    g = O.group(idx, E, C)
+    keep = capacity_bruteforce(idx, E, C)
+    np.testing.assert_array_equal(g.slot_pos >= 0, keep)
+    np.testing.assert_array_equal(g.kept, np.minimum(g.counts, C))
+    assert g.kept.sum() + np.sum(~keep) == N * k
+    for e in range(E):  # each segment lists its kept copies in increasing copy id
+        seg = g.perm[g.offsets[e]:g.offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0) and np.all(idx.ravel()[seg] == e)
+
+
+def test_capacity_special_cases():
+    rng = np.random.default_rng(8)
+    N, k, E, d, f = 24, 2, 4, 16, 16
+    x = rng.standard_normal((N, d))
+    Wr = rng.standard_normal((E, d))
+    wg, wu, wd, shared = rand_layer(rng, E, d, f, S=1)
+    base = O.moe_layer(x, Wr, wg, wu, wd, k, shared=shared, capacity=0)
+    big = O.moe_layer(x, Wr, wg, wu, wd, k, shared=shared, capacity=N * k)
+    np.testing.assert_array_equal(base.y, big.y)
+    np.testing.assert_array_equal(base.grouping.perm, big.grouping.perm)
+    # C = 0 is "no limit" in the ABI; a buffer of 1 with every token on one expert keeps one copy
+    one = O.group(np.zeros((N, 1), dtype=int), E, 1)
+    assert one.kept.tolist() == [1, 0, 0, 0] and one.perm.tolist() == [0]
+    # everything dropped: y is the shared expert alone
+    lr = O.moe_layer(x, Wr, wg, wu, wd, 1, shared=shared, forced_idx=np.zeros((N, 1), int),
+                     capacity=1)
+    only_shared = O.swiglu_expert(x, shared[0][0], shared[1][0], shared[2][0], False)
+    np.testing.assert_allclose(lr.y[1:], only_shared[1:], rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------ experts
+
+def torch_swiglu(x, g, u, d):
+    F = torch.nn.functional
+    tx = torch.from_numpy(x)
+    return F.linear(F.silu(F.linear(tx, torch.from_numpy(g))) * F.linear(tx, torch.from_numpy(u)),
+                    torch.from_numpy(d)).numpy()
+
+
+def test_silu_matches_libraries():
+    z = np.linspace(-40, 40, 2001)
+    np.testing.assert_allclose(O.silu(z), z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(O.silu(z), torch.nn.functional.silu(torch.from_numpy(z)).numpy(),
+                               rtol=1e-14, atol=1e-300)
+
+
+def test_e1_k1_is_dense_swiglu_ffn():
+    # one expert, top-1: the MoE layer is the dense FFN it replaces ("结构")
+    rng = np.random.default_rng(9)
+    N, d, f = 33, 24, 40
+    x = rng.standard_normal((N, d))
+    wg, wu, wd, _ = rand_layer(rng, 1, d, f)
+    for form in ("per_token", "grouped"):
+        lr = O.moe_layer(x, rng.standard_normal((1, d)), wg, wu, wd, 1, form=form)
+        np.testing.assert_allclose(lr.y, torch_swiglu(x, wg[0], wu[0], wd[0]), rtol=1e-12, atol=1e-13)
+
+
+def test_shared_expert_adds_dense_ffn():
+    rng = np.random.default_rng(10)
+    N, d, f, E, k = 20, 16, 24, 5, 2
+    x = rng.standard_normal((N, d))
+    Wr = rng.standard_normal((E, d))
+    wg, wu, wd, shared = rand_layer(rng, E, d, f, S=2)
+    a = O.moe_layer(x, Wr, wg, wu, wd, k, shared=shared).y
+    b = O.moe_layer(x, Wr, wg, wu, wd, k).y
+    dense = sum(torch_swiglu(x, shared[0][s], shared[1][s], shared[2][s]) for s in range(2))
+    np.testing.assert_allclose(a - b, dense, rtol=1e-11, atol=1e-12)
+
+
+def test_single_copy_against_torch_expert():
+    # y_t = w * Expert_e(x_t) for one routed copy, expert applied by torch
+    rng = np.random.default_rng(11)
+    N, d, f, E = 6, 16, 32, 3
+    x = rng.standard_normal((N, d))
+    Wr = rng.standard_normal((E, d))
+    wg, wu, wd, _ = rand_layer(rng, E, d, f)
+    lr = O.moe_layer(x, Wr, wg, wu, wd, 1)
+    for t in range(N):
+        e = lr.routing.idx[t, 0]
+        np.testing.assert_allclose(lr.y[t], torch_swiglu(x[t:t + 1], wg[e], wu[e], wd[e])[0],
+                                   rtol=1e-12, atol=1e-13)
+    # k = 2: weights from the renormalised softmax, checked against torch's topk
+    lr2 = O.moe_layer(x, Wr, wg, wu, wd, 2)
+    tp = torch.softmax(torch.from_numpy(x @ Wr.T), -1)
+    tw, ti = tp.topk(2, -1)
+    tw = tw / tw.sum(-1, keepdim=True)
+    for t in range(N):
+        ref = sum(tw[t, j].item() * torch_swiglu(x[t:t + 1], wg[ti[t, j]], wu[ti[t, j]], wd[ti[t, j]])[0]
+                  for j in range(2))
+        np.testing.assert_allclose(lr2.y[t], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_naive_equals_grouped_page_shape():
+    g = read_golden("naive_vs_grouped.txt")
+    cfg = mi.CONFIGS["p2_shape"]
+    assert (cfg.n_tokens, cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k) == (
+        g["n_tokens"], g["d_model"], g["d_ff"], g["n_experts"], g["top_k"])
+    lay = mi.make_layer(cfg)
+    x = mi.to_f64(mi.make_x(cfg))
+    sh = (mi.to_f64(lay.s_gate), mi.to_f64(lay.s_up), mi.to_f64(lay.s_down))
+    args = (x, mi.to_f64(lay.w_router), mi.to_f64(lay.w_gate), mi.to_f64(lay.w_up), mi.to_f64(lay.w_down),
+            cfg.top_k)
+    a = O.moe_layer(*args, shared=sh, form="per_token").y
+    b = O.moe_layer(*args, shared=sh, form="grouped").y
+    assert np.max(np.abs(a - b)) <= g["atol"]
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)  # fp64: far tighter than the page's 1e-5
+
+
+def test_naive_equals_grouped_with_capacity_and_rounding():
+    rng = np.random.default_rng(12)
+    N, d, f, E, k = 48, 32, 64, 6, 3
+    x = mi.to_f64(mi.f32_to_bf16_bits(rng.standard_normal((N, d)).astype(np.float32)))
+    Wr = rng.standard_normal((E, d)) * 0.3
+    wg, wu, wd, shared = rand_layer(rng, E, d, f, S=1)
+    for C in (0, 5, 13):
+        a = O.moe_layer(x, Wr, wg, wu, wd, k, shared=shared, capacity=C, round_h=True).y
+        b = O.moe_layer(x, Wr, wg, wu, wd, k, shared=shared, capacity=C, round_h=True, form="grouped").y
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------ statistic
+
+def test_balance_stat_uniform_probs_is_one():
+    rng = np.random.default_rng(13)
+    for E, k, N in ((8, 2, 64), (16, 4, 50), (256, 8, 33)):
+        counts = np.bincount(rng.integers(0, E, N * k), minlength=E)
+        prob_sum = np.full(E, N / E)
+        assert O.balance_stat(counts, prob_sum, N, k) == pytest.approx(1.0, abs=1e-14)
+
+
+def test_balance_stat_uniform_counts_is_one():
+    rng = np.random.default_rng(14)
+    E, k, N = 8, 2, 64
+    p = rng.dirichlet(np.ones(E), size=N)
+    counts = np.full(E, N * k // E)
+    assert O.balance_stat(counts, p.sum(0), N, k) == pytest.approx(1.0, abs=1e-14)
+
+
+def test_balance_stat_one_hot_is_E():
+    for E in (4, 16, 128):
+        N = 10
+        counts = np.zeros(E)
+        counts[3] = N
+        prob_sum = np.zeros(E)
+        prob_sum[3] = N
+        assert O.balance_stat(counts, prob_sum, N, 1) == E
+
+
+def test_balance_stat_skewed_page_case():
+    g = read_golden("skewed_aux.txt")
+    N, E, H = int(g["n_tokens"]), int(g["n_experts"]), int(g["hot"])
+    probs = np.zeros((N, E))
+    probs[:, :H] = g["p_hot"]
+    bad_idx = np.tile(np.arange(H), (N, 1))
+    counts = O.expert_counts(bad_idx, E)
+    assert O.balance_stat(counts, probs.sum(0), N, H) == g["value"]
+
+
+def test_balance_stat_random_router_near_one():
+    # the page: a randomly initialised router gives about 1
+    rng = np.random.default_rng(15)
+    N, d, E, k = 4000, 64, 16, 4
+    x = rng.standard_normal((N, d))
+    Wr = rng.standard_normal((E, d)) * 0.02
+    r = O.route(x, Wr, k)
+    stat = O.balance_stat(O.expert_counts(r.idx, E), r.probs.sum(0), N, k)
+    assert abs(stat - 1.0) < 0.05
+
+
+# ------------------------------------------------------------------ bf16 rounding
+
+def _all_bf16_values():
+    bits = np.arange(0, 0x7F80, dtype=np.uint32)  # +0 .. largest finite
+    return (bits << 16).view(np.float32).astype(np.float64)
+
+
+def test_bf16_round_is_nearest_even_bruteforce():
+    vals = _all_bf16_values()
+    rng = np.random.default_rng(16)
+    a = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-40, 38, 20000),
+        (vals[1:200] + vals[:199]) / 2,            # exact ties in the subnormal range
+        (vals[30000:30200] + vals[30001:30201]) / 2,  # exact ties among normals
+    ])
+    a = a[np.abs(a) < vals[-1]]
+    r = O.bf16_round(a)
+    m = np.abs(a)
+    j = np.searchsorted(vals, m)                    # vals[j-1] < m <= vals[j]
+    lo, hi = vals[np.maximum(j - 1, 0)], vals[j]
+    dlo, dhi = m - lo, hi - m
+    lo_even = (np.maximum(j - 1, 0) % 2) == 0
+    expect = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo_even, lo, hi)))
+    expect = np.where(m == hi, hi, expect)
+    np.testing.assert_array_equal(np.abs(r), expect)
+    np.testing.assert_array_equal(np.signbit(r), np.signbit(a))  # zeros keep their sign
+
+
+def test_bf16_round_matches_torch_on_fp32():
+    rng = np.random.default_rng(17)
+    a = (rng.standard_normal(100000) * 3).astype(np.float32)
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16_round(a.astype(np.float64)), ref)
+
+
+# ------------------------------------------------------------------ parameter model
+
+def test_exercise_parameter_count():
+    import bench
+    g = read_golden("exercise_params.txt")
+    per = bench.expert_params(int(g["d_model"]), int(g["d_ff"]))
+    total = g["n_experts"] * per * g["layers"]
+    active = g["top_k"] * per * g["layers"]
+    assert round(total / 1e9, 2) == g["total_billions_2dp"]
+    assert round(active / 1e9, 2) == g["active_billions_2dp"]
