@@ -1,3 +1,260 @@
+"""Benchmark: the forward pass of the MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
+
+One step is one moe_forward over the whole layer: route, permute, the gate|up
+and down grouped GEMMs, and combine. Inputs are seeded synthetic tensors
+(moe_inputs), already resident in HBM when the timed region starts. The
+timed region is K back-to-back steps, with a device synchronisation on each
+side. HIP events recorded inside each step give the per-stage times.
+
+It prints one JSON line:
+* value: tokens per second;
+* roofline: the dominant kernel (the gate|up grouped GEMM) against the
+  bf16 MFMA peak;
+* cpu_baseline: the CPU oracle timed on a bounded sample of the same
+  workload, on this host's cores;
+* extras: layer TFLOP/s and algorithmic GB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + TFLOP/s (%MFMA peak); decode HBM GB/s (%peak)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
 def expert_params(d_model: int, d_ff: int) -> int:
     """Parameters of one SwiGLU expert (gate, up, down; no biases): 3 * d * d_ff."""
     return 3 * d_model * d_ff
+
+
+WORKLOADS = {
+    # name -> (moe_inputs config, description)
+    "mixtral": ("mixtral", "Mixtral-shaped prefill: N=4096 d=4096 d_ff=14336 E=8 k=2, bf16"),
+    "dsv3_prefill": ("dsv3_prefill", "DeepSeek-V3-shaped prefill: N=8192 d=7168 d_ff=2048 E=256 k=8 +1 shared, bf16"),
+    "dsv3_decode": ("dsv3_decode", "DeepSeek-V3-shaped decode: N=64 d=7168 d_ff=2048 E=256 k=8 +1 shared, bf16"),
+    "switch_cap": ("switch_cap", "Switch-style top-1 with capacity 160: N=16384 d=2048 d_ff=8192 E=128, bf16"),
+}
+
+
+def algorithmic_work(cfg, counts, kept):
+    """Work the method must do, from the real routing.
+
+    The returned dict holds:
+    * flops_gate_up: 2 * d * 2F per kept copy, plus per token per shared expert;
+    * flops_down: 2 * F * d per kept copy, plus the shared experts;
+    * bytes: x once, W_r, every expert with at least one kept copy (3 d F
+      weights each), the shared experts, fp32 y, and idx/w (8 bytes per copy);
+    * bytes_gate_up: what the gate|up kernel must move: x, the gate and up
+      weights of the touched experts (and the shared ones), and bf16 h out.
+    """
+    import numpy as np
+    d, F, E, N, k = cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.n_tokens, cfg.top_k
+    S, Fs = cfg.n_shared, cfg.d_ff_shared
+    b = 2 if cfg.dtype == "bf16" else 4
+    n_kept = int(np.sum(kept))
+    touched = int(np.sum(np.asarray(kept) > 0))
+    fl_gu = 2 * d * 2 * F * n_kept + S * N * 2 * d * 2 * Fs
+    fl_dn = 2 * F * d * n_kept + S * N * 2 * Fs * d
+    w_bytes = touched * expert_params(d, F) * b + S * expert_params(d, Fs) * b
+    byts = N * d * b + E * d * b + w_bytes + N * d * 4 + N * k * 8
+    by_gu = N * d * b + (touched * 2 * F * d + S * 2 * Fs * d) * b + (n_kept * F + S * N * Fs) * b
+    return dict(flops_gate_up=fl_gu, flops_down=fl_dn, flops=fl_gu + fl_dn, bytes=byts,
+                bytes_gate_up=by_gu, touched=touched, kept=n_kept)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[a]), ctypes.c_void_p(self.ev[b])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_mixture_experts_44_amd", "csrc")
+    for f in ("grouped_swiglu.hip", "moe_common.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per gate|up launch from the committed rocprofv3 counter summary, or None.
+
+    The summary is used only when it was taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"gate_up_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, layer, x, budget_s=20.0):
+    """The oracle as it stands (grouped fp64 form) on the first rows of the workload.
+
+    The sample grows from 16 rows, doubling, until one run takes about a
+    tenth of the budget. It is then scaled to fill about the budget. The time
+    covers routing of the sample, grouping, the fp64 upcast of each touched
+    expert, the expert products and the combine. Input generation is left out.
+    """
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import moe_inputs as mi
+    from oracle import moe_oracle as O
+
+    def run(n):
+        xs = x[:n]
+        t = time.perf_counter()
+        r = O.route(mi.to_f64(xs), mi.to_f64(layer.w_router), cfg.top_k, layer.logit_bias,
+                    layer.select_bias, cfg.renormalize)
+        g = O.group(r.idx, cfg.n_experts, cfg.capacity)
+
+        class View:
+            def __init__(self, a):
+                self.a = a
+
+            def __getitem__(self, e):
+                return mi.to_f64(self.a[e])
+
+            def __len__(self):
+                return len(self.a)
+
+        shared = None
+        if layer.s_gate is not None:
+            shared = (View(layer.s_gate), View(layer.s_up), View(layer.s_down))
+        O.forward_grouped(mi.to_f64(xs), r.idx, r.w, g, View(layer.w_gate), View(layer.w_up),
+                          View(layer.w_down), shared=shared, round_h=(cfg.dtype == "bf16"))
+        return time.perf_counter() - t
+
+    n = 16
+    dt = run(n)
+    while dt < budget_s / 10 and n * 2 <= cfg.n_tokens:
+        n *= 2
+        dt = run(n)
+    if dt < budget_s / 2 and n < cfg.n_tokens:
+        n = int(min(cfg.n_tokens, max(n, n * (budget_s / max(dt, 1e-3)) * 0.8)))
+        dt = run(n)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("internal_api") == "openblas"] or [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {cfg.n_tokens} tokens of the same layer, full route+group+"
+                      f"grouped fp64 experts+combine, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this MoE layer build has no multi-GPU path "
+              "(expert-parallel sharding is a design note, not code). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import moe_inputs as mi
+    import sparse_mixture_experts_44_amd as moe
+    from sparse_mixture_experts_44_amd.layer import MoELayer, to_device
+
+    cfg_name, desc = WORKLOADS[args.workload]
+    cfg = mi.CONFIGS[cfg_name]
+    t = time.time()
+    layer, x = mi.make_layer(cfg), mi.make_x(cfg)
+    print(f"# inputs generated in {time.time() - t:.1f}s", file=sys.stderr, flush=True)
+    dev = "cuda:0"
+    L = MoELayer.from_numpy(moe.shape_for(cfg), layer, dev)
+    xd = to_device(x, dev)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        L.forward(xd)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = HipEvents(6 * K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        L.forward(xd, stage_events=ev.ev[6 * i: 6 * i + 6])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage_ms = {s: [] for s in moe.STAGES}
+    step_ms = []
+    for i in range(K):
+        for j, s in enumerate(moe.STAGES):
+            stage_ms[s].append(ev.elapsed_ms(6 * i + j, 6 * i + j + 1))
+        step_ms.append(ev.elapsed_ms(6 * i, 6 * i + 5))
+    avg = {s: float(np.mean(v)) for s, v in stage_ms.items()}
+
+    counts = L.out.counts.cpu().numpy()
+    offs = L.out.offsets.cpu().numpy()
+    kept = np.diff(offs)
+    work = algorithmic_work(cfg, counts, kept)
+    ms_step = wall / K * 1e3
+    tok_s = cfg.n_tokens * K / wall
+    gu_s = avg["gate_up"] * 1e-3
+    achieved_tf = work["flops_gate_up"] / gu_s / 1e12
+    traffic = measured_traffic(args.workload)
+
+    out = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, shapes of the pages' models)",
+        "config": {"workload": desc, "tokens": cfg.n_tokens, "d_model": cfg.d_model,
+                   "d_ff": cfg.d_ff, "experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "shared": cfg.n_shared, "capacity": cfg.capacity},
+        "roofline": {"kernel": "grouped gate|up (phase 1)", "bound": "mfma", "achieved": achieved_tf,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "avg_launch_ms": avg["gate_up"],
+                     "algorithmic_flops_per_launch": work["flops_gate_up"]},
+        "layer": {"tflops": work["flops"] / (ms_step * 1e-3) / 1e12,
+                  "mfma_frac": work["flops"] / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "algorithmic_GBs": work["bytes"] / (ms_step * 1e-3) / 1e9,
+                  "hbm_frac": work["bytes"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "event_ms_per_step": float(np.mean(step_ms)), "stage_ms": avg,
+                  "touched_experts": work["touched"], "kept_copies": work["kept"],
+                  "balance_stat": float(L.out.balance_stat.item())},
+    }
+    if not args.no_cpu_baseline:
+        del L, xd
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(cfg, layer, x, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * moe.h - C ABI of libmoe.so: the forward pass of a top-k routed
+ * Mixture-of-Experts layer on one AMD MI355X (gfx950).
+ *
+ * The layer is the MoE module of "混合专家 MoE" (anrans ai-infra
+ * handbook), section "实现：逐 token 与按专家分组". It is
+ * MoE(d, d_ff, n_experts, top_k, n_shared), built from:
+ *   route(x)              -> (weights, idx, probs)
+ *   forward_grouped(x)    -> y
+ *   aux_loss(probs, idx)  -> the balance statistic (section "负载均衡")
+ * It has two options from the other pages:
+ *   - an additive router bias: MoEGating's nn.Linear(input_dim,
+ *     num_experts) on the cloud.baidu.com overview;
+ *   - a per-expert capacity: the notes "混合专家模型 (MoE)：大规模稀疏条件计算的
+ *     架构与工程实践", section 三.1.
+ *
+ * Conventions, for every entry point:
+ *   - Every pointer is a DEVICE pointer, except `shape` (host) and
+ *     `stage_events` (a host array of event handles).
+ *   - Tensors are dense and row-major, with exactly the shapes given. Data
+ *     pointers are 16-byte aligned. Inputs are read-only.
+ *   - The caller owns every buffer, including the workspace. The library
+ *     allocates nothing, keeps no state between calls, and never
+ *     synchronises the host. Work is queued on `stream`; outputs are valid
+ *     once the stream reaches the end of the call. Two calls may run at the
+ *     same time if their output and workspace buffers do not overlap.
+ *   - Every argument is validated before anything is launched. On an error
+ *     nothing is queued and a negative moe_status is returned. A launch
+ *     failure reported by the runtime returns MOE_ERR_HIP; earlier work of
+ *     the same call may already be queued.
+ *   - Supported sizes:
+ *       d_model and every d_ff a multiple of 64;
+ *       1 <= top_k <= min(n_experts, 32);
+ *       n_experts <= 512;
+ *       n_tokens * top_k < 2^31.
+ *     Other sizes return MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null required pointer, bad dimension, k outside [1, E] */
+  MOE_ERR_UNSUPPORTED = -2, /* valid, but outside the sizes the kernels handle */
+  MOE_ERR_WORKSPACE = -3,   /* ws_bytes smaller than required */
+  MOE_ERR_HIP = -4          /* the runtime reported a launch error */
+} moe_status;
+
+typedef enum {
+  MOE_DTYPE_F32 = 0,  /* x and all weights fp32; h stays fp32 */
+  MOE_DTYPE_BF16 = 1  /* x and all weights bf16; fp32 accumulation; h rounded to bf16 */
+} moe_dtype;
+
+/* The layer's sizes and options. Tensor shapes below use these names:
+ * N = n_tokens, d = d_model, F = d_ff, E = n_experts, k = top_k,
+ * S = n_shared, Fs = d_ff_shared. */
+typedef struct {
+  int32_t n_tokens;
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t n_shared;     /* always-on shared experts (0 = none) */
+  int32_t d_ff_shared;  /* their hidden size (ignored when n_shared == 0) */
+  int32_t capacity;     /* rows per expert buffer C; <= 0 means unlimited */
+  int32_t renormalize;  /* 1: w = p / sum of the k selected p; 0: w = p */
+  int32_t dtype;        /* moe_dtype */
+} moe_shape;
+
+/* Number of hipEvent_t handles moe_forward records when given stage_events. */
+#define MOE_STAGE_EVENTS 6
+
+/* Workspace bytes that suffice for every entry point called with this shape
+ * (route, permute, grouped_swiglu with max_rows <= N*k + S*N, forward).
+ * At least 256 for a valid shape (also when N = 0); 0 for an invalid shape. */
+size_t moe_workspace_bytes(const moe_shape* shape);
+
+/* Static text for a status code; never NULL. */
+const char* moe_status_string(int status);
+
+/* Router: linear d -> E, softmax, selection-only bias, top-k, renormalise.
+ * ("实现" section: route; "负载均衡" section: the bias for selection only.)
+ *   x           [N, d]  (dtype)
+ *   w_router    [E, d]  (dtype); logits l = x W_r^T
+ *   logit_bias  [E] fp32 or NULL: added to the logits before the softmax
+ *   select_bias [E] fp32 or NULL: s = p + select_bias chooses the top-k;
+ *               the weights always come from the unbiased p
+ *   topk_idx    [N, k] int32 out: the k largest s, best first; an equal
+ *               score ranks the lower expert index first
+ *   topk_w      [N, k] fp32 out: p at topk_idx, divided by their sum if
+ *               renormalize
+ *   prob_sum    [E] fp64 out: sum over tokens of p[t, e], summed in a fixed
+ *               order, so it is reproducible bit for bit
+ *   ws          >= moe_workspace_bytes(shape) bytes */
+int moe_route(const moe_shape* shape, const void* x, const void* w_router,
+              const float* logit_bias, const float* select_bias,
+              int32_t* topk_idx, float* topk_w, double* prob_sum,
+              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Grouping of the N*k token copies by expert: histogram, capacity, prefix
+ * sum, stable permutation. This is forward_grouped's flatten, stable
+ * argsort and bincount ("实现" section). Copy c = t*k + j is slot j of token
+ * t. A copy is kept iff fewer than C earlier copies (in c order) went to the
+ * same expert (capacity, notes section 三.1).
+ *   topk_idx     [N, k] int32 in, values in [0, E) (other values: undefined result)
+ *   prob_sum     [E] fp64 in, or NULL (then balance_stat must be NULL)
+ *   counts       [E] int32 out: routed copies per expert, before capacity
+ *   offsets      [E+1] int32 out: exclusive prefix sum of min(counts, C)
+ *   perm         [N*k] int32 out: kept copy ids grouped by expert, and
+ *                increasing within each expert; entries past offsets[E]
+ *                are left untouched
+ *   slot_pos     [N*k] int32 out: row of copy c in perm, or -1 if dropped
+ *   balance_stat [1] fp64 out or NULL: E * sum_e (counts_e/(N*k)) * (prob_sum_e/N)
+ *                (aux_loss, "负载均衡" section) */
+int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const double* prob_sum,
+                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
+                double* balance_stat, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Grouped SwiGLU experts: for every group g and every row r of its segment
+ * [offsets[g], offsets[g+1]):
+ *   out[r] = W_down[g] (silu(W_gate[g] x_r) * (W_up[g] x_r))
+ * This is Expert.forward ("实现" section), one matrix product per group.
+ * In bf16 layers h = silu(.)*(.) is rounded to bf16 before the down
+ * projection, and accumulation is fp32.
+ *   shape       n_tokens, d_model and dtype are read; nothing else
+ *   n_groups    G >= 1;  d_ff: F of these experts
+ *   x           [N, d] (dtype)
+ *   perm        [max_rows] int32, or NULL. Row r's input is
+ *               x[perm[r] / rows_per_token]; with NULL it is
+ *               x[r - offsets[g]] (identity rows, as for a shared expert
+ *               with offsets {0, N})
+ *   offsets     [G+1] int32: non-decreasing, offsets[0] = 0,
+ *               offsets[G] <= max_rows. Rows past max_rows are not
+ *               computed, and input rows past N read as zero
+ *   w_gate/w_up [G, F, d] (dtype);  w_down [G, d, F] (dtype)
+ *   out         [max_rows, d] fp32 out, in grouped order; rows past
+ *               offsets[G] are left untouched
+ *   ws          >= max_rows * F * sizeof(dtype) + 256 bytes */
+int moe_grouped_swiglu(const moe_shape* shape, int32_t n_groups, int32_t d_ff,
+                       const void* x, const int32_t* perm, int32_t rows_per_token,
+                       const int32_t* offsets, int32_t max_rows,
+                       const void* w_gate, const void* w_up, const void* w_down,
+                       float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Weighted combine in token order, with no atomics and a fixed summation
+ * order:
+ *   y[t] = sum_{j=0..k-1, slot_pos[t*k+j] >= 0} topk_w[t,j] * expert_out[slot_pos[t*k+j]]
+ *          + sum_{s<S} shared_out[s, t]
+ * This is the output formula of section "结构", and forward_grouped's
+ * index_add_. A dropped copy adds nothing. The residual is the caller's.
+ *   expert_out [rows, d] fp32 (rows >= max slot_pos + 1)
+ *   slot_pos   [N*k] int32;  topk_w [N, k] fp32
+ *   shared_out [S, N, d] fp32, or NULL (required when S > 0)
+ *   y          [N, d] fp32 out */
+int moe_combine(const moe_shape* shape, const float* expert_out, const int32_t* slot_pos,
+                const float* topk_w, const float* shared_out, float* y, hipStream_t stream);
+
+/* The whole layer: route, permute, the grouped experts (routed and shared
+ * in one launch per projection), then combine. Outputs are as in the
+ * calls above. s_gate/s_up [S, Fs, d] and s_down [S, d, Fs] may be NULL
+ * only when S == 0.
+ * stage_events: NULL, or MOE_STAGE_EVENTS events created by the caller. It
+ * records event i before stage i (route, permute, gate|up, down, combine)
+ * and the last event after combine, all on `stream`. */
+int moe_forward(const moe_shape* shape, const void* x, const void* w_router,
+                const float* logit_bias, const float* select_bias,
+                const void* w_gate, const void* w_up, const void* w_down,
+                const void* s_gate, const void* s_up, const void* s_down,
+                float* y, int32_t* topk_idx, float* topk_w,
+                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
+                double* prob_sum, double* balance_stat,
+                void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

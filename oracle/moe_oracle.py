@@ -292,7 +292,7 @@ def forward_per_token(x, idx, w, keep, w_gate: WeightSet, w_up: WeightSet, w_dow
 
 
 def forward_grouped(x, idx, w, grouping: Grouping, w_gate: WeightSet, w_up: WeightSet,
-                    w_down: WeightSet, shared=None, round_h: bool = False) -> np.ndarray:
+                    w_down: WeightSet, shared=None, round_h: bool = False, rows=None) -> np.ndarray:
     """The grouped form: one matrix product per expert over its segment.
 
     Follows ``forward_grouped`` ("实现" section). The segment of expert e is
@@ -300,24 +300,31 @@ def forward_grouped(x, idx, w, grouping: Grouping, w_gate: WeightSet, w_up: Weig
     segment with at least one row runs the expert once over all of its rows.
     The result is added back at the tokens, scaled by their weights. Empty
     segments are skipped, as that section's second exercise requires.
+
+    ``rows`` keeps only those token rows, in the order given (all if None).
+    Each segment then holds only the copies of those tokens.
     """
     x = np.asarray(x, dtype=F64)
     N, k = idx.shape
-    out = np.zeros_like(x)
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    where = np.full(N, -1, dtype=np.int64)   # token -> output row, -1 if not kept
+    where[rows] = np.arange(rows.shape[0])
+    out = np.zeros((rows.shape[0], x.shape[1]), dtype=F64)
     wf = np.asarray(w, dtype=F64).reshape(-1)
     E = grouping.offsets.shape[0] - 1
     for e in range(E):
         a, b = int(grouping.offsets[e]), int(grouping.offsets[e + 1])
-        if a == b:
-            continue
         sel = grouping.perm[a:b]
+        sel = sel[where[sel // k] >= 0]
+        if sel.shape[0] == 0:
+            continue
         tok = sel // k
         y = swiglu_expert(x[tok], w_gate[e], w_up[e], w_down[e], round_h=round_h)
-        np.add.at(out, tok, y * wf[sel][:, None])
+        np.add.at(out, where[tok], y * wf[sel][:, None])
     if shared is not None:
         sg, su, sd = shared
         for s in range(len(sg)):
-            out += swiglu_expert(x, sg[s], su[s], sd[s], round_h=round_h)
+            out += swiglu_expert(x[rows], sg[s], su[s], sd[s], round_h=round_h)
     return out
 
 
@@ -382,7 +389,5 @@ def moe_layer(x, w_router, w_gate, w_up, w_down, k: int, *, shared=None, logit_b
                               shared=shared, round_h=round_h, rows=rows)
     elif form == "grouped":
         y = forward_grouped(x, r.idx, r.w, g, w_gate, w_up, w_down, shared=shared,
-                            round_h=round_h)
-        if rows is not None:
-            y = y[np.asarray(rows)]
+                            round_h=round_h, rows=rows)
     return LayerResult(routing=r, grouping=g, prob_sum=prob_sum, stat=stat, y=y)

@@ -1,0 +1,19 @@
+"""Forward pass of a top-k routed Mixture-of-Experts layer on AMD MI355X (gfx950).
+
+libmoe.so holds the hand-written HIP kernels behind a C ABI (include/moe.h).
+This package is its ctypes binding, with the same names, plus MoELayer, which
+keeps the weights resident on the device. Importing the package does not load
+the library; the first call does, and fails loudly if it has not been built.
+"""
+from ._native import (  # noqa: F401
+    LIB_PATH, MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
+    MOE_ERR_WORKSPACE, MOE_OK, MOE_STAGE_EVENTS, STAGES, MoEError, MoEShape, lib, moe_combine,
+    moe_forward, moe_grouped_swiglu, moe_permute, moe_route, status_string, workspace_bytes,
+)
+
+
+def shape_for(cfg, n_tokens=None) -> MoEShape:
+    """MoEShape of a moe_inputs.MoEConfig."""
+    return MoEShape.make(cfg.n_tokens if n_tokens is None else n_tokens, cfg.d_model, cfg.d_ff,
+                         cfg.n_experts, cfg.top_k, cfg.n_shared, cfg.d_ff_shared, cfg.capacity,
+                         cfg.renormalize, MOE_DTYPE_BF16 if cfg.dtype == "bf16" else MOE_DTYPE_F32)

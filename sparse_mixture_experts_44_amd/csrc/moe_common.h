@@ -1,0 +1,80 @@
+// Shared device helpers and the internal launch interfaces of libmoe.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte piece (a native vector, not HIP's uint4 struct)
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxTileEntries = 1024;  // routed groups + shared groups in one grouped launch
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  return (bf16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ------------------------------------------------------------------ router
+int launch_route(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
+                 const float* select_bias, int32_t* topk_idx, float* topk_w, double* prob_sum,
+                 double* partials, hipStream_t stream);
+int route_blocks(const moe_shape& s);  // number of router workgroups (rows of `partials`)
+
+// ------------------------------------------------------------------ permute
+int permute_chunks(const moe_shape& s);
+int launch_permute(const moe_shape& s, const int32_t* topk_idx, const double* prob_sum,
+                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
+                   double* balance_stat, int32_t* hist, int32_t* base, hipStream_t stream);
+
+// ------------------------------------------------------------------ grouped SwiGLU
+// One set of segments (the routed experts, or the shared experts).
+struct SegSet {
+  const int32_t* offsets;  // [n_groups+1] on the device; NULL: group g = rows [g*uniform_rows, (g+1)*uniform_rows)
+  const int32_t* perm;     // row r reads x[perm[r] / rows_per_token]; NULL: x[r - seg_start]
+  int32_t n_groups;
+  int32_t uniform_rows;
+  int32_t rows_per_token;
+  int32_t max_rows;        // rows at or past this are never computed
+  int32_t d_ff;
+  const void* w_gate;      // [G, d_ff, d]
+  const void* w_up;        // [G, d_ff, d]
+  const void* w_down;      // [G, d, d_ff]
+  void* h;                 // [max_rows, d_ff]: gate|up output, down input
+  float* out;              // [max_rows, d]
+};
+
+struct GroupedParams {
+  SegSet set[2];
+  int32_t n_sets;
+  const void* x;           // [n_tokens, d]
+  int32_t n_tokens;
+  int32_t d_model;
+  int32_t dtype;
+};
+
+// Phase 1: h = silu(x Wg^T) * (x Wu^T) per segment; phase 2: out = h Wd^T.
+int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream);
+
+// ------------------------------------------------------------------ combine
+int launch_combine(const moe_shape& s, const float* expert_out, const int32_t* slot_pos,
+                   const float* topk_w, const float* shared_out, float* y, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,92 @@
+"""A MoE layer whose weights stay resident in HBM and whose outputs are
+preallocated: MoE(d, d_ff, n_experts, top_k, n_shared) of "混合专家 MoE"
+(anrans ai-infra handbook), section "实现：逐 token 与按专家分组".
+
+This is plumbing around moe_forward. torch allocates the device buffers, and
+libmoe.so does every step of the computation.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _native as N
+
+
+def to_device(a: Optional[np.ndarray], device) -> Optional[torch.Tensor]:
+    """numpy -> device tensor. uint16 arrays are bf16 bit patterns."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+@dataclass
+class Outputs:
+    y: torch.Tensor          # [N, d] fp32
+    topk_idx: torch.Tensor   # [N, k] int32
+    topk_w: torch.Tensor     # [N, k] fp32
+    counts: torch.Tensor     # [E] int32
+    offsets: torch.Tensor    # [E+1] int32
+    perm: torch.Tensor       # [N*k] int32
+    slot_pos: torch.Tensor   # [N*k] int32
+    prob_sum: torch.Tensor   # [E] fp64
+    balance_stat: torch.Tensor  # [1] fp64
+
+    @classmethod
+    def empty(cls, n, d, E, k, device):
+        i32, f32, f64 = torch.int32, torch.float32, torch.float64
+        return cls(torch.empty(n, d, dtype=f32, device=device),
+                   torch.empty(n, k, dtype=i32, device=device),
+                   torch.empty(n, k, dtype=f32, device=device),
+                   torch.empty(E, dtype=i32, device=device),
+                   torch.empty(E + 1, dtype=i32, device=device),
+                   torch.empty(max(1, n * k), dtype=i32, device=device),
+                   torch.empty(max(1, n * k), dtype=i32, device=device),
+                   torch.empty(E, dtype=f64, device=device),
+                   torch.empty(1, dtype=f64, device=device))
+
+
+class MoELayer:
+    """Weights on the device plus a workspace and outputs sized for n_tokens."""
+
+    def __init__(self, shape: N.MoEShape, w_router, w_gate, w_up, w_down, s_gate=None, s_up=None,
+                 s_down=None, logit_bias=None, select_bias=None, device="cuda:0"):
+        self.shape = shape
+        self.device = torch.device(device)
+        self.w_router, self.w_gate, self.w_up, self.w_down = w_router, w_gate, w_up, w_down
+        self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
+        self.logit_bias, self.select_bias = logit_bias, select_bias
+        self._alloc()
+
+    @classmethod
+    def from_numpy(cls, shape: N.MoEShape, layer, device="cuda:0") -> "MoELayer":
+        """From a moe_inputs.Layer (numpy, storage format)."""
+        dv = lambda a: to_device(a, device)
+        return cls(shape, dv(layer.w_router), dv(layer.w_gate), dv(layer.w_up), dv(layer.w_down),
+                   dv(layer.s_gate), dv(layer.s_up), dv(layer.s_down), dv(layer.logit_bias),
+                   dv(layer.select_bias), device)
+
+    def _alloc(self):
+        s = self.shape
+        nbytes = N.workspace_bytes(s)
+        if nbytes == 0:
+            raise N.MoEError("moe_workspace_bytes", N.MOE_ERR_INVALID_ARG, "invalid shape")
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.out = Outputs.empty(s.n_tokens, s.d_model, s.n_experts, s.top_k, self.device)
+
+    def forward(self, x: torch.Tensor, stage_events=None, stream=None) -> Outputs:
+        if x.shape[0] != self.shape.n_tokens:
+            self.shape.n_tokens = x.shape[0]
+            self._alloc()
+        o = self.out
+        N.moe_forward(self.shape, x, self.w_router, self.logit_bias, self.select_bias, self.w_gate,
+                      self.w_up, self.w_down, self.s_gate, self.s_up, self.s_down, o.y, o.topk_idx,
+                      o.topk_w, o.counts, o.offsets, o.perm, o.slot_pos, o.prob_sum,
+                      o.balance_stat, self.ws, stage_events=stage_events, stream=stream)
+        return o

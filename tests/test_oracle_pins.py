@@ -283,6 +283,21 @@ def test_naive_equals_grouped_with_capacity_and_rounding():
         np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
 
 
+def test_grouped_on_row_subset_equals_per_token():
+    rng = np.random.default_rng(18)
+    N, d, f, E, k = 40, 16, 32, 5, 2
+    x = rng.standard_normal((N, d))
+    Wr = rng.standard_normal((E, d))
+    wg, wu, wd, shared = rand_layer(rng, E, d, f, S=1)
+    rows = np.array([39, 0, 17, 5])
+    for C in (0, 6):
+        a = O.moe_layer(x, Wr, wg, wu, wd, k, shared=shared, capacity=C, rows=rows).y
+        b = O.moe_layer(x, Wr, wg, wu, wd, k, shared=shared, capacity=C, rows=rows, form="grouped").y
+        full = O.moe_layer(x, Wr, wg, wu, wd, k, shared=shared, capacity=C, form="grouped").y
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(b, full[rows], rtol=1e-12, atol=1e-13)
+
+
 # ------------------------------------------------------------------ statistic
 
 def test_balance_stat_uniform_probs_is_one():
