@@ -31,7 +31,7 @@
  *   - Supported sizes:
  *       d_model and every d_ff a multiple of 64;
  *       1 <= top_k <= min(n_experts, 32);
- *       n_experts <= 512;
+ *       n_experts <= 512; n_shared <= 16; grouped_swiglu n_groups <= 528;
  *       n_tokens * top_k < 2^31.
  *     Other sizes return MOE_ERR_UNSUPPORTED.
  */

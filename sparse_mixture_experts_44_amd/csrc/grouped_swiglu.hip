@@ -83,20 +83,21 @@ struct TableLds {
   int cum[kMaxTileEntries + 1];
   int start[kMaxTileEntries];
   int rows[kMaxTileEntries];
-  int tmp[kThreads];
 };
 
-template <int BM>
-__device__ int build_table(const GroupedParams& p, int nt0, int nt1, TableLds& t) {
+// `scratch` holds NT ints of LDS that are free while the table is built.
+template <int BM, int NT>
+__device__ int build_table(const GroupedParams& p, int nt0, int nt1, TableLds& t, int* scratch) {
+  constexpr int PER = (kMaxTileEntries + NT - 1) / NT;
   const int G0 = p.set[0].n_groups;
   const int G1 = p.n_sets > 1 ? p.set[1].n_groups : 0;
   const int n = G0 + G1;
   const int tid = threadIdx.x;
-  const int per = (n + kThreads - 1) / kThreads;  // <= 4
-  int local[kMaxTileEntries / kThreads];
+  const int per = (n + NT - 1) / NT;  // <= PER
+  int local[PER];
   int sum = 0;
 #pragma unroll
-  for (int q = 0; q < kMaxTileEntries / kThreads; ++q) {
+  for (int q = 0; q < PER; ++q) {
     local[q] = 0;
     const int i = tid * per + q;
     if (q < per && i < n) {
@@ -109,24 +110,24 @@ __device__ int build_table(const GroupedParams& p, int nt0, int nt1, TableLds& t
       sum += local[q];
     }
   }
-  t.tmp[tid] = sum;
+  scratch[tid] = sum;
   __syncthreads();
-  for (int o = 1; o < kThreads; o <<= 1) {
-    const int add = tid >= o ? t.tmp[tid - o] : 0;
+  for (int o = 1; o < NT; o <<= 1) {
+    const int add = tid >= o ? scratch[tid - o] : 0;
     __syncthreads();
-    t.tmp[tid] += add;
+    scratch[tid] += add;
     __syncthreads();
   }
-  int run = tid ? t.tmp[tid - 1] : 0;
+  int run = tid ? scratch[tid - 1] : 0;
 #pragma unroll
-  for (int q = 0; q < kMaxTileEntries / kThreads; ++q) {
+  for (int q = 0; q < PER; ++q) {
     const int i = tid * per + q;
     if (q < per && i < n) {
       t.cum[i] = run;
       run += local[q];
     }
   }
-  if (tid == kThreads - 1) t.cum[n] = t.tmp[kThreads - 1];
+  if (tid == NT - 1) t.cum[n] = scratch[NT - 1];
   __syncthreads();
   return t.cum[n];
 }
@@ -152,29 +153,77 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + 
 
 // =====================================================================  bf16 MFMA
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// LDS tile rows hold BK bf16 of K: PPR = BK/8 pieces of 16 bytes, stored at
+// piece ^ swz(row). A wave's MFMA operand read has lanes 0..31 on 32
+// consecutive rows at the same logical piece. These XOR patterns spread every
+// group of 8 lanes (128 bytes per clock) and every group of 16 lanes (256
+// bytes per clock) over distinct banks:
+//   PPR = 8 (128-byte rows): g(r) = (r & 7) ^ ((r >> 3) & 1)
+//   PPR = 4 (64-byte rows):  g(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1)
+template <int PPR>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (PPR == 8) return (row & 7) ^ ((row >> 3) & 1);
+  else return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+}
 
-template <int BM, int BN, int WGM, int WGN, bool P1>
-__global__ __launch_bounds__(kThreads, 1) void grouped_mfma_kernel(GroupedParams p) {
-  constexpr int BK = 64;              // bf16 per K step
+// Copy 16 bytes per lane from global memory straight into LDS at
+// lds_addr + 16 * lane (global_load_lds_dwordx4; no VGPR staging, counted by
+// vmcnt). It is written as an instruction rather than the builtin: the
+// compiler treats the builtin's LDS write as aliasing every LDS read and
+// would drain all copies in flight (vmcnt(0)) before each fragment read,
+// which defeats the multi-stage prefetch. The instruction has no output
+// registers; the explicit vmcnt waits below order the reads after the copies.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding, then a workgroup barrier. The barrier is written out (not
+// __syncthreads) so that the compiler does not also wait for the LDS copies
+// of later stages that are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// One grouped GEMM launch (phase 1: gate|up + SiLU*up -> H; phase 2: down -> O).
+// Workgroup tile BM x BN x BK with NS LDS stages, filled by direct global->LDS
+// copies issued NS-1 steps ahead. WGM x WGN waves; wave tile (BM/WGM) x
+// (BN/WGN) of v_mfma_f32_32x32x16_bf16 blocks with fp32 accumulators.
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB, bool P1>
+__global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(GroupedParams p) {
   constexpr int ROWB = BK * 2;        // LDS bytes per tile row
+  constexpr int PPR = BK / 8;         // 16-byte pieces per row
+  constexpr int RPI = kWave / PPR;    // rows per 1 KB copy instruction
   constexpr int TM = BM / WGM;        // rows per wave
   constexpr int FM = TM / 32;
   constexpr int BH = P1 ? BN / 2 : BN;  // output columns per tile
   constexpr int TN = BH / WGN;          // output columns per wave
   constexpr int FN = TN / 32;
-  constexpr int NB = P1 ? 2 * FN : FN;  // B fragments per k-step
-  constexpr int A_PER = BM * 8 / kThreads;
-  constexpr int B_PER = BN * 8 / kThreads;
-  static_assert(A_PER >= 1 && B_PER >= 2 && FM >= 1 && FN >= 1, "tile shape");
+  constexpr int NB = P1 ? 2 * FN : FN;  // B fragments per k16 step
+  constexpr int WAVES = WGM * WGN;
+  constexpr int NT = WAVES * kWave;
+  constexpr int A_INS = BM / RPI / WAVES;  // copy instructions per wave per stage
+  constexpr int B_INS = BN / RPI / WAVES;
+  constexpr int L = A_INS + B_INS;         // vector-memory ops per wave per stage
+  constexpr int STAGE_A = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(A_INS >= 1 && B_INS >= 1 && FM >= 1 && FN >= 1 && NS >= 2 && NS <= 6, "tile shape");
+  static_assert(A_INS * RPI * WAVES == BM && B_INS * RPI * WAVES == BN, "copy slots cover the tile");
+  static_assert(!P1 || (BN / 2) % (RPI * B_INS) == 0, "a wave's B rows come from one matrix");
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][BM * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][BN * ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_tile[NS][STAGE];
   __shared__ TableLds tab;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / WGN, wn = wave % WGN;
   const int d = p.d_model;
   // output columns per set (h columns in phase 1, d in phase 2); the last n-tile may be partial
@@ -182,11 +231,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_mfma_kernel(GroupedParams
   const int nt1 = p.n_sets > 1 ? ((P1 ? p.set[1].d_ff : d) + BH - 1) / BH : 0;
   const int G0 = p.set[0].n_groups;
   const int nent = G0 + (p.n_sets > 1 ? p.set[1].n_groups : 0);
-  const int total = build_table<BM>(p, nt0, nt1, tab);
+  static_assert(NS * STAGE >= NT * 4, "table scan scratch fits in the stage buffers");
+  const int total = build_table<BM, NT>(p, nt0, nt1, tab, reinterpret_cast<int*>(&s_tile[0][0]));
   const bf16_t* __restrict__ xg = static_cast<const bf16_t*>(p.x);
 
-  // this thread's load slots: row (tid >> 3) + 32 q, 16-byte piece (tid & 7)
-  const int lrow = tid >> 3, lpc = tid & 7;
+  // Copy slots: instruction i of this wave fills tile rows (wave*INS + i)*RPI + lane/PPR;
+  // lane writes LDS piece (lane % PPR), so it fetches logical piece (lane % PPR) ^ swz(row).
+  const int crow = lane / PPR, cpc = lane % PPR;
 
   for (int T = xcd_block(); T < total; T += gridDim.x) {
     const int ent = find_entry(tab.cum, nent, T);
@@ -203,87 +254,55 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_mfma_kernel(GroupedParams
     const int F = S.d_ff;
     const int K = P1 ? d : F;
     const int nk = K / BK;
-
-    // ---- global sources: 32-bit element offsets of this thread's 16-byte pieces.
-    // Rows past the segment (or tokens out of range) load row 0 of the
-    // source and are zeroed after the load.
-    const bf16_t* a_base = P1 ? xg : static_cast<const bf16_t*>(S.h);
-    uint32_t a_off[A_PER];
-    uint32_t a_ok = 0;
-#pragma unroll
-    for (int q = 0; q < A_PER; ++q) {
-      const int r = lrow + 32 * q;
-      uint32_t off = 0;
-      if (r < mvalid) {
-        const int row = start + m0 + r;
-        if constexpr (P1) {
-          const int tok = S.perm ? S.perm[row] / S.rpt : row - start;
-          if ((unsigned)tok < (unsigned)p.n_tokens) {
-            off = (uint32_t)tok * (uint32_t)d + lpc * 8;
-            a_ok |= 1u << q;
-          }
-        } else {
-          off = (uint32_t)row * (uint32_t)F + lpc * 8;
-          a_ok |= 1u << q;
-        }
-      }
-      a_off[q] = off;
-    }
-    // B rows: weight rows n0 + lrow + 32 q. Rows past the last output column
-    // (a partial n-tile; columns come in multiples of 64) re-read an in-range
-    // row, and their results are never stored.
     const int ncols = P1 ? F : d;
-    const int qmax = (min(BH, ncols - n0) + 31) / 32 - 1;
-    constexpr int BQ = P1 ? B_PER / 2 : B_PER;  // B pieces per weight matrix
-    const bf16_t* b_base0;  // gate (phase 1) or down (phase 2) weights of group g
-    const bf16_t* b_base1;  // up weights of group g (phase 1)
-    if constexpr (P1) {
-      b_base0 = static_cast<const bf16_t*>(S.wg) + (size_t)g * F * d;
-      b_base1 = static_cast<const bf16_t*>(S.wu) + (size_t)g * F * d;
-    } else {
-      b_base0 = static_cast<const bf16_t*>(S.wd) + (size_t)g * d * F;
-      b_base1 = b_base0;
-    }
-    uint32_t b_off[BQ];
-#pragma unroll
-    for (int q = 0; q < BQ; ++q) b_off[q] = (uint32_t)(n0 + lrow + 32 * min(q, qmax)) * (uint32_t)K + lpc * 8;
-    // LDS byte offsets of this thread's pieces (same for both buffers)
-    uint32_t a_lds[A_PER], b_lds[B_PER];
-#pragma unroll
-    for (int q = 0; q < A_PER; ++q) {
-      const int r = lrow + 32 * q;
-      a_lds[q] = r * ROWB + ((lpc ^ swz(r)) << 4);
-    }
-#pragma unroll
-    for (int q = 0; q < B_PER; ++q) {
-      // phase 1: pieces [0, BQ) are gate rows (tile rows [0, BN/2)), [BQ, 2 BQ) up rows
-      const int r = lrow + 32 * (q % BQ) + (q / BQ) * (BN / 2);
-      b_lds[q] = r * ROWB + ((lpc ^ swz(r)) << 4);
-    }
 
-    u32x4_t ra[A_PER], rb[B_PER];
-#define MOE_GLOAD(KT)                                                                      \
-  {                                                                                        \
-    const int ko_ = (KT) * BK;                                                             \
-    _Pragma("unroll") for (int q = 0; q < A_PER; ++q) {                                    \
-      ra[q] = *reinterpret_cast<const u32x4_t*>(a_base + a_off[q] + ko_);                    \
-    }                                                                                      \
-    _Pragma("unroll") for (int q = 0; q < BQ; ++q) {                                       \
-      rb[q] = *reinterpret_cast<const u32x4_t*>(b_base0 + b_off[q] + ko_);                 \
-      if constexpr (P1) rb[q + BQ] = *reinterpret_cast<const u32x4_t*>(b_base1 + b_off[q] + ko_); \
-    }                                                                                      \
-  }
-#define MOE_LSTORE(BUF)                                                                    \
-  {                                                                                        \
-    _Pragma("unroll") for (int q = 0; q < A_PER; ++q) {                                    \
-      u32x4_t v_ = ra[q];                                                                    \
-      if (!((a_ok >> q) & 1u)) v_ = u32x4_t{0u, 0u, 0u, 0u};                                \
-      *reinterpret_cast<u32x4_t*>(&s_a[BUF][a_lds[q]]) = v_;                                 \
-    }                                                                                      \
-    _Pragma("unroll") for (int q = 0; q < B_PER; ++q) {                                    \
-      *reinterpret_cast<u32x4_t*>(&s_b[BUF][b_lds[q]]) = rb[q];                              \
-    }                                                                                      \
-  }
+    // ---- A sources: rows past the segment (or with a token out of range)
+    // re-read the segment's first row; their outputs are never stored.
+    const bf16_t* a_base = P1 ? xg : static_cast<const bf16_t*>(S.h);
+    uint32_t a_off[A_INS];
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+      const int r = (wave * A_INS + i) * RPI + crow;
+      const int rr = r < mvalid ? r : 0;
+      const int row = start + m0 + rr;
+      uint32_t src;
+      if constexpr (P1) {
+        const int tok = S.perm ? S.perm[row] / S.rpt : row - start;
+        src = (unsigned)tok < (unsigned)p.n_tokens ? (uint32_t)tok : 0u;
+        src *= (uint32_t)d;
+      } else {
+        src = (uint32_t)row * (uint32_t)F;
+      }
+      a_off[i] = src + ((cpc ^ swz<PPR>(r)) << 3);
+    }
+    // ---- B sources: weight rows n0 + (tile row within its matrix); rows past
+    // the last output column (partial n-tile) re-read an in-range row.
+    const int lastq = min(BH, ncols - n0) - 1;
+    const bf16_t* b_base;
+    if constexpr (P1) {
+      const bool up = wave * B_INS * RPI >= BN / 2;
+      b_base = static_cast<const bf16_t*>(up ? S.wu : S.wg) + (size_t)g * F * d;
+    } else {
+      b_base = static_cast<const bf16_t*>(S.wd) + (size_t)g * d * F;
+    }
+    uint32_t b_off[B_INS];
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+      const int r = (wave * B_INS + i) * RPI + crow;      // tile row
+      const int mr = P1 ? (r % (BN / 2)) : r;              // row within its weight matrix tile
+      b_off[i] = (uint32_t)(n0 + min(mr, lastq)) * (uint32_t)K + ((cpc ^ swz<PPR>(r)) << 3);
+    }
+    const uint32_t a_lds0 = lds_addr(&s_tile[0][(wave * A_INS) * 1024]);
+    const uint32_t b_lds0 = lds_addr(&s_tile[0][STAGE_A + (wave * B_INS) * 1024]);
+
+    auto issue = [&](int kt) {
+      const int st = kt % NS;
+      const int ko = kt * BK;
+#pragma unroll
+      for (int i = 0; i < A_INS; ++i) dma16(a_base + a_off[i] + ko, a_lds0 + st * STAGE + i * 1024);
+#pragma unroll
+      for (int i = 0; i < B_INS; ++i) dma16(b_base + b_off[i] + ko, b_lds0 + st * STAGE + i * 1024);
+    };
 
     f32x16_t acc[FM][NB];
 #pragma unroll
@@ -293,50 +312,68 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_mfma_kernel(GroupedParams
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    __syncthreads();  // previous tile's LDS reads are done
-    MOE_GLOAD(0);
-    MOE_LSTORE(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) MOE_GLOAD(kt + 1);
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int chunk = ks * 2 + (lane >> 5);
-        bf16x8_t af[FM], bfr[NB];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * TM + i * 32 + (lane & 31);
-          af[i] = *reinterpret_cast<const bf16x8_t*>(&s_a[buf][r * ROWB + ((chunk ^ swz(r)) << 4)]);
-        }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          // phase 1: fragments [0, FN) are gate rows, [FN, 2 FN) the matching up rows
-          const int jj = P1 ? (j % FN) : j;
-          const int half = P1 ? (j / FN) * (BN / 2) : 0;
-          const int r = half + wn * TN + jj * 32 + (lane & 31);
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(&s_b[buf][r * ROWB + ((chunk ^ swz(r)) << 4)]);
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-      if (kt + 1 < nk) MOE_LSTORE(buf ^ 1);
-      __syncthreads();
+    // 32-row MFMA blocks of this wave that hold segment rows: a segment's last
+    // tile is often short, and its empty blocks skip their reads and MFMAs.
+    const int nact = max(0, min(FM, (mvalid - wm * TM + 31) / 32));
+
+#define MOE_K_LOOP(ACTIVE)                                                                       \
+    for (int kt = 0; kt < nk; ++kt) {                                                            \
+      /* stage kt has landed once at most (stages issued after it) * L copies are outstanding */ \
+      const int later = min(NS - 2, nk - 1 - kt);                                                \
+      if (later >= 4) wait_vm_barrier<4 * L>();                                                 \
+      else if (later == 3) wait_vm_barrier<3 * L>();                                             \
+      else if (later == 2) wait_vm_barrier<2 * L>();                                             \
+      else if (later == 1) wait_vm_barrier<L>();                                                 \
+      else wait_vm_barrier<0>();                                                                 \
+      if (kt + NS - 1 < nk) issue(kt + NS - 1); /* refills the stage read in step kt-1 */        \
+      const uint8_t* sa = &s_tile[kt % NS][0];                                                   \
+      const uint8_t* sb = sa + STAGE_A;                                                          \
+      _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                   \
+        const int chunk = ks * 2 + (lane >> 5);                                                  \
+        bf16x8_t af[FM], bfr[NB];                                                                \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                         \
+          if (!(ACTIVE(i))) continue;                                                            \
+          const int r = wm * TM + i * 32 + (lane & 31);                                          \
+          af[i] = *reinterpret_cast<const bf16x8_t*>(sa + r * ROWB + ((chunk ^ swz<PPR>(r)) << 4)); \
+        }                                                                                        \
+        _Pragma("unroll") for (int j = 0; j < NB; ++j) {                                         \
+          /* phase 1: fragments [0, FN) are gate rows, [FN, 2 FN) the matching up rows */        \
+          const int jj = P1 ? (j % FN) : j;                                                      \
+          const int half = P1 ? (j / FN) * (BN / 2) : 0;                                         \
+          const int r = half + wn * TN + jj * 32 + (lane & 31);                                  \
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + r * ROWB + ((chunk ^ swz<PPR>(r)) << 4)); \
+        }                                                                                        \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                         \
+          if (!(ACTIVE(i))) continue;                                                            \
+          _Pragma("unroll") for (int j = 0; j < NB; ++j)                                         \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0); \
+        }                                                                                        \
+      }                                                                                          \
     }
-#undef MOE_GLOAD
-#undef MOE_LSTORE
+#define MOE_ALL(i) true
+#define MOE_SOME(i) ((i) < nact)
+    __syncthreads();  // every wave is done with the previous tile's stages
+#pragma unroll
+    for (int s2 = 0; s2 < NS - 1; ++s2)
+      if (s2 < nk) issue(s2);
+    if (nact == FM) {
+      MOE_K_LOOP(MOE_ALL)
+    } else {
+      MOE_K_LOOP(MOE_SOME)
+    }
+#undef MOE_ALL
+#undef MOE_SOME
+#undef MOE_K_LOOP
 
     // ---- epilogue. acc[i][j][v]: column (lane & 31), row 8 (v / 4) + 4 (lane / 32) + (v % 4)
-    const int col_l = lane & 31;
-    const int col0 = n0 + wn * TN + col_l;  // this lane's first output column
+    const int col0 = n0 + wn * TN + (lane & 31);  // this lane's first output column
+    int rbase = wm * TM + 4 * (lane >> 5);
+    asm volatile("" : "+v"(rbase));  // per tile: keeps the 64 row offsets from being hoisted (and spilled)
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
         if (r >= mvalid) continue;
         const size_t row = (size_t)(start + m0 + r);
         if constexpr (P1) {
@@ -371,7 +408,8 @@ __global__ __launch_bounds__(kThreads) void grouped_f32_kernel(GroupedParams p) 
   const int nt1 = p.n_sets > 1 ? (P1 ? p.set[1].d_ff : d) / BC : 0;
   const int G0 = p.set[0].n_groups;
   const int nent = G0 + (p.n_sets > 1 ? p.set[1].n_groups : 0);
-  const int total = build_table<BM>(p, nt0, nt1, tab);
+  __shared__ int s_scan[kThreads];
+  const int total = build_table<BM, kThreads>(p, nt0, nt1, tab, s_scan);
   const float* __restrict__ xg = static_cast<const float*>(p.x);
 
   for (int T = xcd_block(); T < total; T += gridDim.x) {
@@ -460,14 +498,16 @@ int grid_for(long long ub, int per_cu) {
   return (int)((g + kXcds - 1) / kXcds * kXcds);
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB = 1>
 void launch_mfma(const GroupedParams& p, int phase, hipStream_t st) {
   const int BH = phase == 1 ? BN / 2 : BN;
-  const int grid = grid_for(tiles_upper_bound(p, phase, BM, BH), 1);
+  const int grid = grid_for(tiles_upper_bound(p, phase, BM, BH), MINB);
   if (phase == 1)
-    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, WGM, WGN, true>), dim3(grid), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, true>), dim3(grid),
+                       dim3(WGM * WGN * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, WGM, WGN, false>), dim3(grid), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, false>), dim3(grid),
+                       dim3(WGM * WGN * 64), 0, st, p);
 }
 
 }  // namespace
@@ -482,8 +522,8 @@ int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream) {
   } else {
     // tile height from the mean routed rows per expert segment
     const long long avg = (long long)p.set[0].max_rows / std::max(1, p.set[0].n_groups);
-    if (avg >= 128) launch_mfma<256, 256, 2, 2>(p, phase, stream);
-    else launch_mfma<64, 256, 1, 4>(p, phase, stream);
+    if (avg >= 128) launch_mfma<256, 256, 64, 2, 4, 2>(p, phase, stream);
+    else launch_mfma<64, 256, 64, 1, 4, 3>(p, phase, stream);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

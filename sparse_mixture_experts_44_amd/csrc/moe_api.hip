@@ -25,7 +25,7 @@ int check_shape(const moe_shape* sp) {
   if (s.renormalize != 0 && s.renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (s.d_model % 64 || s.d_ff % 64 || (s.n_shared > 0 && s.d_ff_shared % 64)) return MOE_ERR_UNSUPPORTED;
   if (s.n_experts > kMaxExperts || s.top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
-  if (s.n_shared > kMaxTileEntries - kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (s.n_shared > kMaxShared) return MOE_ERR_UNSUPPORTED;
   const long long N = s.n_tokens;
   if (N * s.top_k >= (1LL << 31) || N * (s.top_k + s.n_shared) >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;

@@ -19,7 +19,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte piece 
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
-constexpr int kMaxTileEntries = 1024;  // routed groups + shared groups in one grouped launch
+constexpr int kMaxShared = 16;
+constexpr int kMaxTileEntries = kMaxExperts + kMaxShared;  // routed + shared groups in one grouped launch
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
