@@ -33,7 +33,7 @@ int check_shape(const moe_shape* sp) {
 
 // Workspace layout shared by the entry points (byte offsets, 256-aligned).
 struct Layout {
-  size_t partials, hist, base, h_routed, h_shared, o, total;
+  size_t partials, logits, hist, base, h_routed, h_shared, o, total;
 };
 
 Layout layout(const moe_shape& s) {
@@ -43,6 +43,8 @@ Layout layout(const moe_shape& s) {
   size_t off = 0;
   L.partials = off;
   off += align256((size_t)route_blocks(s) * E * sizeof(double));
+  L.logits = off;
+  off += align256(route_logits_floats(s) * sizeof(float));
   L.hist = off;
   off += align256((size_t)permute_chunks(s) * E * sizeof(int32_t));
   L.base = off;
@@ -68,8 +70,10 @@ int zero_f64(double* p, int n, hipStream_t st) {
 int do_route(const moe_shape& s, const void* x, const void* w_router, const float* lb, const float* sb,
              int32_t* idx, float* tw, double* prob_sum, void* ws, hipStream_t st) {
   if (s.n_tokens == 0) return zero_f64(prob_sum, s.n_experts, st);
+  const Layout L = layout(s);
   return launch_route(s, x, w_router, lb, sb, idx, tw, prob_sum,
-                      reinterpret_cast<double*>(at(ws, layout(s).partials)), st);
+                      reinterpret_cast<double*>(at(ws, L.partials)),
+                      reinterpret_cast<float*>(at(ws, L.logits)), st);
 }
 
 int do_permute(const moe_shape& s, const int32_t* idx, const double* prob_sum, int32_t* counts,

@@ -34,10 +34,12 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // ------------------------------------------------------------------ router
+// `partials`: route_blocks(s) x E doubles; `logits`: route_logits_floats(s) floats (workspace).
 int launch_route(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                  const float* select_bias, int32_t* topk_idx, float* topk_w, double* prob_sum,
-                 double* partials, hipStream_t stream);
-int route_blocks(const moe_shape& s);  // number of router workgroups (rows of `partials`)
+                 double* partials, float* logits, hipStream_t stream);
+int route_blocks(const moe_shape& s);
+size_t route_logits_floats(const moe_shape& s);
 
 // ------------------------------------------------------------------ permute
 int permute_chunks(const moe_shape& s);

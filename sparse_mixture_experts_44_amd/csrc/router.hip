@@ -4,26 +4,28 @@
 // "实现：逐 token 与按专家分组". The bias for selection only is the
 // aux-loss-free balancing of its section "负载均衡".
 //
-// One workgroup takes 32 tokens and every expert.
-//
-// Logits: a VALU GEMM. The matrix cores are kept for the expert GEMMs.
-//   - The K dimension is staged through LDS in chunks of 128 bytes per row.
-//     Rows are padded to 144 bytes, so 16-byte reads from consecutive rows
-//     fall in different banks.
-//   - Each thread owns 4 tokens x EPT experts. bf16 uses v_dot2_f32_bf16,
-//     two products per instruction with fp32 accumulation.
-//   - Each chunk is summed into a fresh partial, which is then added to the
-//     running sum. This keeps the fp32 rounding of long rows small.
-//
-// Softmax and top-k: one wavefront per token.
-//   - Each lane holds E/64 scores.
-//   - Max and sum use butterfly reductions, whose order is fixed.
-//   - Top-k runs k rounds of a wave arg-max. A larger score wins; on equal
-//     scores the lower expert index wins.
-//
-// Probability sums: p is added into fp64 per-wave partials, then the waves
-// are combined in a fixed order. A second kernel adds the workgroup rows in
-// workgroup order. So prob_sum is bit-reproducible.
+// Three kernels:
+//   1. logits_kernel: a VALU GEMM (the matrix cores are kept for the expert
+//      GEMMs).
+//      - Grid: (token tile) x (K split), sized to give every CU more than one
+//        workgroup also at decode sizes (N = 64).
+//      - K is staged through LDS 128 bytes per row at a time. Rows are padded
+//        to 144 bytes, so 16-byte reads from consecutive rows use distinct
+//        banks.
+//      - Each thread owns TPT tokens x EPT experts. bf16 uses v_dot2_f32_bf16
+//        (two products per instruction, fp32 accumulation).
+//      - Each chunk is summed into a fresh partial before it is added to the
+//        running sum.
+//      - Output: fp32 partial logits [split][N][E].
+//   2. select_kernel: one wavefront per token.
+//      - Sums the splits in split order, adds the logit bias, then softmax
+//        with butterfly reductions in a fixed order, the selection score, and
+//        k rounds of a wave arg-max. A larger score wins; on equal scores the
+//        lower expert index wins.
+//      - Renormalises the k weights.
+//      - Adds p into fp64 per-workgroup sums in a fixed order.
+//   3. prob_sum_kernel: one wavefront per expert adds the workgroup sums with
+//      a fixed tree, so prob_sum is bit-reproducible.
 #include <math.h>
 
 #include "moe_common.h"
@@ -31,10 +33,11 @@
 namespace moe {
 namespace {
 
-constexpr int kTok = 32;          // tokens per workgroup
 constexpr int kThreads = 256;
-constexpr int kChunk = 32;        // dwords per row chunk: 64 bf16 or 32 fp32
-constexpr int kRow = kChunk + 4;  // padded LDS row stride in dwords
+constexpr int kChunk = 32;         // dwords per row chunk: 64 bf16 or 32 fp32
+constexpr int kRow = kChunk + 4;   // padded LDS row stride in dwords
+constexpr int kSelTokMax = 32;     // tokens per select workgroup, at most (8 per wave)
+constexpr int kTargetBlocks = 512; // logits workgroups to aim for
 
 template <bool BF16>
 __device__ __forceinline__ float mac(uint32_t a, uint32_t b, float c) {
@@ -58,112 +61,134 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <bool BF16, int EPT>
-__global__ __launch_bounds__(kThreads) void router_kernel(
-    const uint32_t* __restrict__ x, const uint32_t* __restrict__ w,
-    const float* __restrict__ logit_bias, const float* __restrict__ select_bias, int N,
-    int dw, int E, int k, int renorm, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, double* __restrict__ partials) {
-  constexpr int EROWS = 32 * EPT;                 // expert rows covered by the thread grid
-  constexpr int EL = (EROWS + kWave - 1) / kWave;  // experts per lane in the softmax phase
-  constexpr int LROW = EROWS + 1;                 // logits row stride (floats)
-  static_assert(kTok * LROW <= EROWS * kRow, "logits must fit in the W staging area");
+// ---------------------------------------------------------------- 1. logits
+
+// Thread grid: EG expert groups x (256/EG) token groups. Thread (tg, eg) owns
+// tokens tg + TG*i (i < TPT) and experts eg + EG*j (j < EPT).
+template <bool BF16, int EG, int EPT, int TPT>
+__global__ __launch_bounds__(kThreads) void logits_kernel(const uint32_t* __restrict__ x,
+                                                          const uint32_t* __restrict__ w, int N,
+                                                          int dw, int E, int chunks_per_split,
+                                                          float* __restrict__ part) {
+  constexpr int TG = kThreads / EG;
+  constexpr int TT = TG * TPT;        // tokens per workgroup
+  constexpr int EROWS = EG * EPT;     // expert rows covered
+  constexpr int XP = (TT * 8 + kThreads - 1) / kThreads;     // x pieces (16 B) per thread per chunk
+  constexpr int WP = (EROWS * 8 + kThreads - 1) / kThreads;  // W pieces per thread per chunk
   __shared__ uint32_t s_w[EROWS * kRow];
-  __shared__ uint32_t s_x[kTok * kRow];
-  __shared__ double s_part[kThreads / kWave][EROWS];
+  __shared__ uint32_t s_x[TT * kRow];
 
   const int tid = threadIdx.x;
-  const int eg = tid & 31;   // expert group: experts eg + 32 j
-  const int tg = tid >> 5;   // token group: tokens tg + 8 i
-  const int t0 = blockIdx.x * kTok;
+  const int eg = tid % EG, tg = tid / EG;
+  const int t0 = blockIdx.x * TT;
+  const int split = blockIdx.y;
+  const int nchunks = dw / kChunk;
+  const int c0 = split * chunks_per_split;
+  const int c1 = min(nchunks, c0 + chunks_per_split);
 
-  float acc[4][EPT];
+  float acc[TPT][EPT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TPT; ++i)
 #pragma unroll
     for (int j = 0; j < EPT; ++j) acc[i][j] = 0.f;
 
-  u32x4_t px;
-  u32x4_t pw[EPT];
+  u32x4_t px[XP], pw[WP];
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  auto load_chunk = [&](int kc) {
-    const int r = tid >> 3, pc = tid & 7;
-    const int t = t0 + r;
-    px = (t < N) ? *reinterpret_cast<const u32x4_t*>(x + (size_t)t * dw + kc + pc * 4) : zero;
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const int piece = tid + kThreads * j;
-      const int er = piece >> 3, epc = piece & 7;
-      pw[j] = (er < E) ? *reinterpret_cast<const u32x4_t*>(w + (size_t)er * dw + kc + epc * 4) : zero;
-    }
-  };
+#define MOE_LOAD_CHUNK(C)                                                                 \
+  {                                                                                       \
+    const int kc_ = (C) * kChunk;                                                         \
+    _Pragma("unroll") for (int q = 0; q < XP; ++q) {                                      \
+      const int piece = tid + kThreads * q, r = piece >> 3, pc = piece & 7;               \
+      const int t = t0 + r;                                                               \
+      px[q] = (r < TT && t < N) ? *reinterpret_cast<const u32x4_t*>(x + (size_t)t * dw + kc_ + pc * 4) : zero; \
+    }                                                                                     \
+    _Pragma("unroll") for (int q = 0; q < WP; ++q) {                                      \
+      const int piece = tid + kThreads * q, er = piece >> 3, pc = piece & 7;              \
+      pw[q] = (er < EROWS && er < E) ? *reinterpret_cast<const u32x4_t*>(w + (size_t)er * dw + kc_ + pc * 4) : zero; \
+    }                                                                                     \
+  }
 
-  load_chunk(0);
-  for (int kc = 0; kc < dw; kc += kChunk) {
+  if (c0 < c1) MOE_LOAD_CHUNK(c0);
+  for (int c = c0; c < c1; ++c) {
     __syncthreads();  // everyone finished reading the previous chunk
-    *reinterpret_cast<u32x4_t*>(s_x + (tid >> 3) * kRow + (tid & 7) * 4) = px;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const int piece = tid + kThreads * j;
-      *reinterpret_cast<u32x4_t*>(s_w + (piece >> 3) * kRow + (piece & 7) * 4) = pw[j];
+    for (int q = 0; q < XP; ++q) {
+      const int piece = tid + kThreads * q;
+      if (piece < TT * 8) *reinterpret_cast<u32x4_t*>(s_x + (piece >> 3) * kRow + (piece & 7) * 4) = px[q];
+    }
+#pragma unroll
+    for (int q = 0; q < WP; ++q) {
+      const int piece = tid + kThreads * q;
+      if (piece < EROWS * 8) *reinterpret_cast<u32x4_t*>(s_w + (piece >> 3) * kRow + (piece & 7) * 4) = pw[q];
     }
     __syncthreads();
-    if (kc + kChunk < dw) load_chunk(kc + kChunk);
-    float part[4][EPT];
+    if (c + 1 < c1) MOE_LOAD_CHUNK(c + 1);
+    float pt[TPT][EPT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TPT; ++i)
 #pragma unroll
-      for (int j = 0; j < EPT; ++j) part[i][j] = 0.f;
+      for (int j = 0; j < EPT; ++j) pt[i][j] = 0.f;
 #pragma unroll
     for (int q = 0; q < kChunk / 4; ++q) {
-      u32x4_t xv[4], wv[EPT];
+      u32x4_t xv[TPT], wv[EPT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const u32x4_t*>(s_x + (tg + 8 * i) * kRow + q * 4);
+      for (int i = 0; i < TPT; ++i) xv[i] = *reinterpret_cast<const u32x4_t*>(s_x + (tg + TG * i) * kRow + q * 4);
 #pragma unroll
-      for (int j = 0; j < EPT; ++j) wv[j] = *reinterpret_cast<const u32x4_t*>(s_w + (eg + 32 * j) * kRow + q * 4);
+      for (int j = 0; j < EPT; ++j) wv[j] = *reinterpret_cast<const u32x4_t*>(s_w + (eg + EG * j) * kRow + q * 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TPT; ++i)
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
-          float a = part[i][j];
+          float a = pt[i][j];
           a = mac<BF16>(xv[i].x, wv[j].x, a);
           a = mac<BF16>(xv[i].y, wv[j].y, a);
           a = mac<BF16>(xv[i].z, wv[j].z, a);
           a = mac<BF16>(xv[i].w, wv[j].w, a);
-          part[i][j] = a;
+          pt[i][j] = a;
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TPT; ++i)
 #pragma unroll
-      for (int j = 0; j < EPT; ++j) acc[i][j] += part[i][j];
+      for (int j = 0; j < EPT; ++j) acc[i][j] += pt[i][j];
   }
+#undef MOE_LOAD_CHUNK
 
-  // ---- logits to LDS (reusing the W staging area)
-  __syncthreads();
-  float* s_log = reinterpret_cast<float*>(s_w);
+  float* out = part + (size_t)split * N * E;
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int e = eg + 32 * j;
-    if (e < E) {
-      const float lb = logit_bias ? logit_bias[e] : 0.f;
+  for (int i = 0; i < TPT; ++i) {
+    const int t = t0 + tg + TG * i;
+    if (t >= N) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_log[(tg + 8 * i) * LROW + e] = acc[i][j] + lb;
+    for (int j = 0; j < EPT; ++j) {
+      const int e = eg + EG * j;
+      if (e < E) out[(size_t)t * E + e] = acc[i][j];
     }
   }
-  __syncthreads();
+}
 
-  // ---- softmax, selection score, top-k, renormalise: one wavefront per token
+// ---------------------------------------------------------------- 2. select
+
+template <int EL>  // experts per lane: E <= 64 * EL
+__global__ __launch_bounds__(kThreads) void select_kernel(
+    const float* __restrict__ part, int splits, const float* __restrict__ logit_bias,
+    const float* __restrict__ select_bias, int N, int E, int k, int renorm, int tpb,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, double* __restrict__ partials) {
+  __shared__ double s_part[kThreads / kWave][64 * EL];
+  const int tid = threadIdx.x;
   const int wv = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.x * tpb;
   double pacc[EL];
-  float sb[EL];
+  float lb[EL], sb[EL];
 #pragma unroll
   for (int m = 0; m < EL; ++m) {
     const int e = lane + kWave * m;
     pacc[m] = 0.0;
+    lb[m] = (logit_bias && e < E) ? logit_bias[e] : 0.f;
     sb[m] = (select_bias && e < E) ? select_bias[e] : 0.f;
   }
-  for (int tt = wv; tt < kTok; tt += kThreads / kWave) {
+  const size_t split_stride = (size_t)N * E;
+  for (int tt = wv; tt < tpb; tt += kThreads / kWave) {
     const int t = t0 + tt;
     if (t >= N) break;
     float v[EL], p[EL], s[EL];
@@ -171,8 +196,23 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 #pragma unroll
     for (int m = 0; m < EL; ++m) {
       const int e = lane + kWave * m;
-      v[m] = (e < E) ? s_log[tt * LROW + e] : -INFINITY;
-      mx = fmaxf(mx, v[m]);
+      float l = -INFINITY;
+      if (e < E) {
+        // splits added in split order; loaded 8 at a time so the loads overlap
+        const float* src = part + (size_t)t * E + e;
+        l = 0.f;
+        for (int q0 = 0; q0 < splits; q0 += 8) {
+          float b[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) b[u] = (q0 + u < splits) ? src[(size_t)(q0 + u) * split_stride] : 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (q0 + u < splits) l += b[u];
+        }
+        l += lb[m];
+      }
+      v[m] = l;
+      mx = fmaxf(mx, l);
     }
     mx = wave_max(mx);
     float sum = 0.f;
@@ -227,13 +267,9 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
       topk_w[(size_t)t * k + lane] = renorm ? mine_p / sel_sum : mine_p;
     }
   }
-
-  // ---- per-workgroup probability sums, waves combined in a fixed order
+  // per-workgroup probability sums, waves combined in a fixed order
 #pragma unroll
-  for (int m = 0; m < EL; ++m) {
-    const int e = lane + kWave * m;
-    if (e < EROWS) s_part[wv][e] = pacc[m];
-  }
+  for (int m = 0; m < EL; ++m) s_part[wv][lane + kWave * m] = pacc[m];
   __syncthreads();
   for (int e = tid; e < E; e += kThreads) {
     double a = s_part[0][e];
@@ -243,50 +279,105 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   }
 }
 
-// prob_sum[e] = sum over workgroups b (in order) of partials[b][e].
-__global__ __launch_bounds__(256) void prob_sum_kernel(const double* __restrict__ partials, int nb,
-                                                       int E, double* __restrict__ prob_sum) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+// ---------------------------------------------------------------- 3. prob_sum
+
+// prob_sum[e] = sum over select workgroups b of partials[b][e]: lane l adds
+// b = l, l+64, ... in order, then a butterfly adds the 64 lane sums.
+__global__ __launch_bounds__(kThreads) void prob_sum_kernel(const double* __restrict__ partials,
+                                                           int nb, int E, double* __restrict__ prob_sum) {
+  const int e = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (e >= E) return;
   double a = 0.0;
-  for (int b = 0; b < nb; ++b) a += partials[(size_t)b * E + e];
-  prob_sum[e] = a;
+  for (int b = lane; b < nb; b += kWave) a += partials[(size_t)b * E + e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+  if (lane == 0) prob_sum[e] = a;
 }
 
-template <bool BF16, int EPT>
-void launch_router_t(const moe_shape& s, const void* x, const void* w, const float* lb,
-                     const float* sb, int32_t* idx, float* tw, double* partials, hipStream_t st) {
-  const int nb = route_blocks(s);
+// ---------------------------------------------------------------- launch
+
+struct LogitsPlan {
+  int eg, ept, tpt, tt, tiles, splits, chunks_per_split;
+};
+
+LogitsPlan plan_logits(const moe_shape& s) {
+  LogitsPlan L;
+  const int E = s.n_experts;
+  if (E <= 8) { L.eg = 8; L.ept = 1; L.tpt = 4; }
+  else if (E <= 32) { L.eg = 32; L.ept = 1; L.tpt = 4; }
+  else if (E <= 64) { L.eg = 32; L.ept = 2; L.tpt = 4; }
+  else if (E <= 128) { L.eg = 32; L.ept = 4; L.tpt = 4; }
+  else if (E <= 256) { L.eg = 32; L.ept = 8; L.tpt = 4; }
+  else { L.eg = 32; L.ept = 16; L.tpt = 2; }
+  L.tt = (kThreads / L.eg) * L.tpt;
+  L.tiles = (s.n_tokens + L.tt - 1) / L.tt;
+  const int dw = s.dtype == MOE_DTYPE_BF16 ? s.d_model / 2 : s.d_model;
+  const int nchunks = dw / kChunk;
+  // enough workgroups to fill the chip, each with at least two chunks of K
+  int splits = (kTargetBlocks + L.tiles - 1) / std::max(1, L.tiles);
+  splits = std::max(1, std::min({splits, 64, nchunks / 2}));
+  L.chunks_per_split = (nchunks + splits - 1) / splits;
+  L.splits = (nchunks + L.chunks_per_split - 1) / L.chunks_per_split;
+  return L;
+}
+
+template <bool BF16, int EG, int EPT, int TPT>
+void launch_logits_t(const moe_shape& s, const LogitsPlan& L, const void* x, const void* w,
+                     float* part, hipStream_t st) {
   const int dw = BF16 ? s.d_model / 2 : s.d_model;
-  hipLaunchKernelGGL((router_kernel<BF16, EPT>), dim3(nb), dim3(kThreads), 0, st,
-                     static_cast<const uint32_t*>(x), static_cast<const uint32_t*>(w), lb, sb,
-                     s.n_tokens, dw, s.n_experts, s.top_k, s.renormalize, idx, tw, partials);
+  hipLaunchKernelGGL((logits_kernel<BF16, EG, EPT, TPT>), dim3(L.tiles, L.splits), dim3(kThreads), 0, st,
+                     static_cast<const uint32_t*>(x), static_cast<const uint32_t*>(w), s.n_tokens, dw,
+                     s.n_experts, L.chunks_per_split, part);
 }
 
 template <bool BF16>
-void launch_router_e(const moe_shape& s, const void* x, const void* w, const float* lb,
-                     const float* sb, int32_t* idx, float* tw, double* partials, hipStream_t st) {
-  const int need = (s.n_experts + 31) / 32;
-  if (need <= 1) launch_router_t<BF16, 1>(s, x, w, lb, sb, idx, tw, partials, st);
-  else if (need <= 2) launch_router_t<BF16, 2>(s, x, w, lb, sb, idx, tw, partials, st);
-  else if (need <= 4) launch_router_t<BF16, 4>(s, x, w, lb, sb, idx, tw, partials, st);
-  else if (need <= 8) launch_router_t<BF16, 8>(s, x, w, lb, sb, idx, tw, partials, st);
-  else launch_router_t<BF16, 16>(s, x, w, lb, sb, idx, tw, partials, st);
+void launch_logits(const moe_shape& s, const LogitsPlan& L, const void* x, const void* w, float* part,
+                   hipStream_t st) {
+  if (L.eg == 8) launch_logits_t<BF16, 8, 1, 4>(s, L, x, w, part, st);
+  else if (L.ept == 1) launch_logits_t<BF16, 32, 1, 4>(s, L, x, w, part, st);
+  else if (L.ept == 2) launch_logits_t<BF16, 32, 2, 4>(s, L, x, w, part, st);
+  else if (L.ept == 4) launch_logits_t<BF16, 32, 4, 4>(s, L, x, w, part, st);
+  else if (L.ept == 8) launch_logits_t<BF16, 32, 8, 4>(s, L, x, w, part, st);
+  else launch_logits_t<BF16, 32, 16, 2>(s, L, x, w, part, st);
 }
 
 }  // namespace
 
-int route_blocks(const moe_shape& s) { return (s.n_tokens + kTok - 1) / kTok; }
+// tokens per select workgroup: enough workgroups (>= 256) at small N, 32 at most
+int select_tpb(const moe_shape& s) {
+  return std::max(4, std::min(kSelTokMax, (s.n_tokens / 256) / 4 * 4));
+}
+
+int route_blocks(const moe_shape& s) {
+  const int tpb = select_tpb(s);
+  return (s.n_tokens + tpb - 1) / tpb;
+}
+
+size_t route_logits_floats(const moe_shape& s) {
+  const LogitsPlan L = plan_logits(s);
+  return (size_t)L.splits * s.n_tokens * s.n_experts;
+}
 
 int launch_route(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                  const float* select_bias, int32_t* topk_idx, float* topk_w, double* prob_sum,
-                 double* partials, hipStream_t stream) {
-  if (s.dtype == MOE_DTYPE_BF16)
-    launch_router_e<true>(s, x, w_router, logit_bias, select_bias, topk_idx, topk_w, partials, stream);
-  else
-    launch_router_e<false>(s, x, w_router, logit_bias, select_bias, topk_idx, topk_w, partials, stream);
-  hipLaunchKernelGGL(prob_sum_kernel, dim3((s.n_experts + 255) / 256), dim3(256), 0, stream,
-                     partials, route_blocks(s), s.n_experts, prob_sum);
+                 double* partials, float* logits, hipStream_t stream) {
+  const LogitsPlan L = plan_logits(s);
+  if (s.dtype == MOE_DTYPE_BF16) launch_logits<true>(s, L, x, w_router, logits, stream);
+  else launch_logits<false>(s, L, x, w_router, logits, stream);
+  const int nb = route_blocks(s);
+  const int el = (s.n_experts + kWave - 1) / kWave;
+#define MOE_SELECT(EL_)                                                                          \
+  hipLaunchKernelGGL(select_kernel<EL_>, dim3(nb), dim3(kThreads), 0, stream, logits, L.splits, \
+                     logit_bias, select_bias, s.n_tokens, s.n_experts, s.top_k, s.renormalize,   \
+                     select_tpb(s), topk_idx, topk_w, partials)
+  if (el <= 1) MOE_SELECT(1);
+  else if (el <= 2) MOE_SELECT(2);
+  else if (el <= 4) MOE_SELECT(4);
+  else MOE_SELECT(8);
+#undef MOE_SELECT
+  hipLaunchKernelGGL(prob_sum_kernel, dim3((s.n_experts + 3) / 4), dim3(kThreads), 0, stream,
+                     partials, nb, s.n_experts, prob_sum);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
