@@ -12,17 +12,18 @@
 // The work runs in three kernels, over chunks of kChunk consecutive copies:
 //   1. hist:    a per-chunk expert histogram from LDS atomics. Counting
 //               does not depend on the order of the atomics.
-//   2. scan:    one workgroup.
-//               - For each expert, an exclusive scan over the chunks gives
-//                 the rank of each chunk's first copy within the expert.
-//               - counts = the totals; kept = min(counts, C).
-//               - offsets = exclusive scan of kept.
-//               - The balance statistic, summed in expert order.
-//   3. scatter: one wavefront per chunk, 64 copies at a time, in copy order.
-//               - A copy's rank within its expert = the chunk base
-//                 + the copies of that expert already seen in this chunk
-//                 + the lower lanes of this step with the same expert.
-//               - Lanes with equal experts are matched with ballots.
+//   2. colscan: one wavefront per expert scans the chunk histograms, giving
+//               each chunk's base rank within the expert and the expert's
+//               total count (integer sums, so exact in any order).
+//   3. scatter: one wavefront per chunk.
+//               - It loads the counts and forms kept = min(count, C) and
+//                 offsets = exclusive scan of kept in LDS. Workgroup 0 also
+//                 writes offsets and the balance statistic.
+//               - It then walks its copies 64 at a time, in copy order. A
+//                 copy's rank within its expert = the chunk base + the copies
+//                 of that expert already seen in this chunk + the lower lanes
+//                 of this step with the same expert. Lanes with equal experts
+//                 are matched with ballots.
 //               - Rank < C keeps the copy at offsets[e] + rank.
 // Every output is a pure function of topk_idx: there are no races and no
 // order-dependent atomics.
@@ -48,64 +49,84 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(size_t)blockIdx.x * E + e] = s_h[e];
 }
 
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ hist, int nchunks,
-                                                    int E, int C, int N, int k,
-                                                    int32_t* __restrict__ base,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    const double* __restrict__ prob_sum,
-                                                    double* __restrict__ stat) {
-  __shared__ int32_t s_kept[kMaxExperts];
-  __shared__ int32_t s_cnt[kMaxExperts];
-  __shared__ int32_t s_scan[1024];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int b = 0; b < nchunks; ++b) {
-      base[(size_t)b * E + e] = run;
-      run += hist[(size_t)b * E + e];
-    }
-    counts[e] = run;
-    s_cnt[e] = run;
-    s_kept[e] = (C > 0 && run > C) ? C : run;
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
   }
-  __syncthreads();
-  // inclusive Hillis-Steele scan of kept over e (E <= 1024 = blockDim)
-  int v = tid < E ? s_kept[tid] : 0;
-  s_scan[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int add = tid >= o ? s_scan[tid - o] : 0;
-    __syncthreads();
-    s_scan[tid] += add;
-    __syncthreads();
+  return v;
+}
+
+// One wavefront per expert: base[b][e] = sum_{b' < b} hist[b'][e]; counts[e] = total.
+__global__ __launch_bounds__(256) void colscan_kernel(const int32_t* __restrict__ hist, int nchunks,
+                                                      int E, int32_t* __restrict__ base,
+                                                      int32_t* __restrict__ counts) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (e >= E) return;
+  int run = 0;
+  for (int b0 = 0; b0 < nchunks; b0 += kWave) {
+    const int b = b0 + lane;
+    const int v = b < nchunks ? hist[(size_t)b * E + e] : 0;
+    const int incl = wave_incl_scan(v, lane);
+    if (b < nchunks) base[(size_t)b * E + e] = run + incl - v;
+    run += __shfl(incl, kWave - 1, kWave);
   }
-  if (tid < E) offsets[tid] = s_scan[tid] - v;
-  if (tid == 0) offsets[E] = E > 0 ? s_scan[E - 1] : 0;
-  if (tid == 0 && stat) {
-    // E * sum_e (counts_e / (N k)) (prob_sum_e / N), summed in expert order
-    // (no copies: the statistic is defined as 0)
-    const double nk = (double)N * (double)k, n = (double)N;
-    double a = 0.0;
-    if (N > 0)
-      for (int e = 0; e < E; ++e) a += ((double)s_cnt[e] / nk) * (prob_sum[e] / n);
-    *stat = (double)E * a;
-  }
+  if (lane == 0) counts[e] = run;
 }
 
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ idx, int NK, int E,
-                                                     int C, const int32_t* __restrict__ base,
-                                                     const int32_t* __restrict__ offsets,
+                                                     int C, int N, int k,
+                                                     const int32_t* __restrict__ base,
+                                                     const int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm,
-                                                     int32_t* __restrict__ slot_pos) {
+                                                     int32_t* __restrict__ slot_pos,
+                                                     const double* __restrict__ prob_sum,
+                                                     double* __restrict__ stat) {
   __shared__ int32_t s_run[kMaxExperts];
-  __shared__ int32_t s_off[kMaxExperts];
+  __shared__ int32_t s_off[kMaxExperts + 1];
   const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += kWave) {
-    s_run[e] = base[(size_t)blockIdx.x * E + e];
-    s_off[e] = offsets[e];
+  // offsets = exclusive scan of kept = min(counts, C), lane l owning experts [l*per, (l+1)*per)
+  const int per = (E + kWave - 1) / kWave;
+  int sum = 0;
+  for (int q = 0; q < per; ++q) {
+    const int e = lane * per + q;
+    if (e < E) {
+      const int c = counts[e];
+      const int kept = (C > 0 && c > C) ? C : c;
+      s_off[e] = kept;
+      sum += kept;
+    }
   }
+  const int incl = wave_incl_scan(sum, lane);
+  int run = incl - sum;
+  for (int q = 0; q < per; ++q) {
+    const int e = lane * per + q;
+    if (e < E) {
+      const int kept = s_off[e];
+      s_off[e] = run;
+      run += kept;
+    }
+  }
+  if (lane == kWave - 1) s_off[E] = incl;
+  for (int e = lane; e < E; e += kWave) s_run[e] = base[(size_t)blockIdx.x * E + e];
   __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int e = lane; e <= E; e += kWave) offsets[e] = s_off[e];
+    if (stat) {
+      // E * sum_e (counts_e / (N k)) (prob_sum_e / N): lane-strided sums, then a fixed butterfly
+      // (no copies: the statistic is defined as 0)
+      const double nk = (double)N * (double)k, n = (double)N;
+      double a = 0.0;
+      if (N > 0)
+        for (int e = lane; e < E; e += kWave) a += ((double)counts[e] / nk) * (prob_sum[e] / n);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+      if (lane == 0) *stat = (double)E * a;
+    }
+  }
   const int c0 = blockIdx.x * kChunk;
   const int c1 = min(NK, c0 + kChunk);
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes below this one
@@ -141,6 +162,15 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   }
 }
 
+__global__ void empty_kernel(int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                             double* __restrict__ stat) {
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+    if (e < E) counts[e] = 0;
+    offsets[e] = 0;
+  }
+  if (threadIdx.x == 0 && stat) *stat = 0.0;
+}
+
 }  // namespace
 
 int permute_chunks(const moe_shape& s) {
@@ -154,13 +184,15 @@ int launch_permute(const moe_shape& s, const int32_t* topk_idx, const double* pr
   const int NK = s.n_tokens * s.top_k;
   const int nch = permute_chunks(s);
   const int C = s.capacity > 0 ? s.capacity : 0;
-  if (nch > 0)
-    hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(256), 0, stream, topk_idx, NK, s.n_experts, hist);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, hist, nch, s.n_experts, C,
-                     s.n_tokens, s.top_k, base, counts, offsets, prob_sum, balance_stat);
-  if (nch > 0)
-    hipLaunchKernelGGL(scatter_kernel, dim3(nch), dim3(kWave), 0, stream, topk_idx, NK,
-                       s.n_experts, C, base, offsets, perm, slot_pos);
+  const int E = s.n_experts;
+  if (nch == 0) {  // no copies
+    hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(256), 0, stream, E, counts, offsets, balance_stat);
+  } else {
+    hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(256), 0, stream, topk_idx, NK, E, hist);
+    hipLaunchKernelGGL(colscan_kernel, dim3((E + 3) / 4), dim3(256), 0, stream, hist, nch, E, base, counts);
+    hipLaunchKernelGGL(scatter_kernel, dim3(nch), dim3(kWave), 0, stream, topk_idx, NK, E, C,
+                       s.n_tokens, s.top_k, base, counts, offsets, perm, slot_pos, prob_sum, balance_stat);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
