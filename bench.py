@@ -176,7 +176,19 @@ def main():
     ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device-to-device copy 3 times (calibrates the HBM byte counters)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "reps": 3}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this MoE layer build has no multi-GPU path "

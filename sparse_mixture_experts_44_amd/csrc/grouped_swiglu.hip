@@ -498,10 +498,13 @@ int grid_for(long long ub, int per_cu) {
   return (int)((g + kXcds - 1) / kXcds * kXcds);
 }
 
+// per_cu: workgroups launched per CU at most. 1 is a persistent grid; a
+// large value launches about one workgroup per tile, and the dispatcher then
+// balances uneven tile counts (the down projection has few, long tiles).
 template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB = 1>
-void launch_mfma(const GroupedParams& p, int phase, hipStream_t st) {
+void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) {
   const int BH = phase == 1 ? BN / 2 : BN;
-  const int grid = grid_for(tiles_upper_bound(p, phase, BM, BH), MINB);
+  const int grid = grid_for(tiles_upper_bound(p, phase, BM, BH), per_cu);
   if (phase == 1)
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, true>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
@@ -522,8 +525,8 @@ int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream) {
   } else {
     // tile height from the mean routed rows per expert segment
     const long long avg = (long long)p.set[0].max_rows / std::max(1, p.set[0].n_groups);
-    if (avg >= 128) launch_mfma<256, 256, 64, 2, 4, 2>(p, phase, stream);
-    else launch_mfma<64, 256, 64, 1, 4, 3>(p, phase, stream);
+    if (avg >= 128) launch_mfma<256, 256, 64, 2, 4, 2>(p, phase, phase == 1 ? 1 : 64, stream);
+    else launch_mfma<64, 256, 64, 1, 4, 3>(p, phase, 1, stream);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
