@@ -14,7 +14,9 @@ It prints one JSON line:
   bf16 MFMA peak;
 * cpu_baseline: the CPU oracle timed on a bounded sample of the same
   workload, on this host's cores;
-* extras: layer TFLOP/s and algorithmic GB/s.
+* extras: layer TFLOP/s and algorithmic GB/s, and cold-cache reps (each
+  after a 1 GiB write that evicts L2 and the Infinity Cache; median, min,
+  max), outside the timed region.
 """
 from __future__ import annotations
 
@@ -176,6 +178,9 @@ def main():
     ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="extra untimed-region reps, each after a 1 GiB write that evicts L2 and the "
+                         "Infinity Cache; reported as layer.cold (median/min/max)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -232,6 +237,24 @@ def main():
         step_ms.append(ev.elapsed_ms(6 * i, 6 * i + 5))
     avg = {s: float(np.mean(v)) for s, v in stage_ms.items()}
 
+    # Cold-cache reps: a 1 GiB write before each rep leaves no weights in L2 or
+    # the 256 MB Infinity Cache; each rep is timed by its own stage events.
+    cold = None
+    if args.cold_reps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cev = HipEvents(6 * args.cold_reps)
+        for i in range(args.cold_reps):
+            flush.fill_(i & 0xFF)
+            L.forward(xd, stage_events=cev.ev[6 * i: 6 * i + 6])
+        torch.cuda.synchronize()
+        rep_ms = [cev.elapsed_ms(6 * i, 6 * i + 5) for i in range(args.cold_reps)]
+        cstage = {s: float(np.median([cev.elapsed_ms(6 * i + j, 6 * i + j + 1) for i in range(args.cold_reps)]))
+                  for j, s in enumerate(moe.STAGES)}
+        cold = {"reps": args.cold_reps, "flush_bytes": 1 << 30, "ms_median": float(np.median(rep_ms)),
+                "ms_min": float(np.min(rep_ms)), "ms_max": float(np.max(rep_ms)), "stage_ms_median": cstage,
+                "tokens_per_s_median": cfg.n_tokens / (float(np.median(rep_ms)) * 1e-3)}
+        del flush
+
     counts = L.out.counts.cpu().numpy()
     offs = L.out.offsets.cpu().numpy()
     kept = np.diff(offs)
@@ -259,7 +282,7 @@ def main():
                   "hbm_frac": work["bytes"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
                   "event_ms_per_step": float(np.mean(step_ms)), "stage_ms": avg,
                   "touched_experts": work["touched"], "kept_copies": work["kept"],
-                  "balance_stat": float(L.out.balance_stat.item())},
+                  "balance_stat": float(L.out.balance_stat.item()), "cold": cold},
     }
     if not args.no_cpu_baseline:
         del L, xd

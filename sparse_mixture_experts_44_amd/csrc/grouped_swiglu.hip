@@ -173,8 +173,10 @@ __device__ __forceinline__ int swz(int row) {
 // would drain all copies in flight (vmcnt(0)) before each fragment read,
 // which defeats the multi-stage prefetch. The instruction has no output
 // registers; the explicit vmcnt waits below order the reads after the copies.
+// On gfx9 an LDS copy needs one wait state after a scalar write of M0 (the
+// compiler inserts it for the builtin, not inside inline asm): hence the nop.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
                "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory", "m0");
 }
@@ -248,8 +250,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     const int mt = (rows + BM - 1) / BM;
     const int local = T - tab.cum[ent];
     const int ntile = local / mt, mtile = local - ntile * mt;
-    const int m0 = mtile * BM;
-    const int mvalid = min(BM, rows - m0);
+    // A segment of `rows` rows takes mt = ceil(rows / BM) m-tiles: either BM
+    // rows each and a short last one, or (balance_m) an even split, so that
+    // the tiles sharing a weight tile take the same time.
+    const int m0 = p.balance_m ? (int)((long long)mtile * rows / mt) : mtile * BM;
+    const int mvalid = p.balance_m ? (int)((long long)(mtile + 1) * rows / mt) - m0 : min(BM, rows - m0);
     const int n0 = ntile * BH;
     const int F = S.d_ff;
     const int K = P1 ? d : F;
@@ -498,9 +503,9 @@ int grid_for(long long ub, int per_cu) {
   return (int)((g + kXcds - 1) / kXcds * kXcds);
 }
 
-// per_cu: workgroups launched per CU at most. 1 is a persistent grid; a
-// large value launches about one workgroup per tile, and the dispatcher then
-// balances uneven tile counts (the down projection has few, long tiles).
+// per_cu: workgroups launched per CU at most. 1 is a persistent grid (each
+// workgroup walks the tile list with stride gridDim.x); a large value
+// launches about one workgroup per tile.
 template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB = 1>
 void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) {
   const int BH = phase == 1 ? BN / 2 : BN;
@@ -525,8 +530,15 @@ int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream) {
   } else {
     // tile height from the mean routed rows per expert segment
     const long long avg = (long long)p.set[0].max_rows / std::max(1, p.set[0].n_groups);
-    if (avg >= 128) launch_mfma<256, 256, 64, 2, 4, 2>(p, phase, phase == 1 ? 1 : 64, stream);
-    else launch_mfma<64, 256, 64, 1, 4, 3>(p, phase, 1, stream);
+    if (avg >= 128) {
+      // persistent grid with even m-tiles: the workgroups that share a weight
+      // tile run in step, so their copies of it hit in L2
+      GroupedParams q = p;
+      q.balance_m = 1;
+      launch_mfma<256, 256, 64, 2, 4, 2>(q, phase, 1, stream);
+    } else {
+      launch_mfma<64, 256, 64, 1, 4, 3>(p, phase, 1, stream);
+    }
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -71,6 +71,7 @@ struct GroupedParams {
   int32_t n_tokens;
   int32_t d_model;
   int32_t dtype;
+  int32_t balance_m;       // 1: split each segment into equal m-tiles (else BM rows and a short last tile)
 };
 
 // Phase 1: h = silu(x Wg^T) * (x Wu^T) per segment; phase 2: out = h Wd^T.
