@@ -169,7 +169,8 @@ int moe_combine(const moe_shape* shape, const float* expert_out, const int32_t* 
  * only when S == 0.
  * stage_events: NULL, or MOE_STAGE_EVENTS events created by the caller. It
  * records event i before stage i (route, permute, gate|up, down, combine)
- * and the last event after combine, all on `stream`. */
+ * and the last event after combine, all on `stream`. A NULL entry is
+ * skipped (each recorded event costs the stream a few microseconds). */
 int moe_forward(const moe_shape* shape, const void* x, const void* w_router,
                 const float* logit_bias, const float* select_bias,
                 const void* w_gate, const void* w_up, const void* w_down,

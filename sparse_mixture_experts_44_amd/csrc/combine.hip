@@ -2,21 +2,26 @@
 // of "混合专家 MoE" (anrans ai-infra handbook), which forward_grouped
 // computes with index_add_.
 //
-// This is a gather instead of atomics. One workgroup per token reads its k
-// expert rows (through slot_pos) and its shared-expert rows. It adds them in
-// a fixed order (slot 0 .. k-1, then shared 0 .. S-1) and writes y once with
-// 16-byte stores. The result is bit-reproducible. A dropped copy
-// (slot_pos -1) adds nothing, and a row with nothing to add is exactly +0.
+// This is a gather instead of atomics. Workgroup (t, c) sums a 1024-column
+// slice of token t: its k expert rows (through slot_pos), then its
+// shared-expert rows. They are added in a fixed order (slot 0 .. k-1, then
+// shared 0 .. S-1) and y is written once with 16-byte stores. The result is
+// bit-reproducible. A dropped copy (slot_pos -1) adds nothing, and a row with
+// nothing to add is exactly +0. The rows of one batch of slots are loaded
+// together before they are added, so the loads overlap.
 #include "moe_common.h"
 
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ O,
-                                                      const int32_t* __restrict__ slot_pos,
-                                                      const float* __restrict__ w,
-                                                      const float4* __restrict__ shared, int S,
-                                                      int N, int d4, int k, float4* __restrict__ y) {
+constexpr int kThreads = 256;
+constexpr int kBatch = 8;  // slots loaded together
+
+__global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restrict__ O,
+                                                           const int32_t* __restrict__ slot_pos,
+                                                           const float* __restrict__ w,
+                                                           const float4* __restrict__ shared, int S,
+                                                           int N, int d4, int k, float4* __restrict__ y) {
   __shared__ int32_t s_slot[kMaxTopK];
   __shared__ float s_w[kMaxTopK];
   const int t = blockIdx.x;
@@ -25,27 +30,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
     s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < d4; c += blockDim.x) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int sp = s_slot[j];
-      if (sp < 0) continue;
-      const float4 o = O[(size_t)sp * d4 + c];
-      const float wj = s_w[j];
-      a.x = fmaf(wj, o.x, a.x);
-      a.y = fmaf(wj, o.y, a.y);
-      a.z = fmaf(wj, o.z, a.z);
-      a.w = fmaf(wj, o.w, a.w);
+  const int c = blockIdx.y * kThreads + threadIdx.x;
+  if (c >= d4) return;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < k; j0 += kBatch) {
+    float4 o[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int sp = j0 + u < k ? s_slot[j0 + u] : -1;
+      o[u] = sp >= 0 ? O[(size_t)sp * d4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int s = 0; s < S; ++s) {
-      const float4 o = shared[((size_t)s * N + t) * d4 + c];
-      a.x += o.x;
-      a.y += o.y;
-      a.z += o.z;
-      a.w += o.w;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (j0 + u >= k || s_slot[j0 + u] < 0) continue;
+      const float wj = s_w[j0 + u];
+      a.x = fmaf(wj, o[u].x, a.x);
+      a.y = fmaf(wj, o[u].y, a.y);
+      a.z = fmaf(wj, o[u].z, a.z);
+      a.w = fmaf(wj, o[u].w, a.w);
     }
-    y[(size_t)t * d4 + c] = a;
   }
+  for (int s = 0; s < S; ++s) {
+    const float4 o = shared[((size_t)s * N + t) * d4 + c];
+    a.x += o.x;
+    a.y += o.y;
+    a.z += o.z;
+    a.w += o.w;
+  }
+  y[(size_t)t * d4 + c] = a;
 }
 
 }  // namespace
@@ -53,7 +65,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
 int launch_combine(const moe_shape& s, const float* expert_out, const int32_t* slot_pos,
                    const float* topk_w, const float* shared_out, float* y, hipStream_t stream) {
   if (s.n_tokens == 0) return MOE_OK;
-  hipLaunchKernelGGL(combine_kernel, dim3(s.n_tokens), dim3(256), 0, stream,
+  const int d4 = s.d_model / 4;
+  hipLaunchKernelGGL(combine_kernel, dim3(s.n_tokens, (d4 + kThreads - 1) / kThreads), dim3(kThreads), 0, stream,
                      reinterpret_cast<const float4*>(expert_out), slot_pos, topk_w,
                      reinterpret_cast<const float4*>(shared_out), shared_out ? s.n_shared : 0,
                      s.n_tokens, s.d_model / 4, s.top_k, reinterpret_cast<float4*>(y));

@@ -300,11 +300,19 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     const uint32_t a_lds0 = lds_addr(&s_tile[0][(wave * A_INS) * 1024]);
     const uint32_t b_lds0 = lds_addr(&s_tile[0][STAGE_A + (wave * B_INS) * 1024]);
 
+    // A copies whose RPI rows all lie past the segment are skipped: those LDS
+    // rows keep stale data, which only reaches output rows that are never
+    // stored (an MFMA output row depends on its own A row alone). Skipping
+    // makes the copy count per wave vary, so it is done only with two stages,
+    // where every wait is for all of this wave's copies (vmcnt(0)).
+    const int a_act = NS == 2 ? min(A_INS, max(0, (mvalid + RPI - 1) / RPI - wave * A_INS)) : A_INS;
+
     auto issue = [&](int kt) {
       const int st = kt % NS;
       const int ko = kt * BK;
 #pragma unroll
-      for (int i = 0; i < A_INS; ++i) dma16(a_base + a_off[i] + ko, a_lds0 + st * STAGE + i * 1024);
+      for (int i = 0; i < A_INS; ++i)
+        if (i < a_act) dma16(a_base + a_off[i] + ko, a_lds0 + st * STAGE + i * 1024);
 #pragma unroll
       for (int i = 0; i < B_INS; ++i) dma16(b_base + b_off[i] + ko, b_lds0 + st * STAGE + i * 1024);
     };

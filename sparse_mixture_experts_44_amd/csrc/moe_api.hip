@@ -200,7 +200,7 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
 
   auto mark = [&](int i) {
-    if (stage_events) hipEventRecord(stage_events[i], stream);
+    if (stage_events && stage_events[i]) hipEventRecord(stage_events[i], stream);
   };
   mark(0);
   if ((st = do_route(s, x, w_router, logit_bias, select_bias, topk_idx, topk_w, prob_sum, ws, stream)))

@@ -7,8 +7,9 @@
 // Three kernels:
 //   1. logits_kernel: a VALU GEMM (the matrix cores are kept for the expert
 //      GEMMs).
-//      - Grid: (token tile) x (K split), sized to give every CU more than one
-//        workgroup also at decode sizes (N = 64).
+//      - Grid: (token tile) x (K split) x (expert tile), sized to give every
+//        CU more than one workgroup also at decode sizes (N = 64). At most 8
+//        K splits; few tokens get one output per thread and expert tiles.
 //      - K is staged through LDS 128 bytes per row at a time. Rows are padded
 //        to 144 bytes, so 16-byte reads from consecutive rows use distinct
 //        banks.
@@ -36,8 +37,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 32;         // dwords per row chunk: 64 bf16 or 32 fp32
 constexpr int kRow = kChunk + 4;   // padded LDS row stride in dwords
-constexpr int kSelTokMax = 32;     // tokens per select workgroup, at most (8 per wave)
+constexpr int kSelTokMax = 8;      // tokens per select workgroup, at most (2 per wave)
 constexpr int kTargetBlocks = 512; // logits workgroups to aim for
+constexpr int kMaxSplits = 8;      // K splits of the logits, at most
+constexpr int kFewTiles = 64;      // fewer token tiles than this: split the experts over workgroups
 
 template <bool BF16>
 __device__ __forceinline__ float mac(uint32_t a, uint32_t b, float c) {
@@ -48,6 +51,11 @@ __device__ __forceinline__ float mac(uint32_t a, uint32_t b, float c) {
     return fmaf(__uint_as_float(a), __uint_as_float(b), c);
   }
 }
+
+// Workgroup barrier after this wave's LDS accesses have completed. Unlike
+// __syncthreads it does not wait for global loads in flight (the prefetched
+// chunks).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -65,7 +73,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Thread grid: EG expert groups x (256/EG) token groups. Thread (tg, eg) owns
 // tokens tg + TG*i (i < TPT) and experts eg + EG*j (j < EPT).
-template <bool BF16, int EG, int EPT, int TPT>
+template <bool BF16, int EG, int EPT, int TPT, int PD>
 __global__ __launch_bounds__(kThreads) void logits_kernel(const uint32_t* __restrict__ x,
                                                           const uint32_t* __restrict__ w, int N,
                                                           int dw, int E, int chunks_per_split,
@@ -82,6 +90,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const uint32_t* __rest
   const int eg = tid % EG, tg = tid / EG;
   const int t0 = blockIdx.x * TT;
   const int split = blockIdx.y;
+  const int e0 = blockIdx.z * EROWS;  // first expert of this workgroup's expert tile
   const int nchunks = dw / kChunk;
   const int c0 = split * chunks_per_split;
   const int c1 = min(nchunks, c0 + chunks_per_split);
@@ -92,65 +101,73 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const uint32_t* __rest
 #pragma unroll
     for (int j = 0; j < EPT; ++j) acc[i][j] = 0.f;
 
-  u32x4_t px[XP], pw[WP];
+  // PD chunks in flight per thread: slot u of the ring holds chunk c0 + PD*i + u
+  u32x4_t px[PD][XP], pw[PD][WP];
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-#define MOE_LOAD_CHUNK(C)                                                                 \
+#define MOE_LOAD_CHUNK(C, U)                                                              \
   {                                                                                       \
     const int kc_ = (C) * kChunk;                                                         \
     _Pragma("unroll") for (int q = 0; q < XP; ++q) {                                      \
       const int piece = tid + kThreads * q, r = piece >> 3, pc = piece & 7;               \
       const int t = t0 + r;                                                               \
-      px[q] = (r < TT && t < N) ? *reinterpret_cast<const u32x4_t*>(x + (size_t)t * dw + kc_ + pc * 4) : zero; \
+      px[U][q] = (r < TT && t < N) ? *reinterpret_cast<const u32x4_t*>(x + (size_t)t * dw + kc_ + pc * 4) : zero; \
     }                                                                                     \
     _Pragma("unroll") for (int q = 0; q < WP; ++q) {                                      \
       const int piece = tid + kThreads * q, er = piece >> 3, pc = piece & 7;              \
-      pw[q] = (er < EROWS && er < E) ? *reinterpret_cast<const u32x4_t*>(w + (size_t)er * dw + kc_ + pc * 4) : zero; \
+      pw[U][q] = (er < EROWS && e0 + er < E) ? *reinterpret_cast<const u32x4_t*>(w + (size_t)(e0 + er) * dw + kc_ + pc * 4) : zero; \
     }                                                                                     \
   }
 
-  if (c0 < c1) MOE_LOAD_CHUNK(c0);
-  for (int c = c0; c < c1; ++c) {
-    __syncthreads();  // everyone finished reading the previous chunk
 #pragma unroll
-    for (int q = 0; q < XP; ++q) {
-      const int piece = tid + kThreads * q;
-      if (piece < TT * 8) *reinterpret_cast<u32x4_t*>(s_x + (piece >> 3) * kRow + (piece & 7) * 4) = px[q];
-    }
+  for (int u = 0; u < PD; ++u)
+    if (c0 + u < c1) MOE_LOAD_CHUNK(c0 + u, u);
+  for (int cb = c0; cb < c1; cb += PD) {
 #pragma unroll
-    for (int q = 0; q < WP; ++q) {
-      const int piece = tid + kThreads * q;
-      if (piece < EROWS * 8) *reinterpret_cast<u32x4_t*>(s_w + (piece >> 3) * kRow + (piece & 7) * 4) = pw[q];
-    }
-    __syncthreads();
-    if (c + 1 < c1) MOE_LOAD_CHUNK(c + 1);
-    float pt[TPT][EPT];
+    for (int u = 0; u < PD; ++u) {
+      const int c = cb + u;
+      if (c >= c1) break;
+      lds_barrier();  // everyone finished reading the previous chunk
 #pragma unroll
-    for (int i = 0; i < TPT; ++i)
+      for (int q = 0; q < XP; ++q) {
+        const int piece = tid + kThreads * q;
+        if (piece < TT * 8) *reinterpret_cast<u32x4_t*>(s_x + (piece >> 3) * kRow + (piece & 7) * 4) = px[u][q];
+      }
 #pragma unroll
-      for (int j = 0; j < EPT; ++j) pt[i][j] = 0.f;
-#pragma unroll
-    for (int q = 0; q < kChunk / 4; ++q) {
-      u32x4_t xv[TPT], wv[EPT];
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) xv[i] = *reinterpret_cast<const u32x4_t*>(s_x + (tg + TG * i) * kRow + q * 4);
-#pragma unroll
-      for (int j = 0; j < EPT; ++j) wv[j] = *reinterpret_cast<const u32x4_t*>(s_w + (eg + EG * j) * kRow + q * 4);
+      for (int q = 0; q < WP; ++q) {
+        const int piece = tid + kThreads * q;
+        if (piece < EROWS * 8) *reinterpret_cast<u32x4_t*>(s_w + (piece >> 3) * kRow + (piece & 7) * 4) = pw[u][q];
+      }
+      lds_barrier();
+      if (c + PD < c1) MOE_LOAD_CHUNK(c + PD, u);
+      float pt[TPT][EPT];
 #pragma unroll
       for (int i = 0; i < TPT; ++i)
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-          float a = pt[i][j];
-          a = mac<BF16>(xv[i].x, wv[j].x, a);
-          a = mac<BF16>(xv[i].y, wv[j].y, a);
-          a = mac<BF16>(xv[i].z, wv[j].z, a);
-          a = mac<BF16>(xv[i].w, wv[j].w, a);
-          pt[i][j] = a;
-        }
+        for (int j = 0; j < EPT; ++j) pt[i][j] = 0.f;
+#pragma unroll
+      for (int q = 0; q < kChunk / 4; ++q) {
+        u32x4_t xv[TPT], wv[EPT];
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) xv[i] = *reinterpret_cast<const u32x4_t*>(s_x + (tg + TG * i) * kRow + q * 4);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) wv[j] = *reinterpret_cast<const u32x4_t*>(s_w + (eg + EG * j) * kRow + q * 4);
+#pragma unroll
+        for (int i = 0; i < TPT; ++i)
+#pragma unroll
+          for (int j = 0; j < EPT; ++j) {
+            float a = pt[i][j];
+            a = mac<BF16>(xv[i].x, wv[j].x, a);
+            a = mac<BF16>(xv[i].y, wv[j].y, a);
+            a = mac<BF16>(xv[i].z, wv[j].z, a);
+            a = mac<BF16>(xv[i].w, wv[j].w, a);
+            pt[i][j] = a;
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < TPT; ++i)
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) acc[i][j] += pt[i][j];
     }
-#pragma unroll
-    for (int i = 0; i < TPT; ++i)
-#pragma unroll
-      for (int j = 0; j < EPT; ++j) acc[i][j] += pt[i][j];
   }
 #undef MOE_LOAD_CHUNK
 
@@ -161,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const uint32_t* __rest
     if (t >= N) continue;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-      const int e = eg + EG * j;
+      const int e = e0 + eg + EG * j;
       if (e < E) out[(size_t)t * E + e] = acc[i][j];
     }
   }
@@ -298,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void prob_sum_kernel(const double* __rest
 // ---------------------------------------------------------------- launch
 
 struct LogitsPlan {
-  int eg, ept, tpt, tt, tiles, splits, chunks_per_split;
+  int eg, ept, tpt, tt, tiles, etiles, splits, chunks_per_split;
 };
 
 LogitsPlan plan_logits(const moe_shape& s) {
@@ -312,11 +329,24 @@ LogitsPlan plan_logits(const moe_shape& s) {
   else { L.eg = 32; L.ept = 16; L.tpt = 2; }
   L.tt = (kThreads / L.eg) * L.tpt;
   L.tiles = (s.n_tokens + L.tt - 1) / L.tt;
+  L.etiles = 1;
+  if (L.tiles < kFewTiles) {
+    // few tokens: one expert (or 8) per thread and one token per thread, and
+    // the experts split over workgroups, so that the chip fills with few K
+    // splits (the select kernel adds the splits one by one)
+    L.eg = E <= 8 ? 8 : 32;
+    L.ept = 1;
+    L.tpt = 1;
+    L.tt = kThreads / L.eg;
+    L.tiles = (s.n_tokens + L.tt - 1) / L.tt;
+    L.etiles = (E + L.eg - 1) / L.eg;
+  }
   const int dw = s.dtype == MOE_DTYPE_BF16 ? s.d_model / 2 : s.d_model;
   const int nchunks = dw / kChunk;
   // enough workgroups to fill the chip, each with at least two chunks of K
-  int splits = (kTargetBlocks + L.tiles - 1) / std::max(1, L.tiles);
-  splits = std::max(1, std::min({splits, 64, nchunks / 2}));
+  const int tiles = std::max(1, L.tiles * L.etiles);
+  int splits = (kTargetBlocks + tiles - 1) / tiles;
+  splits = std::max(1, std::min({splits, kMaxSplits, nchunks / 2}));
   L.chunks_per_split = (nchunks + splits - 1) / splits;
   L.splits = (nchunks + L.chunks_per_split - 1) / L.chunks_per_split;
   return L;
@@ -326,7 +356,8 @@ template <bool BF16, int EG, int EPT, int TPT>
 void launch_logits_t(const moe_shape& s, const LogitsPlan& L, const void* x, const void* w,
                      float* part, hipStream_t st) {
   const int dw = BF16 ? s.d_model / 2 : s.d_model;
-  hipLaunchKernelGGL((logits_kernel<BF16, EG, EPT, TPT>), dim3(L.tiles, L.splits), dim3(kThreads), 0, st,
+  constexpr int PD = TPT == 1 ? 4 : 1;  // one output per thread: registers to spare for prefetch
+  hipLaunchKernelGGL((logits_kernel<BF16, EG, EPT, TPT, PD>), dim3(L.tiles, L.splits, L.etiles), dim3(kThreads), 0, st,
                      static_cast<const uint32_t*>(x), static_cast<const uint32_t*>(w), s.n_tokens, dw,
                      s.n_experts, L.chunks_per_split, part);
 }
@@ -334,7 +365,10 @@ void launch_logits_t(const moe_shape& s, const LogitsPlan& L, const void* x, con
 template <bool BF16>
 void launch_logits(const moe_shape& s, const LogitsPlan& L, const void* x, const void* w, float* part,
                    hipStream_t st) {
-  if (L.eg == 8) launch_logits_t<BF16, 8, 1, 4>(s, L, x, w, part, st);
+  if (L.tpt == 1) {
+    if (L.eg == 8) launch_logits_t<BF16, 8, 1, 1>(s, L, x, w, part, st);
+    else launch_logits_t<BF16, 32, 1, 1>(s, L, x, w, part, st);
+  } else if (L.eg == 8) launch_logits_t<BF16, 8, 1, 4>(s, L, x, w, part, st);
   else if (L.ept == 1) launch_logits_t<BF16, 32, 1, 4>(s, L, x, w, part, st);
   else if (L.ept == 2) launch_logits_t<BF16, 32, 2, 4>(s, L, x, w, part, st);
   else if (L.ept == 4) launch_logits_t<BF16, 32, 4, 4>(s, L, x, w, part, st);
