@@ -39,7 +39,20 @@ What pins each function (in tests/test_oracle_*.py):
 * balance statistic: uniform gives 1, one-hot gives E, and the handbook's
   skewed case gives exactly 4;
 * bf16_round: nearest-value brute force over every bf16 pattern, and torch's
-  fp32 -> bf16 cast.
+  fp32 -> bf16 cast;
+* FP8 expert weights: decode against torch's float8_e4m3fn for all 256 codes;
+  encode against a nearest-code brute force and torch's cast; per-row
+  quantisation against its invariants (the row maximum maps to 448, the
+  dequantised error is within half a code step) and a dense layer rebuilt
+  from the dequantised weights.
+
+FP8 expert weights (a W8A16 variant for decode) follow the remark in section
+"推理视角" of the handbook that DeepSeek-V3 ships its weights in FP8. The page
+names no format and no scale granularity. The readings: OCP FP8 E4M3
+(e4m3fn: bias 7, largest 448, no infinities), one fp32 scale per output row
+of each weight matrix (scale = row max |w| / 448), codes by round-to-nearest-
+even of w / scale, both divisions in fp32. The quantised layer is the bf16
+layer with every expert weight replaced by scale * decode(code).
 
 Parity unpinned: y on general random inputs has no printed value on any page.
 It rests on the special cases above and on the per-token and grouped forms
@@ -58,6 +71,68 @@ F64 = np.float64
 # ---------------------------------------------------------------- rounding
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+# ---------------------------------------------------------------- FP8 (E4M3) weights
+
+FP8_MAX = 448.0          # largest finite e4m3fn value: 1.75 * 2**8
+_FP8_MIN_NORMAL = 2.0 ** -6
+_FP8_SUB_STEP = 2.0 ** -9  # code step below the smallest normal
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Values of e4m3fn codes (fp64): sign bit 7, exponent bits 6..3 with bias
+    7, mantissa bits 2..0; exponent 0 is subnormal (m * 2**-9); 0x7F and 0xFF
+    are NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * _FP8_SUB_STEP, (1.0 + m / 8.0) * np.exp2(e.astype(F64) - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def fp8_e4m3_encode(v) -> np.ndarray:
+    """Round float values to the nearest e4m3fn code, ties to the even code,
+    the sign bit copied from the input;
+    magnitudes that round above 448 saturate to 448 (this quantisation never
+    produces them: |w / scale| <= 448 up to one fp32 rounding)."""
+    a = np.abs(np.asarray(v, dtype=F64))
+    neg = np.signbit(np.asarray(v, dtype=F64))
+    # code step: 2**(exponent - 3) for normal magnitudes, 2**-9 below 2**-6
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))          # a = f * 2**ex, f in [0.5, 1)
+    step = np.where(a >= _FP8_MIN_NORMAL, np.exp2((ex - 1 - 3).astype(F64)), _FP8_SUB_STEP)
+    q = np.rint(a / step) * step                       # exact: a / step is a scaled binary value
+    q = np.minimum(q, FP8_MAX)
+    # value -> code
+    sub = q < _FP8_MIN_NORMAL
+    m_sub = np.rint(q / _FP8_SUB_STEP).astype(np.int64)   # 0..8 (8 is the smallest normal)
+    _, qe = np.frexp(np.where(q > 0, q, 1.0))
+    e_field = (qe - 1 + 7).astype(np.int64)
+    m_norm = np.rint((q / np.exp2((qe - 1).astype(F64)) - 1.0) * 8.0).astype(np.int64)
+    code = np.where(sub, m_sub, (e_field << 3) | m_norm)
+    code = np.where(neg, code | 0x80, code)  # the sign bit follows the input's (-0 and tiny negatives: 0x80)
+    return code.astype(np.uint8)
+
+
+def quantize_fp8_rows(w) -> tuple:
+    """Per-output-row FP8 quantisation of one weight matrix [rows, cols]:
+    scale_r = fp32(max_c |w[r, c]|) / 448 in fp32; code = e4m3(fp32(w / scale_r));
+    an all-zero row has scale 0 and codes 0. Returns (codes uint8, scales fp32)."""
+    w32 = np.asarray(w, dtype=np.float32)
+    amax = np.max(np.abs(w32), axis=1)
+    scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    ratio = (w32 / safe[:, None]).astype(np.float32)
+    codes = fp8_e4m3_encode(ratio)
+    codes[scale == 0] = 0
+    return codes, scale
+
+
+def dequantize_fp8_rows(codes, scales) -> np.ndarray:
+    """scale_r * decode(code) in fp64 (exact)."""
+    return fp8_e4m3_decode(codes) * np.asarray(scales, dtype=F64)[:, None]
+
 
 
 def bf16_round(a) -> np.ndarray:

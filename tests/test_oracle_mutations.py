@@ -112,3 +112,20 @@ def test_bf16_truncation_is_caught(monkeypatch):
         return np.ldexp(np.trunc(m * 256) / 256, e)
     monkeypatch.setattr(O, "bf16_round", bad)
     _fails(pins.test_bf16_round_matches_torch_on_fp32)
+
+
+def test_fp8_ties_away_from_zero_is_caught(monkeypatch):
+    orig = O.fp8_e4m3_encode
+
+    def bad(v):
+        a = np.asarray(v, dtype=F64)
+        # nudge every magnitude up by a hair: ties now round away from zero
+        return orig(np.sign(a) * np.nextafter(np.abs(a), np.inf))
+    monkeypatch.setattr(O, "fp8_e4m3_encode", bad)
+    _fails(pins.test_fp8_encode_is_nearest_even_bruteforce)
+
+
+def test_fp8_scale_per_column_is_caught(monkeypatch):
+    orig = O.quantize_fp8_rows
+    monkeypatch.setattr(O, "quantize_fp8_rows", lambda w: tuple(a.T if a.ndim == 2 else a for a in orig(np.asarray(w).T)))
+    _fails(pins.test_fp8_row_quantisation_invariants)

@@ -392,3 +392,88 @@ def test_exercise_parameter_count():
     active = g["top_k"] * per * g["layers"]
     assert round(total / 1e9, 2) == g["total_billions_2dp"]
     assert round(active / 1e9, 2) == g["active_billions_2dp"]
+
+
+# ------------------------------------------------------------------ FP8 (E4M3) expert weights
+
+def _fp8_finite_values():
+    """The 127 finite non-negative e4m3fn values, ascending (from torch's decode)."""
+    v = torch.arange(128, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    return v[~np.isnan(v)]
+
+
+def test_fp8_decode_matches_torch_all_codes():
+    c = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy()
+    got = O.fp8_e4m3_decode(c)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[fin], ref[fin])
+    np.testing.assert_array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    assert O.fp8_e4m3_decode(np.uint8(0x7E)) == O.FP8_MAX
+
+
+def test_fp8_encode_is_nearest_even_bruteforce():
+    vals = _fp8_finite_values()                   # 0 .. 448, code i <-> vals[i]
+    rng = np.random.default_rng(30)
+    a = np.concatenate([
+        rng.uniform(0, 464, 20000),
+        rng.standard_normal(20000) * np.exp2(rng.uniform(-14, 8, 20000)),
+        (vals[:-1] + vals[1:]) / 2,                 # every exact tie between neighbours
+        vals,                                      # every value itself
+    ])
+    a = a[np.abs(a) <= 464]
+    codes = O.fp8_e4m3_encode(a)
+    m = np.abs(a)
+    j = np.clip(np.searchsorted(vals, m), 1, len(vals) - 1)   # vals[j-1] < m <= vals[j]
+    lo, hi = vals[j - 1], vals[j]
+    dlo, dhi = m - lo, hi - m
+    lo_even = ((j - 1) % 2) == 0                  # even code <-> even mantissa
+    near = np.where(dlo < dhi, j - 1, np.where(dhi < dlo, j, np.where(lo_even, j - 1, j)))
+    near = np.where(m == hi, j, near)
+    near = np.where(m > vals[-1], len(vals) - 1, near)  # (448, 464]: saturate to 448
+    np.testing.assert_array_equal(codes & 0x7F, near)
+    np.testing.assert_array_equal((codes >> 7).astype(bool), np.signbit(a))
+
+
+def test_fp8_encode_matches_torch_cast():
+    rng = np.random.default_rng(31)
+    v = (rng.standard_normal(100000) * np.exp2(rng.uniform(-14, 8, 100000))).astype(np.float32)
+    v = v[np.abs(v) <= 448]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.fp8_e4m3_encode(v), ref)
+
+
+def test_fp8_row_quantisation_invariants():
+    rng = np.random.default_rng(32)
+    w = mi.bf16_bits_to_f32(mi.f32_to_bf16_bits((rng.standard_normal((64, 96)) *
+                                                 np.exp2(rng.uniform(-8, 4, (64, 1)))).astype(np.float32)))
+    w[5] = 0.0                                     # an all-zero row
+    codes, scale = O.quantize_fp8_rows(w)
+    assert codes.dtype == np.uint8 and scale.dtype == np.float32
+    assert scale[5] == 0 and not codes[5].any()
+    deq = O.dequantize_fp8_rows(codes, scale)
+    nz = scale > 0
+    # the largest magnitude of each row maps to the largest code
+    amax_col = np.argmax(np.abs(w), axis=1)
+    assert np.all(np.abs(O.fp8_e4m3_decode(codes[np.arange(64), amax_col]))[nz] == O.FP8_MAX)
+    # error within half a code step of the scaled value (normal: 2**-4 relative; subnormal: 2**-10 * scale)
+    ratio = np.abs(w.astype(np.float64)) / np.where(nz, scale, 1.0)[:, None]
+    half_step = np.where(ratio >= 2.0 ** -6, np.exp2(np.floor(np.log2(np.maximum(ratio, 1e-300))) - 4), 2.0 ** -10)
+    err = np.abs(deq - w) / np.where(nz, scale, 1.0)[:, None]
+    assert np.all(err[nz] <= half_step[nz] * (1 + 1e-6) + 1e-7 * ratio[nz])
+
+
+def test_fp8_layer_is_dense_ffn_with_dequantised_weights():
+    # E=1, k=1 with FP8 weights: the dense SwiGLU FFN on weights decoded by torch's float8_e4m3fn
+    rng = np.random.default_rng(33)
+    N, d, f = 17, 32, 48
+    x = rng.standard_normal((N, d))
+    wg, wu, wd, _ = rand_layer(rng, 1, d, f)
+    deq, tdeq = [], []
+    for w in (wg[0], wu[0], wd[0]):
+        c, s = O.quantize_fp8_rows(w)
+        deq.append(O.dequantize_fp8_rows(c, s)[None])
+        tdeq.append(torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy() * s.astype(np.float64)[:, None])
+    lr = O.moe_layer(x, rng.standard_normal((1, d)), deq[0], deq[1], deq[2], 1)
+    np.testing.assert_allclose(lr.y, torch_swiglu(x, tdeq[0], tdeq[1], tdeq[2]), rtol=1e-12, atol=1e-13)
