@@ -46,15 +46,20 @@ def expert_params(d_model: int, d_ff: int) -> int:
 
 
 WORKLOADS = {
-    # name -> (moe_inputs config, description)
-    "mixtral": ("mixtral", "Mixtral-shaped prefill: N=4096 d=4096 d_ff=14336 E=8 k=2, bf16"),
-    "dsv3_prefill": ("dsv3_prefill", "DeepSeek-V3-shaped prefill: N=8192 d=7168 d_ff=2048 E=256 k=8 +1 shared, bf16"),
-    "dsv3_decode": ("dsv3_decode", "DeepSeek-V3-shaped decode: N=64 d=7168 d_ff=2048 E=256 k=8 +1 shared, bf16"),
-    "switch_cap": ("switch_cap", "Switch-style top-1 with capacity 160: N=16384 d=2048 d_ff=8192 E=128, bf16"),
+    # name -> (moe_inputs config, description, expert weight format, roofline bound of the gate|up kernel)
+    "mixtral": ("mixtral", "Mixtral-shaped prefill: N=4096 d=4096 d_ff=14336 E=8 k=2, bf16", "bf16", "mfma"),
+    "dsv3_prefill": ("dsv3_prefill", "DeepSeek-V3-shaped prefill: N=8192 d=7168 d_ff=2048 E=256 k=8 +1 shared, bf16",
+                     "bf16", "mfma"),
+    "dsv3_decode": ("dsv3_decode", "DeepSeek-V3-shaped decode: N=64 d=7168 d_ff=2048 E=256 k=8 +1 shared, bf16",
+                    "bf16", "hbm"),
+    "dsv3_decode_fp8": ("dsv3_decode", "DeepSeek-V3-shaped decode with FP8 (E4M3, per-row scale) expert weights: "
+                        "N=64 d=7168 d_ff=2048 E=256 k=8 +1 shared, bf16 activations", "fp8", "hbm"),
+    "switch_cap": ("switch_cap", "Switch-style top-1 with capacity 160: N=16384 d=2048 d_ff=8192 E=128, bf16",
+                   "bf16", "hbm"),
 }
 
 
-def algorithmic_work(cfg, counts, kept):
+def algorithmic_work(cfg, counts, kept, weights="bf16"):
     """Work the method must do, from the real routing.
 
     The returned dict holds:
@@ -64,6 +69,7 @@ def algorithmic_work(cfg, counts, kept):
       weights each), the shared experts, fp32 y, and idx/w (8 bytes per copy);
     * bytes_gate_up: what the gate|up kernel must move: x, the gate and up
       weights of the touched experts (and the shared ones), and bf16 h out.
+    FP8 expert weights count 1 byte per weight plus a 4-byte scale per row.
     """
     import numpy as np
     d, F, E, N, k = cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.n_tokens, cfg.top_k
@@ -73,9 +79,13 @@ def algorithmic_work(cfg, counts, kept):
     touched = int(np.sum(np.asarray(kept) > 0))
     fl_gu = 2 * d * 2 * F * n_kept + S * N * 2 * d * 2 * Fs
     fl_dn = 2 * F * d * n_kept + S * N * 2 * Fs * d
-    w_bytes = touched * expert_params(d, F) * b + S * expert_params(d, Fs) * b
+    bw = 1 if weights == "fp8" else b                         # bytes per expert weight
+    rs = 4 if weights == "fp8" else 0                         # bytes per weight row (its scale)
+    w_bytes = (touched * (expert_params(d, F) * bw + (2 * F + d) * rs)
+               + S * (expert_params(d, Fs) * bw + (2 * Fs + d) * rs))
     byts = N * d * b + E * d * b + w_bytes + N * d * 4 + N * k * 8
-    by_gu = N * d * b + (touched * 2 * F * d + S * 2 * Fs * d) * b + (n_kept * F + S * N * Fs) * b
+    by_gu = (N * d * b + (touched * 2 * F * d + S * 2 * Fs * d) * bw + (touched * 2 * F + S * 2 * Fs) * rs
+             + (n_kept * F + S * N * Fs) * b)
     return dict(flops_gate_up=fl_gu, flops_down=fl_dn, flops=fl_gu + fl_dn, bytes=byts,
                 bytes_gate_up=by_gu, touched=touched, kept=n_kept)
 
@@ -121,13 +131,15 @@ def measured_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, layer, x, budget_s=20.0):
+def cpu_baseline(cfg, layer, x, budget_s=20.0, weights="bf16"):
     """The oracle as it stands (grouped fp64 form) on the first rows of the workload.
 
     The sample grows from 16 rows, doubling, until one run takes about a
     tenth of the budget. It is then scaled to fill about the budget. The time
     covers routing of the sample, grouping, the fp64 upcast of each touched
     expert, the expert products and the combine. Input generation is left out.
+    With FP8 weights each touched expert is quantised and dequantised by the
+    oracle on the way (its form of the FP8 layer).
     """
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -146,6 +158,8 @@ def cpu_baseline(cfg, layer, x, budget_s=20.0):
                 self.a = a
 
             def __getitem__(self, e):
+                if weights == "fp8":
+                    return O.dequantize_fp8_rows(*O.quantize_fp8_rows(mi.bf16_bits_to_f32(self.a[e])))
                 return mi.to_f64(self.a[e])
 
             def __len__(self):
@@ -209,13 +223,15 @@ def main():
     import sparse_mixture_experts_44_amd as moe
     from sparse_mixture_experts_44_amd.layer import MoELayer, to_device
 
-    cfg_name, desc = WORKLOADS[args.workload]
+    cfg_name, desc, weights, bound = WORKLOADS[args.workload]
     cfg = mi.CONFIGS[cfg_name]
     t = time.time()
     layer, x = mi.make_layer(cfg), mi.make_x(cfg)
     print(f"# inputs generated in {time.time() - t:.1f}s", file=sys.stderr, flush=True)
     dev = "cuda:0"
     L = MoELayer.from_numpy(moe.shape_for(cfg), layer, dev)
+    if weights == "fp8":
+        L.quantize_fp8()  # one-off conversion on the device, before any timing
     xd = to_device(x, dev)
     torch.cuda.synchronize()
 
@@ -269,11 +285,16 @@ def main():
     counts = L.out.counts.cpu().numpy()
     offs = L.out.offsets.cpu().numpy()
     kept = np.diff(offs)
-    work = algorithmic_work(cfg, counts, kept)
+    work = algorithmic_work(cfg, counts, kept, weights)
     ms_step = wall / K * 1e3
     tok_s = cfg.n_tokens * K / wall
     gu_s = gate_up_ms * 1e-3
-    achieved_tf = work["flops_gate_up"] / gu_s / 1e12
+    if bound == "mfma":
+        achieved, peak, unit, per_launch = work["flops_gate_up"] / gu_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", \
+            {"algorithmic_flops_per_launch": work["flops_gate_up"]}
+    else:
+        achieved, peak, unit, per_launch = work["bytes_gate_up"] / gu_s / 1e9, PEAK_HBM_GBS, "GB/s", \
+            {"algorithmic_bytes_per_launch": work["bytes_gate_up"]}
     traffic = measured_traffic(args.workload)
 
     out = {
@@ -282,11 +303,10 @@ def main():
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, shapes of the pages' models)",
         "config": {"workload": desc, "tokens": cfg.n_tokens, "d_model": cfg.d_model,
                    "d_ff": cfg.d_ff, "experts": cfg.n_experts, "top_k": cfg.top_k,
-                   "shared": cfg.n_shared, "capacity": cfg.capacity},
-        "roofline": {"kernel": "grouped gate|up (phase 1)", "bound": "mfma", "achieved": achieved_tf,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "avg_launch_ms": gate_up_ms,
-                     "algorithmic_flops_per_launch": work["flops_gate_up"]},
+                   "shared": cfg.n_shared, "capacity": cfg.capacity, "expert_weights": weights},
+        "roofline": {"kernel": "grouped gate|up (phase 1)", "bound": bound, "achieved": achieved,
+                     "peak": peak, "unit": unit, "frac": achieved / peak,
+                     "traffic": traffic, "avg_launch_ms": gate_up_ms, **per_launch},
         "layer": {"tflops": work["flops"] / (ms_step * 1e-3) / 1e12,
                   "mfma_frac": work["flops"] / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                   "algorithmic_GBs": work["bytes"] / (ms_step * 1e-3) / 1e9,
@@ -299,7 +319,7 @@ def main():
     if not args.no_cpu_baseline:
         del L, xd
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(cfg, layer, x, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(cfg, layer, x, args.cpu_budget, weights)
     print(json.dumps(out), flush=True)
 
 

@@ -180,6 +180,59 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router,
                 double* prob_sum, double* balance_stat,
                 void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
 
+/* ---------------------------------------------------------------------
+ * FP8 expert weights (W8A16), for decode, whose time is the time to read
+ * the touched experts' weights ("推理视角" section: DeepSeek-V3 ships FP8
+ * weights). The page names no format or scale granularity; these calls use
+ * OCP FP8 E4M3 codes (e4m3fn: exponent bias 7, largest 448, no infinities)
+ * with one fp32 scale per output row of each weight matrix. The layer they
+ * compute is the bf16 layer with every expert weight replaced by
+ * scale[row] * decode(code). x, the router and h stay bf16; the shape's
+ * dtype must be MOE_DTYPE_BF16 (else MOE_ERR_UNSUPPORTED).
+ * --------------------------------------------------------------------- */
+
+/* Row scales of the FP8 expert weights (device pointers, fp32). */
+typedef struct {
+  const float* gate;    /* [E, F]: scale of w_gate row (e, f) */
+  const float* up;      /* [E, F] */
+  const float* down;    /* [E, d] */
+  const float* s_gate;  /* [S, Fs]; NULL allowed only when S == 0 */
+  const float* s_up;    /* [S, Fs] */
+  const float* s_down;  /* [S, d] */
+} moe_fp8_scales;
+
+/* Quantise a bf16 matrix [rows, cols], row by row:
+ *   scales[r]   = max_c |w[r, c]| / 448                     (fp32 division)
+ *   codes[r, c] = E4M3 round-to-nearest-even of w[r, c] / scales[r]
+ *                 (fp32 division; the sign bit follows the quotient's)
+ * An all-zero row gets scale 0 and codes 0. A stacked [E, F, d] weight is
+ * rows = E*F, cols = d.
+ *   w_bf16 [rows, cols] bf16 in;  codes [rows, cols] uint8 out;  scales [rows] fp32 out
+ * cols must be a multiple of 64 and rows < 2^31 (else MOE_ERR_UNSUPPORTED). */
+int moe_quantize_fp8(int64_t rows, int32_t cols, const void* w_bf16, uint8_t* codes, float* scales,
+                     hipStream_t stream);
+
+/* moe_grouped_swiglu with FP8 weights: w_gate/w_up [G, F, d] and w_down
+ * [G, d, F] are E4M3 codes; sc_gate/sc_up [G, F] and sc_down [G, d] their
+ * row scales. Everything else as in moe_grouped_swiglu (bf16 x and h). */
+int moe_grouped_swiglu_fp8(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const void* x,
+                           const int32_t* perm, int32_t rows_per_token, const int32_t* offsets,
+                           int32_t max_rows, const uint8_t* w_gate, const uint8_t* w_up,
+                           const uint8_t* w_down, const float* sc_gate, const float* sc_up,
+                           const float* sc_down, float* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* moe_forward with FP8 routed and shared expert weights (codes) and their
+ * row scales. The router weights stay bf16. Outputs, workspace and events
+ * as in moe_forward. */
+int moe_forward_fp8(const moe_shape* shape, const void* x, const void* w_router,
+                    const float* logit_bias, const float* select_bias, const uint8_t* w_gate,
+                    const uint8_t* w_up, const uint8_t* w_down, const uint8_t* s_gate,
+                    const uint8_t* s_up, const uint8_t* s_down, const moe_fp8_scales* scales,
+                    float* y, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                    int32_t* perm, int32_t* slot_pos, double* prob_sum, double* balance_stat,
+                    void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,6 +30,8 @@
 // fp32 path: a plain LDS-tiled SIMT kernel for fp32 layers.
 #include <math.h>
 
+#include <type_traits>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -45,6 +47,9 @@ struct SetView {  // the fields of one SegSet, picked with selects rather than a
   const void* wg;
   const void* wu;
   const void* wd;
+  const float* sg;  // FP8 weights: row scales
+  const float* su;
+  const float* sd;
   void* h;
   float* out;
 };
@@ -57,6 +62,9 @@ __device__ __forceinline__ SetView pick(const GroupedParams& p, int si) {
   v.wg = si ? p.set[1].w_gate : p.set[0].w_gate;
   v.wu = si ? p.set[1].w_up : p.set[0].w_up;
   v.wd = si ? p.set[1].w_down : p.set[0].w_down;
+  v.sg = si ? p.set[1].sc_gate : p.set[0].sc_gate;
+  v.su = si ? p.set[1].sc_up : p.set[0].sc_up;
+  v.sd = si ? p.set[1].sc_down : p.set[0].sc_down;
   v.h = si ? p.set[1].h : p.set[0].h;
   v.out = si ? p.set[1].out : p.set[0].out;
   return v;
@@ -194,15 +202,49 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// wait_vm_barrier<n> for a wave-uniform n in [0, MAXN] known only at run time
+// (a chain of scalar compares; anything out of range waits for everything).
+template <int MAXN>
+__device__ __forceinline__ void wait_vm_barrier_rt(int n) {
+  if constexpr (MAXN == 0) {
+    wait_vm_barrier<0>();
+  } else {
+    if (n == MAXN) wait_vm_barrier<MAXN>();
+    else wait_vm_barrier_rt<MAXN - 1>(n);
+  }
+}
+
+// FP8 E4M3 -> bf16 for 8 codes (bytes of lo, then hi): the conversion to fp32
+// is exact, and so is keeping the high half of each fp32 (an e4m3 value has
+// 4 significant bits).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), e = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  constexpr uint32_t kHighHalves = 0x07060302u;  // v_perm: {src1[31:16], src0[31:16]}
+  u32x4_t r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), kHighHalves);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), kHighHalves);
+  r.z = __builtin_amdgcn_perm(__float_as_uint(c.y), __float_as_uint(c.x), kHighHalves);
+  r.w = __builtin_amdgcn_perm(__float_as_uint(e.y), __float_as_uint(e.x), kHighHalves);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
 // One grouped GEMM launch (phase 1: gate|up + SiLU*up -> H; phase 2: down -> O).
 // Workgroup tile BM x BN x BK with NS LDS stages, filled by direct global->LDS
 // copies issued NS-1 steps ahead. WGM x WGN waves; wave tile (BM/WGM) x
 // (BN/WGN) of v_mfma_f32_32x32x16_bf16 blocks with fp32 accumulators.
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB, bool P1>
+// W8: the weights (B) are FP8 E4M3 codes. They are copied to LDS as codes
+// (half the bytes), widened to bf16 exactly as each fragment is read, and
+// each output column is multiplied by its weight row's scale in the epilogue.
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB, bool W8, bool P1>
 __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(GroupedParams p) {
-  constexpr int ROWB = BK * 2;        // LDS bytes per tile row
-  constexpr int PPR = BK / 8;         // 16-byte pieces per row
-  constexpr int RPI = kWave / PPR;    // rows per 1 KB copy instruction
+  using BT = typename std::conditional<W8, uint8_t, bf16_t>::type;  // weight element
+  constexpr int ROWA = BK * 2;                // LDS bytes per A row (bf16)
+  constexpr int ROWB = BK * (int)sizeof(BT);  // LDS bytes per B row
+  constexpr int PPA = ROWA / 16, PPB = ROWB / 16;        // 16-byte pieces per row
+  constexpr int RPIA = kWave / PPA, RPIB = kWave / PPB;  // rows per 1 KB copy instruction
+  constexpr int EPP = 16 / (int)sizeof(BT);   // B elements per 16-byte piece
   constexpr int TM = BM / WGM;        // rows per wave
   constexpr int FM = TM / 32;
   constexpr int BH = P1 ? BN / 2 : BN;  // output columns per tile
@@ -211,14 +253,15 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
   constexpr int NB = P1 ? 2 * FN : FN;  // B fragments per k16 step
   constexpr int WAVES = WGM * WGN;
   constexpr int NT = WAVES * kWave;
-  constexpr int A_INS = BM / RPI / WAVES;  // copy instructions per wave per stage
-  constexpr int B_INS = BN / RPI / WAVES;
-  constexpr int L = A_INS + B_INS;         // vector-memory ops per wave per stage
-  constexpr int STAGE_A = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  constexpr int A_INS = BM / RPIA / WAVES;  // copy instructions per wave per stage
+  constexpr int B_INS = BN / RPIB / WAVES;
+  constexpr int L = A_INS + B_INS;          // vector-memory ops per wave per stage
+  constexpr int STAGE_A = BM * ROWA, STAGE = STAGE_A + BN * ROWB;
   static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(!W8 || BK == 64, "FP8 weights: 64-byte rows");
   static_assert(A_INS >= 1 && B_INS >= 1 && FM >= 1 && FN >= 1 && NS >= 2 && NS <= 6, "tile shape");
-  static_assert(A_INS * RPI * WAVES == BM && B_INS * RPI * WAVES == BN, "copy slots cover the tile");
-  static_assert(!P1 || (BN / 2) % (RPI * B_INS) == 0, "a wave's B rows come from one matrix");
+  static_assert(A_INS * RPIA * WAVES == BM && B_INS * RPIB * WAVES == BN, "copy slots cover the tile");
+  static_assert(!P1 || (BN / 2) % (RPIB * B_INS) == 0, "a wave's B rows come from one matrix");
 
   __shared__ __attribute__((aligned(1024))) uint8_t s_tile[NS][STAGE];
   __shared__ TableLds tab;
@@ -237,9 +280,10 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
   const int total = build_table<BM, NT>(p, nt0, nt1, tab, reinterpret_cast<int*>(&s_tile[0][0]));
   const bf16_t* __restrict__ xg = static_cast<const bf16_t*>(p.x);
 
-  // Copy slots: instruction i of this wave fills tile rows (wave*INS + i)*RPI + lane/PPR;
-  // lane writes LDS piece (lane % PPR), so it fetches logical piece (lane % PPR) ^ swz(row).
-  const int crow = lane / PPR, cpc = lane % PPR;
+  // Copy slots: instruction i of this wave fills tile rows (wave*INS + i)*RPI + lane/PP;
+  // lane writes LDS piece (lane % PP), so it fetches logical piece (lane % PP) ^ swz(row).
+  const int crowA = lane / PPA, cpcA = lane % PPA;
+  const int crowB = lane / PPB, cpcB = lane % PPB;
 
   for (int T = xcd_block(); T < total; T += gridDim.x) {
     const int ent = find_entry(tab.cum, nent, T);
@@ -267,7 +311,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     uint32_t a_off[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-      const int r = (wave * A_INS + i) * RPI + crow;
+      const int r = (wave * A_INS + i) * RPIA + crowA;
       const int rr = r < mvalid ? r : 0;
       const int row = start + m0 + rr;
       uint32_t src;
@@ -278,34 +322,35 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
       } else {
         src = (uint32_t)row * (uint32_t)F;
       }
-      a_off[i] = src + ((cpc ^ swz<PPR>(r)) << 3);
+      a_off[i] = src + ((cpcA ^ swz<PPA>(r)) << 3);
     }
     // ---- B sources: weight rows n0 + (tile row within its matrix); rows past
     // the last output column (partial n-tile) re-read an in-range row.
     const int lastq = min(BH, ncols - n0) - 1;
-    const bf16_t* b_base;
+    const BT* b_base;
     if constexpr (P1) {
-      const bool up = wave * B_INS * RPI >= BN / 2;
-      b_base = static_cast<const bf16_t*>(up ? S.wu : S.wg) + (size_t)g * F * d;
+      const bool up = wave * B_INS * RPIB >= BN / 2;
+      b_base = static_cast<const BT*>(up ? S.wu : S.wg) + (size_t)g * F * d;
     } else {
-      b_base = static_cast<const bf16_t*>(S.wd) + (size_t)g * d * F;
+      b_base = static_cast<const BT*>(S.wd) + (size_t)g * d * F;
     }
     uint32_t b_off[B_INS];
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
-      const int r = (wave * B_INS + i) * RPI + crow;      // tile row
+      const int r = (wave * B_INS + i) * RPIB + crowB;    // tile row
       const int mr = P1 ? (r % (BN / 2)) : r;              // row within its weight matrix tile
-      b_off[i] = (uint32_t)(n0 + min(mr, lastq)) * (uint32_t)K + ((cpc ^ swz<PPR>(r)) << 3);
+      b_off[i] = (uint32_t)(n0 + min(mr, lastq)) * (uint32_t)K + (uint32_t)((cpcB ^ swz<PPB>(r)) * EPP);
     }
     const uint32_t a_lds0 = lds_addr(&s_tile[0][(wave * A_INS) * 1024]);
     const uint32_t b_lds0 = lds_addr(&s_tile[0][STAGE_A + (wave * B_INS) * 1024]);
 
     // A copies whose RPI rows all lie past the segment are skipped: those LDS
     // rows keep stale data, which only reaches output rows that are never
-    // stored (an MFMA output row depends on its own A row alone). Skipping
-    // makes the copy count per wave vary, so it is done only with two stages,
-    // where every wait is for all of this wave's copies (vmcnt(0)).
-    const int a_act = NS == 2 ? min(A_INS, max(0, (mvalid + RPI - 1) / RPI - wave * A_INS)) : A_INS;
+    // stored (an MFMA output row depends on its own A row alone). Each wave
+    // then issues lw = a_act + B_INS copies per stage (fixed for the tile),
+    // and the waits count in units of lw.
+    const int a_act = min(A_INS, max(0, (mvalid + RPIA - 1) / RPIA - wave * A_INS));
+    const int lw = a_act + B_INS;
 
     auto issue = [&](int kt) {
       const int st = kt % NS;
@@ -331,13 +376,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
 
 #define MOE_K_LOOP(ACTIVE)                                                                       \
     for (int kt = 0; kt < nk; ++kt) {                                                            \
-      /* stage kt has landed once at most (stages issued after it) * L copies are outstanding */ \
+      /* stage kt has landed once at most (stages issued after it) * lw copies are outstanding */ \
+      /* (loads complete in issue order) */                                                      \
       const int later = min(NS - 2, nk - 1 - kt);                                                \
-      if (later >= 4) wait_vm_barrier<4 * L>();                                                 \
-      else if (later == 3) wait_vm_barrier<3 * L>();                                             \
-      else if (later == 2) wait_vm_barrier<2 * L>();                                             \
-      else if (later == 1) wait_vm_barrier<L>();                                                 \
-      else wait_vm_barrier<0>();                                                                 \
+      if constexpr (NS == 2) wait_vm_barrier<0>();                                               \
+      else wait_vm_barrier_rt<(NS - 2) * L>(later * lw);                                         \
       if (kt + NS - 1 < nk) issue(kt + NS - 1); /* refills the stage read in step kt-1 */        \
       const uint8_t* sa = &s_tile[kt % NS][0];                                                   \
       const uint8_t* sb = sa + STAGE_A;                                                          \
@@ -347,14 +390,20 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
         _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                         \
           if (!(ACTIVE(i))) continue;                                                            \
           const int r = wm * TM + i * 32 + (lane & 31);                                          \
-          af[i] = *reinterpret_cast<const bf16x8_t*>(sa + r * ROWB + ((chunk ^ swz<PPR>(r)) << 4)); \
+          af[i] = *reinterpret_cast<const bf16x8_t*>(sa + r * ROWA + ((chunk ^ swz<PPA>(r)) << 4)); \
         }                                                                                        \
         _Pragma("unroll") for (int j = 0; j < NB; ++j) {                                         \
           /* phase 1: fragments [0, FN) are gate rows, [FN, 2 FN) the matching up rows */        \
           const int jj = P1 ? (j % FN) : j;                                                      \
           const int half = P1 ? (j / FN) * (BN / 2) : 0;                                         \
           const int r = half + wn * TN + jj * 32 + (lane & 31);                                  \
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + r * ROWB + ((chunk ^ swz<PPR>(r)) << 4)); \
+          if constexpr (W8) {                                                                    \
+            /* piece ks holds the 16 codes of this k16 step; lanes 32-63 take its upper 8 */     \
+            const u32x2_t q = *reinterpret_cast<const u32x2_t*>(sb + r * ROWB + ((ks ^ swz<PPB>(r)) << 4) + ((lane >> 5) << 3)); \
+            bfr[j] = fp8x8_to_bf16(q.x, q.y);                                                    \
+          } else {                                                                               \
+            bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + r * ROWB + ((chunk ^ swz<PPB>(r)) << 4)); \
+          }                                                                                      \
         }                                                                                        \
         _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                         \
           if (!(ACTIVE(i))) continue;                                                            \
@@ -380,6 +429,21 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
 
     // ---- epilogue. acc[i][j][v]: column (lane & 31), row 8 (v / 4) + 4 (lane / 32) + (v % 4)
     const int col0 = n0 + wn * TN + (lane & 31);  // this lane's first output column
+    // FP8 weights: output column c takes its weight row's scale (gate, up or down row c)
+    float sc0[FN], sc1[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      sc0[j] = sc1[j] = 1.f;
+      if constexpr (W8) {
+        const int c = min(col0 + j * 32, ncols - 1);
+        if constexpr (P1) {
+          sc0[j] = S.sg[(size_t)g * F + c];
+          sc1[j] = S.su[(size_t)g * F + c];
+        } else {
+          sc0[j] = S.sd[(size_t)g * d + c];
+        }
+      }
+    }
     int rbase = wm * TM + 4 * (lane >> 5);
     asm volatile("" : "+v"(rbase));  // per tile: keeps the 64 row offsets from being hoisted (and spilled)
 #pragma unroll
@@ -393,12 +457,14 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
           bf16_t* hrow = static_cast<bf16_t*>(S.h) + row * F + col0;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            if (col0 + j * 32 < ncols) hrow[j * 32] = f32_to_bf16(silu_mul(acc[i][j][v], acc[i][j + FN][v]));
+            if (col0 + j * 32 < ncols)
+              hrow[j * 32] = f32_to_bf16(W8 ? silu_mul(acc[i][j][v] * sc0[j], acc[i][j + FN][v] * sc1[j])
+                                            : silu_mul(acc[i][j][v], acc[i][j + FN][v]));
         } else {
           float* orow = S.out + row * d + col0;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            if (col0 + j * 32 < ncols) orow[j * 32] = acc[i][j][v];
+            if (col0 + j * 32 < ncols) orow[j * 32] = W8 ? acc[i][j][v] * sc0[j] : acc[i][j][v];
         }
       }
     }
@@ -514,16 +580,32 @@ int grid_for(long long ub, int per_cu) {
 // per_cu: workgroups launched per CU at most. 1 is a persistent grid (each
 // workgroup walks the tile list with stride gridDim.x); a large value
 // launches about one workgroup per tile.
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB = 1>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, bool W8, int MINB = 1>
 void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) {
   const int BH = phase == 1 ? BN / 2 : BN;
   const int grid = grid_for(tiles_upper_bound(p, phase, BM, BH), per_cu);
   if (phase == 1)
-    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, true>), dim3(grid),
+    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, W8, true>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, false>), dim3(grid),
+    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, W8, false>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
+}
+
+template <bool W8>
+void launch_bf16_class(const GroupedParams& p, int phase, hipStream_t stream) {
+  // tile height from the mean routed rows per expert segment
+  const long long avg = (long long)p.set[0].max_rows / std::max(1, p.set[0].n_groups);
+  if (avg >= 128) {
+    // persistent grid with even m-tiles: the workgroups that share a weight
+    // tile run in step, so their copies of it hit in L2
+    GroupedParams q = p;
+    q.balance_m = 1;
+    launch_mfma<256, 256, 64, 2, 4, 2, W8>(q, phase, 1, stream);
+  } else {
+    // FP8 weights halve the B stages (80 KB of LDS in all), so two workgroups share a CU
+    launch_mfma<64, 256, 64, 1, 4, 3, W8>(p, phase, W8 ? 2 : 1, stream);
+  }
 }
 
 }  // namespace
@@ -535,18 +617,10 @@ int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream) {
       hipLaunchKernelGGL(grouped_f32_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, p);
     else
       hipLaunchKernelGGL(grouped_f32_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (p.w8) {
+    launch_bf16_class<true>(p, phase, stream);
   } else {
-    // tile height from the mean routed rows per expert segment
-    const long long avg = (long long)p.set[0].max_rows / std::max(1, p.set[0].n_groups);
-    if (avg >= 128) {
-      // persistent grid with even m-tiles: the workgroups that share a weight
-      // tile run in step, so their copies of it hit in L2
-      GroupedParams q = p;
-      q.balance_m = 1;
-      launch_mfma<256, 256, 64, 2, 4, 2>(q, phase, 1, stream);
-    } else {
-      launch_mfma<64, 256, 64, 1, 4, 3>(p, phase, 1, stream);
-    }
+    launch_bf16_class<false>(p, phase, stream);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

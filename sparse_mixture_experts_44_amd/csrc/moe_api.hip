@@ -85,6 +85,50 @@ int do_permute(const moe_shape& s, const int32_t* idx, const double* prob_sum, i
                         reinterpret_cast<int32_t*>(at(ws, L.base)), st);
 }
 
+int grouped_impl(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const void* x,
+                 const int32_t* perm, int32_t rows_per_token, const int32_t* offsets, int32_t max_rows,
+                 const void* w_gate, const void* w_up, const void* w_down, const float* sc_gate,
+                 const float* sc_up, const float* sc_down, float* out, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  if (!shape) return MOE_ERR_INVALID_ARG;
+  const moe_shape& s = *shape;
+  if (s.n_tokens < 0 || s.d_model <= 0 || d_ff <= 0 || n_groups < 1 || max_rows < 0 || rows_per_token < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!offsets || !w_gate || !w_up || !w_down || (max_rows > 0 && (!x || !out || !ws)))
+    return MOE_ERR_INVALID_ARG;
+  if (s.d_model % 64 || d_ff % 64 || n_groups > kMaxTileEntries) return MOE_ERR_UNSUPPORTED;
+  const size_t need = align256((size_t)max_rows * d_ff * esize(s));
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (max_rows == 0 || s.n_tokens == 0) return MOE_OK;
+  GroupedParams p{};
+  p.n_sets = 1;
+  p.x = x;
+  p.n_tokens = s.n_tokens;
+  p.d_model = s.d_model;
+  p.dtype = s.dtype;
+  p.w8 = sc_gate != nullptr;
+  SegSet& S = p.set[0];
+  S.offsets = offsets;
+  S.perm = perm;
+  S.n_groups = n_groups;
+  S.uniform_rows = 0;
+  S.rows_per_token = rows_per_token;
+  S.max_rows = max_rows;
+  S.d_ff = d_ff;
+  S.w_gate = w_gate;
+  S.w_up = w_up;
+  S.w_down = w_down;
+  S.sc_gate = sc_gate;
+  S.sc_up = sc_up;
+  S.sc_down = sc_down;
+  S.h = ws;
+  S.out = out;
+  int st = launch_grouped(p, 1, stream);
+  if (st != MOE_OK) return st;
+  return launch_grouped(p, 2, stream);
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -136,39 +180,29 @@ int moe_grouped_swiglu(const moe_shape* shape, int32_t n_groups, int32_t d_ff, c
                        const int32_t* perm, int32_t rows_per_token, const int32_t* offsets,
                        int32_t max_rows, const void* w_gate, const void* w_up, const void* w_down,
                        float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return grouped_impl(shape, n_groups, d_ff, x, perm, rows_per_token, offsets, max_rows, w_gate, w_up,
+                      w_down, nullptr, nullptr, nullptr, out, ws, ws_bytes, stream);
+}
+
+int moe_grouped_swiglu_fp8(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const void* x,
+                           const int32_t* perm, int32_t rows_per_token, const int32_t* offsets,
+                           int32_t max_rows, const uint8_t* w_gate, const uint8_t* w_up,
+                           const uint8_t* w_down, const float* sc_gate, const float* sc_up,
+                           const float* sc_down, float* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
   if (!shape) return MOE_ERR_INVALID_ARG;
-  const moe_shape& s = *shape;
-  if (s.n_tokens < 0 || s.d_model <= 0 || d_ff <= 0 || n_groups < 1 || max_rows < 0 || rows_per_token < 1)
-    return MOE_ERR_INVALID_ARG;
-  if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
-  if (!offsets || !w_gate || !w_up || !w_down || (max_rows > 0 && (!x || !out || !ws)))
-    return MOE_ERR_INVALID_ARG;
-  if (s.d_model % 64 || d_ff % 64 || n_groups > kMaxTileEntries) return MOE_ERR_UNSUPPORTED;
-  const size_t need = align256((size_t)max_rows * d_ff * esize(s));
-  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
-  if (max_rows == 0 || s.n_tokens == 0) return MOE_OK;
-  GroupedParams p{};
-  p.n_sets = 1;
-  p.x = x;
-  p.n_tokens = s.n_tokens;
-  p.d_model = s.d_model;
-  p.dtype = s.dtype;
-  SegSet& S = p.set[0];
-  S.offsets = offsets;
-  S.perm = perm;
-  S.n_groups = n_groups;
-  S.uniform_rows = 0;
-  S.rows_per_token = rows_per_token;
-  S.max_rows = max_rows;
-  S.d_ff = d_ff;
-  S.w_gate = w_gate;
-  S.w_up = w_up;
-  S.w_down = w_down;
-  S.h = ws;
-  S.out = out;
-  int st = launch_grouped(p, 1, stream);
-  if (st != MOE_OK) return st;
-  return launch_grouped(p, 2, stream);
+  if (!sc_gate || !sc_up || !sc_down) return MOE_ERR_INVALID_ARG;
+  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  return grouped_impl(shape, n_groups, d_ff, x, perm, rows_per_token, offsets, max_rows, w_gate, w_up,
+                      w_down, sc_gate, sc_up, sc_down, out, ws, ws_bytes, stream);
+}
+
+int moe_quantize_fp8(int64_t rows, int32_t cols, const void* w_bf16, uint8_t* codes, float* scales,
+                     hipStream_t stream) {
+  if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!w_bf16 || !codes || !scales)) return MOE_ERR_INVALID_ARG;
+  if (cols % 64 || rows >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  return launch_quantize_fp8(rows, cols, w_bf16, codes, scales, stream);
 }
 
 int moe_combine(const moe_shape* shape, const float* expert_out, const int32_t* slot_pos,
@@ -182,12 +216,13 @@ int moe_combine(const moe_shape* shape, const float* expert_out, const int32_t* 
                         stream);
 }
 
-int moe_forward(const moe_shape* shape, const void* x, const void* w_router, const float* logit_bias,
-                const float* select_bias, const void* w_gate, const void* w_up, const void* w_down,
-                const void* s_gate, const void* s_up, const void* s_down, float* y,
-                int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
-                int32_t* slot_pos, double* prob_sum, double* balance_stat, void* ws,
-                size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+static int forward_impl(const moe_shape* shape, const void* x, const void* w_router,
+                        const float* logit_bias, const float* select_bias, const void* w_gate,
+                        const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
+                        const void* s_down, const moe_fp8_scales* sc, float* y, int32_t* topk_idx,
+                        float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* slot_pos, double* prob_sum, double* balance_stat, void* ws,
+                        size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
@@ -230,6 +265,12 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
     R.w_gate = w_gate;
     R.w_up = w_up;
     R.w_down = w_down;
+    if (sc) {
+      p.w8 = 1;
+      R.sc_gate = sc->gate;
+      R.sc_up = sc->up;
+      R.sc_down = sc->down;
+    }
     R.h = at(ws, L.h_routed);
     R.out = O;
     if (s.n_shared > 0) {
@@ -244,6 +285,11 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
       Sh.w_gate = s_gate;
       Sh.w_up = s_up;
       Sh.w_down = s_down;
+      if (sc) {
+        Sh.sc_gate = sc->s_gate;
+        Sh.sc_up = sc->s_up;
+        Sh.sc_down = sc->s_down;
+      }
       Sh.h = at(ws, L.h_shared);
       Sh.out = O_shared;
     }
@@ -256,6 +302,33 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
     return st;
   mark(5);
   return MOE_OK;
+}
+
+int moe_forward(const moe_shape* shape, const void* x, const void* w_router, const float* logit_bias,
+                const float* select_bias, const void* w_gate, const void* w_up, const void* w_down,
+                const void* s_gate, const void* s_up, const void* s_down, float* y,
+                int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                int32_t* slot_pos, double* prob_sum, double* balance_stat, void* ws,
+                size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+  return forward_impl(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
+                      s_down, nullptr, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
+                      balance_stat, ws, ws_bytes, stage_events, stream);
+}
+
+int moe_forward_fp8(const moe_shape* shape, const void* x, const void* w_router,
+                    const float* logit_bias, const float* select_bias, const uint8_t* w_gate,
+                    const uint8_t* w_up, const uint8_t* w_down, const uint8_t* s_gate,
+                    const uint8_t* s_up, const uint8_t* s_down, const moe_fp8_scales* scales,
+                    float* y, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                    int32_t* perm, int32_t* slot_pos, double* prob_sum, double* balance_stat,
+                    void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+  if (!shape || !scales) return MOE_ERR_INVALID_ARG;
+  if (!scales->gate || !scales->up || !scales->down) return MOE_ERR_INVALID_ARG;
+  if (shape->n_shared > 0 && (!scales->s_gate || !scales->s_up || !scales->s_down)) return MOE_ERR_INVALID_ARG;
+  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  return forward_impl(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
+                      s_down, scales, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
+                      balance_stat, ws, ws_bytes, stage_events, stream);
 }
 
 }  // extern "C"

@@ -14,7 +14,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte piece (a native vector, not HIP's uint4 struct)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));  // 16-byte piece (a native vector, not HIP's uint4 struct)
 
 constexpr int kWave = 64;
 constexpr int kMaxExperts = 512;
@@ -57,9 +58,12 @@ struct SegSet {
   int32_t rows_per_token;
   int32_t max_rows;        // rows at or past this are never computed
   int32_t d_ff;
-  const void* w_gate;      // [G, d_ff, d]
+  const void* w_gate;      // [G, d_ff, d]  (bf16, fp32, or FP8 E4M3 codes)
   const void* w_up;        // [G, d_ff, d]
   const void* w_down;      // [G, d, d_ff]
+  const float* sc_gate;    // FP8 weights only: [G, d_ff] row scales of w_gate
+  const float* sc_up;      // [G, d_ff]
+  const float* sc_down;    // [G, d]
   void* h;                 // [max_rows, d_ff]: gate|up output, down input
   float* out;              // [max_rows, d]
 };
@@ -72,10 +76,16 @@ struct GroupedParams {
   int32_t d_model;
   int32_t dtype;
   int32_t balance_m;       // 1: split each segment into equal m-tiles (else BM rows and a short last tile)
+  int32_t w8;              // 1: expert weights are FP8 E4M3 codes with per-row scales (x and h bf16)
 };
 
 // Phase 1: h = silu(x Wg^T) * (x Wu^T) per segment; phase 2: out = h Wd^T.
 int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream);
+
+// ------------------------------------------------------------------ FP8 weights
+// codes[r, c] = e4m3(w[r, c] / scales[r]), scales[r] = max_c |w[r, c]| / 448 (fp32).
+int launch_quantize_fp8(long long rows, int cols, const void* w_bf16, uint8_t* codes, float* scales,
+                        hipStream_t stream);
 
 // ------------------------------------------------------------------ combine
 int launch_combine(const moe_shape& s, const float* expert_out, const int32_t* slot_pos,

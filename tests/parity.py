@@ -45,11 +45,27 @@ class F64View:
         return self.cache[e]
 
 
-def oracle_views(layer: mi.Layer, cache_routed=False):
-    ws = tuple(F64View(a, cache=cache_routed) for a in (layer.w_gate, layer.w_up, layer.w_down))
+class Fp8View(F64View):
+    """Like F64View, but each expert matrix is quantised to FP8 by the oracle
+    (per-row scales) and dequantised: the weights the FP8 layer computes with."""
+
+    def __getitem__(self, e):
+        e = int(e)
+        if self.cache is not None and e in self.cache:
+            return self.cache[e]
+        codes, scales = O.quantize_fp8_rows(mi.bf16_bits_to_f32(self.arr[e]))
+        w = O.dequantize_fp8_rows(codes, scales)
+        if self.cache is not None:
+            self.cache[e] = w
+        return w
+
+
+def oracle_views(layer: mi.Layer, cache_routed=False, fp8=False):
+    V = Fp8View if fp8 else F64View
+    ws = tuple(V(a, cache=cache_routed) for a in (layer.w_gate, layer.w_up, layer.w_down))
     shared = None
     if layer.s_gate is not None:
-        shared = tuple(F64View(a) for a in (layer.s_gate, layer.s_up, layer.s_down))
+        shared = tuple(V(a) for a in (layer.s_gate, layer.s_up, layer.s_down))
     return ws, shared
 
 
@@ -58,9 +74,9 @@ def oracle_route(cfg: mi.MoEConfig, layer: mi.Layer, x: np.ndarray) -> O.Routing
                    layer.select_bias, cfg.renormalize)
 
 
-def oracle_y(cfg, layer, x, idx, rows, form, routing: O.Routing = None):
-    """Forced-routing oracle output on `rows` for the given idx."""
-    (wg, wu, wd), shared = oracle_views(layer, cache_routed=(form == "per_token"))
+def oracle_y(cfg, layer, x, idx, rows, form, routing: O.Routing = None, fp8=False):
+    """Forced-routing oracle output on `rows` for the given idx (fp8: FP8 expert weights)."""
+    (wg, wu, wd), shared = oracle_views(layer, cache_routed=(form == "per_token"), fp8=fp8)
     x64 = mi.to_f64(x)
     if routing is None:
         routing = oracle_route(cfg, layer, x)

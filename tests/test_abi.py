@@ -106,3 +106,31 @@ def test_workspace_sizes_of_the_layers():
         o_bytes = (NK + S * cfg.n_tokens) * cfg.d_model * 4
         assert nb >= o_bytes, name
         assert nb < 2 * o_bytes + (64 << 20) + NK * cfg.d_ff * 4, name
+
+
+def test_fp8_entry_points_validate():
+    L = moe.lib()
+    # quantize: bad sizes, missing pointers, columns not a multiple of 64
+    assert L.moe_quantize_fp8(-1, 64, FAKE, FAKE, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_fp8(4, 0, FAKE, FAKE, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_fp8(4, 64, None, FAKE, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_fp8(4, 96, FAKE, FAKE, FAKE, None) == N.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_fp8(0, 64, None, None, None, None) == N.MOE_OK  # nothing to do
+    # grouped: scales required, bf16 layers only
+    s = shp()
+    args = (64, 256, FAKE, FAKE, 2, FAKE, 128, FAKE, FAKE, FAKE)
+    assert L.moe_grouped_swiglu_fp8(ctypes.byref(s), *args, None, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                    None) == N.MOE_ERR_INVALID_ARG
+    s32 = shp(dtype=N.MOE_DTYPE_F32)
+    assert L.moe_grouped_swiglu_fp8(ctypes.byref(s32), *args, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                    None) == N.MOE_ERR_UNSUPPORTED
+    # forward: a scales struct with every routed pointer, and the shared ones when S > 0
+    sc = N.MoEFp8Scales(FAKE, FAKE, FAKE, None, None, None)
+    fw = lambda shape, scales: L.moe_forward_fp8(
+        ctypes.byref(shape), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None, None, scales,
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, None)
+    assert fw(s, None) == N.MOE_ERR_INVALID_ARG
+    assert fw(s, ctypes.byref(N.MoEFp8Scales(FAKE, None, FAKE, None, None, None))) == N.MOE_ERR_INVALID_ARG
+    assert fw(shp(n_shared=1, d_ff_shared=128), ctypes.byref(sc)) == N.MOE_ERR_INVALID_ARG
+    assert fw(s32, ctypes.byref(sc)) == N.MOE_ERR_UNSUPPORTED
+    assert fw(s, ctypes.byref(sc)) == N.MOE_ERR_WORKSPACE  # 16 bytes: validation reaches the workspace check
