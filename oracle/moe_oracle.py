@@ -54,6 +54,11 @@ of each weight matrix (scale = row max |w| / 448), codes by round-to-nearest-
 even of w / scale, both divisions in fp32. The quantised layer is the bf16
 layer with every expert weight replaced by scale * decode(code).
 
+Training-side router statistics (z-loss, importance, the selection-bias
+update) are readings of passages whose formulas were lost; each function
+states its reading. Pins: closed forms (equal logits, one-hot and uniform
+routing), scipy's logsumexp, numpy's bincount, an element-wise brute force.
+
 Parity unpinned: y on general random inputs has no printed value on any page.
 It rests on the special cases above and on the per-token and grouped forms
 agreeing.
@@ -423,6 +428,62 @@ def balance_stat(counts, prob_sum, n_tokens: int, top_k: int) -> float:
     P = prob_sum / float(n_tokens)
     return float(E * np.sum(f * P))
 
+
+
+# ---------------------------------------------------------------- training-side router statistics
+#
+# Side outputs for training, next to the forward pass. The formulas on the
+# pages are lost in extraction, so each is a reading (stated per function).
+
+def z_loss(logits) -> float:
+    """Router z-loss: the mean over tokens of logsumexp(logits)^2.
+
+    The notes (section 三.3 "路由策略稳定性与 Z-Loss") apply it to the raw gate
+    logits before top-k, to bound their magnitude. Reading: the ST-MoE form
+    (1/N) sum_t (log sum_e exp l[t, e])^2 on the logits that enter the
+    softmax (with the logit bias). An empty batch gives 0.
+    """
+    l = np.asarray(logits, dtype=F64)
+    if l.shape[0] == 0:
+        return 0.0
+    m = l.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(l - m).sum(axis=1))
+    return float(np.mean(lse * lse))
+
+
+def importance(idx, w, n_experts: int) -> np.ndarray:
+    """Importance of each expert: the sum of the gate weights it was given.
+
+    The notes (section 二, "Importance Loss") penalise the spread of the gate
+    weights over experts. Reading: importance_e = sum over copies routed to e
+    (before capacity) of their weight w.
+    """
+    idx = np.asarray(idx, dtype=np.int64).reshape(-1)
+    w = np.asarray(w, dtype=F64).reshape(-1)
+    return np.bincount(idx, weights=w, minlength=n_experts).astype(F64)
+
+
+def importance_cv2(imp) -> float:
+    """The importance loss: squared coefficient of variation of importance over
+    experts, Var/Mean^2 with the population variance (0 if the mean is 0)."""
+    imp = np.asarray(imp, dtype=F64)
+    mean = imp.mean()
+    if mean == 0:
+        return 0.0
+    return float(((imp - mean) ** 2).mean() / (mean * mean))
+
+
+def update_select_bias(bias, counts, n_tokens: int, top_k: int, gamma: float) -> np.ndarray:
+    """One step of the aux-loss-free balancing of section "负载均衡" (handbook):
+    the selection bias of an overloaded expert goes down and that of an idle
+    one goes up. Reading (no step size or rule on the page): with the mean load
+    N*k/E, b_e <- b_e - gamma * sign(counts_e - N*k/E), in fp32 (the bias's
+    storage type); counts before capacity."""
+    b = np.asarray(bias, dtype=np.float32)
+    E = b.shape[0]
+    c = np.asarray(counts, dtype=F64)
+    s = np.sign(c - float(n_tokens) * float(top_k) / float(E)).astype(np.float32)
+    return (b - np.float32(gamma) * s).astype(np.float32)
 
 # ---------------------------------------------------------------- whole layer
 

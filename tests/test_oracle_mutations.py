@@ -129,3 +129,20 @@ def test_fp8_scale_per_column_is_caught(monkeypatch):
     orig = O.quantize_fp8_rows
     monkeypatch.setattr(O, "quantize_fp8_rows", lambda w: tuple(a.T if a.ndim == 2 else a for a in orig(np.asarray(w).T)))
     _fails(pins.test_fp8_row_quantisation_invariants)
+
+
+def test_z_loss_without_square_is_caught(monkeypatch):
+    def bad(logits):
+        l = np.asarray(logits, dtype=F64)
+        if l.shape[0] == 0:
+            return 0.0
+        m = l.max(axis=1, keepdims=True)
+        return float(np.mean(m[:, 0] + np.log(np.exp(l - m).sum(axis=1))))
+    monkeypatch.setattr(O, "z_loss", bad)
+    _fails(pins.test_z_loss_closed_forms_and_scipy)
+
+
+def test_bias_update_wrong_direction_is_caught(monkeypatch):
+    orig = O.update_select_bias
+    monkeypatch.setattr(O, "update_select_bias", lambda b, c, n, k, g: orig(b, c, n, k, -g))
+    _fails(pins.test_select_bias_update_bruteforce)

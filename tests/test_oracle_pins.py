@@ -477,3 +477,58 @@ def test_fp8_layer_is_dense_ffn_with_dequantised_weights():
         tdeq.append(torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy() * s.astype(np.float64)[:, None])
     lr = O.moe_layer(x, rng.standard_normal((1, d)), deq[0], deq[1], deq[2], 1)
     np.testing.assert_allclose(lr.y, torch_swiglu(x, tdeq[0], tdeq[1], tdeq[2]), rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------ training-side router statistics
+
+def test_z_loss_closed_forms_and_scipy():
+    rng = np.random.default_rng(50)
+    l = rng.standard_normal((40, 9)) * 3
+    ref = np.mean(scipy.special.logsumexp(l, axis=1) ** 2)
+    assert abs(O.z_loss(l) - ref) <= 1e-12 * ref
+    # equal logits c over E experts: logsumexp = c + ln E
+    assert abs(O.z_loss(np.full((5, 7), 2.5)) - (2.5 + math.log(7)) ** 2) <= 1e-12
+    # one expert: logsumexp = the logit itself
+    one = rng.standard_normal((11, 1))
+    assert abs(O.z_loss(one) - np.mean(one[:, 0] ** 2)) <= 1e-12
+    assert O.z_loss(np.zeros((0, 4))) == 0.0
+    # shift invariance of the softmax does not hold for z: adding c to every logit adds c to logsumexp
+    assert abs(O.z_loss(l + 1.0) - np.mean((scipy.special.logsumexp(l, axis=1) + 1.0) ** 2)) <= 1e-10
+
+
+def test_importance_bincount_and_closed_forms():
+    rng = np.random.default_rng(51)
+    idx = rng.integers(0, 6, (50, 2))
+    w = rng.random((50, 2))
+    imp = O.importance(idx, w, 8)
+    ref = np.zeros(8)
+    for t in range(50):
+        for j in range(2):
+            ref[idx[t, j]] += w[t, j]
+    np.testing.assert_allclose(imp, ref, rtol=1e-14)
+    assert imp[6] == 0 and imp[7] == 0
+    # equal importance everywhere -> 0; everything on one expert -> E - 1
+    E = 5
+    uni = O.importance(np.tile(np.arange(E), (4, 1)), np.full((4, E), 0.2), E)
+    assert O.importance_cv2(uni) == 0.0
+    hot = O.importance(np.zeros((9, 1), dtype=int), np.ones((9, 1)), E)
+    assert abs(O.importance_cv2(hot) - (E - 1)) <= 1e-12
+    assert O.importance_cv2(np.zeros(E)) == 0.0
+
+
+def test_select_bias_update_bruteforce():
+    rng = np.random.default_rng(52)
+    E, N, k = 12, 30, 2                       # mean load N*k/E = 5
+    counts = np.array([5, 0, 6, 4, 5, 12, 1, 5, 7, 3, 5, 7])
+    b = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    g = 1e-3
+    out = O.update_select_bias(b, counts, N, k, g)
+    assert out.dtype == np.float32
+    for e in range(E):
+        if counts[e] > 5:
+            expect = np.float32(b[e] - np.float32(g))
+        elif counts[e] < 5:
+            expect = np.float32(b[e] + np.float32(g))
+        else:
+            expect = b[e]
+        assert out[e] == expect, e
