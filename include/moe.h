@@ -181,6 +181,38 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router,
                 void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
+ * Training-side router statistics (side outputs; the forward needs none).
+ * The pages' formulas for these were lost in extraction; each call states
+ * the reading it computes.
+ * --------------------------------------------------------------------- */
+
+/* z-loss, importance and the importance loss, from the router of shape:
+ *   z_loss[0]         = (1/N) sum_t (log sum_e exp l[t,e])^2, l = x W_r^T (+ logit_bias):
+ *                       the ST-MoE form of the z-loss on the raw gate logits
+ *                       (notes "混合专家模型 (MoE)...", section 三.3); the logits
+ *                       are recomputed here
+ *   importance[e]     = sum of topk_w[t,j] over the copies with topk_idx[t,j] = e,
+ *                       before capacity (notes, section 二, importance loss)
+ *   importance_cv2[0] = Var_e(importance) / Mean_e(importance)^2, population
+ *                       variance; 0 when the mean is 0
+ * Each output is fp64 and may be NULL (not computed); at least one is given.
+ * topk_idx/topk_w are moe_route's outputs (needed for the importance terms),
+ * x/w_router/logit_bias as in moe_route (needed for z_loss). Sums run in a
+ * fixed order. N = 0 gives zeros. ws >= moe_workspace_bytes(shape). */
+int moe_router_aux(const moe_shape* shape, const void* x, const void* w_router, const float* logit_bias,
+                   const int32_t* topk_idx, const float* topk_w, double* z_loss, double* importance,
+                   double* importance_cv2, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One step of the aux-loss-free balancing of section "负载均衡": the
+ * selection bias of an overloaded expert goes down, an idle one's goes up.
+ * The page gives no rule or step size; this computes, in place and in fp32,
+ *   select_bias[e] -= gamma * sign(counts[e] - N*k/E)
+ * with the sign taken exactly (counts[e]*E against N*k) and counts the
+ * routed copies before capacity (moe_permute's counts). gamma >= 0, finite. */
+int moe_update_select_bias(const moe_shape* shape, const int32_t* counts, float gamma, float* select_bias,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------
  * FP8 expert weights (W8A16), for decode, whose time is the time to read
  * the touched experts' weights ("推理视角" section: DeepSeek-V3 ships FP8
  * weights). The page names no format or scale granularity; these calls use

@@ -60,6 +60,8 @@ _SIGS = {
     "moe_forward": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "moe_quantize_fp8": (ctypes.c_int, [ctypes.c_int64, _I, _P, _P, _P, _P]),
+    "moe_router_aux": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_update_select_bias": (ctypes.c_int, [_SHP, _P, ctypes.c_float, _P, _P]),
     "moe_grouped_swiglu_fp8": (ctypes.c_int, [_SHP, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P,
                                               _P, _P, _P, _SZ, _P]),
     "moe_forward_fp8": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -195,3 +197,16 @@ def moe_forward_fp8(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w
         _ptr(prob_sum), _ptr(balance_stat), _ptr(ws),
         ws.numel() * ws.element_size() if ws is not None else 0,
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)))
+
+
+def moe_router_aux(shape, x, w_router, logit_bias, topk_idx, topk_w, z_loss, importance,
+                   importance_cv2, ws, stream=None):
+    _check("moe_router_aux", lib().moe_router_aux(
+        ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(topk_idx), _ptr(topk_w),
+        _ptr(z_loss), _ptr(importance), _ptr(importance_cv2), _ptr(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def moe_update_select_bias(shape, counts, gamma, select_bias, stream=None):
+    _check("moe_update_select_bias", lib().moe_update_select_bias(
+        ctypes.byref(shape), _ptr(counts), float(gamma), _ptr(select_bias), _stream(stream)))

@@ -1,6 +1,8 @@
 // C ABI of libmoe.so (declared in include/moe.h): argument validation,
 // workspace layout and launch order. Nothing here allocates, synchronises
 // or keeps state between calls.
+#include <math.h>
+
 #include <algorithm>
 
 #include "moe_common.h"
@@ -33,7 +35,7 @@ int check_shape(const moe_shape* sp) {
 
 // Workspace layout shared by the entry points (byte offsets, 256-aligned).
 struct Layout {
-  size_t partials, logits, hist, base, h_routed, h_shared, o, total;
+  size_t partials, logits, hist, base, aux, h_routed, h_shared, o, total;
 };
 
 Layout layout(const moe_shape& s) {
@@ -49,6 +51,8 @@ Layout layout(const moe_shape& s) {
   off += align256((size_t)permute_chunks(s) * E * sizeof(int32_t));
   L.base = off;
   off += align256((size_t)permute_chunks(s) * E * sizeof(int32_t));
+  L.aux = off;  // router statistics: importance when the caller does not keep it
+  off += align256(E * sizeof(double));
   L.h_routed = off;
   off += align256(NK * s.d_ff * esize(s));
   L.h_shared = off;
@@ -329,6 +333,40 @@ int moe_forward_fp8(const moe_shape* shape, const void* x, const void* w_router,
   return forward_impl(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
                       s_down, scales, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
                       balance_stat, ws, ws_bytes, stage_events, stream);
+}
+
+int moe_router_aux(const moe_shape* shape, const void* x, const void* w_router, const float* logit_bias,
+                   const int32_t* topk_idx, const float* topk_w, double* z_loss, double* importance,
+                   double* importance_cv2, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (!z_loss && !importance && !importance_cv2) return MOE_ERR_INVALID_ARG;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (s.n_tokens > 0) {
+    if (z_loss && (!x || !w_router)) return MOE_ERR_INVALID_ARG;
+    if ((importance || importance_cv2) && (!topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  }
+  if (s.n_tokens == 0) {  // no tokens: every statistic is 0
+    if (z_loss && (st = zero_f64(z_loss, 1, stream))) return st;
+    if (importance && (st = zero_f64(importance, s.n_experts, stream))) return st;
+    if (importance_cv2 && (st = zero_f64(importance_cv2, 1, stream))) return st;
+    return MOE_OK;
+  }
+  double* imp = importance ? importance : (importance_cv2 ? reinterpret_cast<double*>(at(ws, L.aux)) : nullptr);
+  return launch_router_aux(s, x, w_router, logit_bias, topk_idx, topk_w, z_loss, imp, importance_cv2,
+                           reinterpret_cast<double*>(at(ws, L.partials)),
+                           reinterpret_cast<float*>(at(ws, L.logits)), stream);
+}
+
+int moe_update_select_bias(const moe_shape* shape, const int32_t* counts, float gamma, float* select_bias,
+                           hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!counts || !select_bias || !(gamma >= 0.0f) || gamma == INFINITY) return MOE_ERR_INVALID_ARG;
+  return launch_bias_update(*shape, counts, gamma, select_bias, stream);
 }
 
 }  // extern "C"

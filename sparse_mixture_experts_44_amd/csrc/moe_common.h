@@ -40,6 +40,12 @@ int launch_route(const moe_shape& s, const void* x, const void* w_router, const 
                  const float* select_bias, int32_t* topk_idx, float* topk_w, double* prob_sum,
                  double* partials, float* logits, hipStream_t stream);
 int route_blocks(const moe_shape& s);
+// Training-side statistics: z-loss (recomputes the logits), importance and its CV^2; any output may be NULL.
+int launch_router_aux(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
+                      const int32_t* topk_idx, const float* topk_w, double* z_loss, double* imp,
+                      double* imp_cv2, double* partials, float* logits, hipStream_t stream);
+int launch_bias_update(const moe_shape& s, const int32_t* counts, float gamma, float* bias,
+                       hipStream_t stream);
 size_t route_logits_floats(const moe_shape& s);
 
 // ------------------------------------------------------------------ permute

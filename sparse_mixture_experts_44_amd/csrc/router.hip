@@ -312,6 +312,118 @@ __global__ __launch_bounds__(kThreads) void prob_sum_kernel(const double* __rest
   if (lane == 0) prob_sum[e] = a;
 }
 
+// ---------------------------------------------------------------- 4. training-side statistics
+//
+// Side outputs for training (the forward does not use them). Readings of the
+// pages, whose formulas were lost in extraction:
+//   z-loss (notes, section 三.3): (1/N) sum_t logsumexp(l[t, :])^2 on the
+//     logits that enter the softmax;
+//   importance (notes, section 二): per expert, the sum of the gate weights
+//     w of the copies routed to it, and its squared coefficient of variation;
+//   aux-loss-free balancing (handbook, "负载均衡"): b_e -= gamma *
+//     sign(counts_e - N k / E).
+// Every sum runs in a fixed order, so the results are reproducible bit for bit.
+
+// One wavefront per token: splits added in split order, then the logit bias,
+// logsumexp in fp32; each workgroup adds its tokens' squares in fp64 in a
+// fixed order.
+template <int EL>
+__global__ __launch_bounds__(kThreads) void lse_sq_kernel(const float* __restrict__ part, int splits,
+                                                          const float* __restrict__ logit_bias, int N,
+                                                          int E, int tpb, double* __restrict__ partials) {
+  __shared__ double s_sq[kThreads / kWave];
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6, lane = tid & 63;
+  const size_t split_stride = (size_t)N * E;
+  double acc = 0.0;
+  for (int tt = wv; tt < tpb; tt += kThreads / kWave) {
+    const int t = blockIdx.x * tpb + tt;
+    if (t >= N) break;
+    float v[EL];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < EL; ++m) {
+      const int e = lane + kWave * m;
+      float l = -INFINITY;
+      if (e < E) {
+        const float* src = part + (size_t)t * E + e;
+        l = 0.f;
+        for (int q = 0; q < splits; ++q) l += src[(size_t)q * split_stride];
+        if (logit_bias) l += logit_bias[e];
+      }
+      v[m] = l;
+      mx = fmaxf(mx, l);
+    }
+    mx = wave_max(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int m = 0; m < EL; ++m) sum += (lane + kWave * m < E) ? expf(v[m] - mx) : 0.f;
+    sum = wave_sum(sum);
+    const double lse = (double)(mx + logf(sum));
+    acc += lse * lse;  // the same value in every lane
+  }
+  if (lane == 0) s_sq[wv] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    double a = s_sq[0];
+#pragma unroll
+    for (int q = 1; q < kThreads / kWave; ++q) a += s_sq[q];
+    partials[blockIdx.x] = a;
+  }
+}
+
+// One wavefront: out = scale * sum of v[0..n): lane-strided sums, then a fixed butterfly.
+__global__ __launch_bounds__(kWave) void sum_f64_kernel(const double* __restrict__ v, int n, double scale,
+                                                        double* __restrict__ out) {
+  const int lane = threadIdx.x;
+  double a = 0.0;
+  for (int i = lane; i < n; i += kWave) a += v[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+  if (lane == 0) *out = a * scale;
+}
+
+// One wavefront per expert: the gate weights of the copies routed to it.
+__global__ __launch_bounds__(kThreads) void importance_kernel(const int32_t* __restrict__ idx,
+                                                              const float* __restrict__ w, int NK, int E,
+                                                              double* __restrict__ imp) {
+  const int e = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (e >= E) return;
+  double a = 0.0;
+  for (int c = lane; c < NK; c += kWave)
+    if (idx[c] == e) a += (double)w[c];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+  if (lane == 0) imp[e] = a;
+}
+
+// One wavefront: Var/Mean^2 of imp[0..E) (population variance; 0 when the mean is 0).
+__global__ __launch_bounds__(kWave) void cv2_kernel(const double* __restrict__ imp, int E,
+                                                    double* __restrict__ out) {
+  const int lane = threadIdx.x;
+  double a = 0.0;
+  for (int e = lane; e < E; e += kWave) a += imp[e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+  const double mean = a / E;
+  double v = 0.0;
+  for (int e = lane; e < E; e += kWave) v += (imp[e] - mean) * (imp[e] - mean);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  if (lane == 0) *out = mean == 0.0 ? 0.0 : (v / E) / (mean * mean);
+}
+
+// b_e -= gamma * sign(counts_e - N k / E), the sign taken exactly on integers (counts_e * E vs N k).
+__global__ void bias_update_kernel(const int32_t* __restrict__ counts, long long nk, int E, float gamma,
+                                   float* __restrict__ bias) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const long long c = (long long)counts[e] * E;
+  if (c > nk) bias[e] = bias[e] - gamma;
+  else if (c < nk) bias[e] = bias[e] + gamma;
+}
+
 // ---------------------------------------------------------------- launch
 
 struct LogitsPlan {
@@ -412,6 +524,41 @@ int launch_route(const moe_shape& s, const void* x, const void* w_router, const 
 #undef MOE_SELECT
   hipLaunchKernelGGL(prob_sum_kernel, dim3((s.n_experts + 3) / 4), dim3(kThreads), 0, stream,
                      partials, nb, s.n_experts, prob_sum);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_router_aux(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
+                      const int32_t* topk_idx, const float* topk_w, double* z_loss, double* imp,
+                      double* imp_cv2, double* partials, float* logits, hipStream_t stream) {
+  const int N = s.n_tokens, E = s.n_experts;
+  if (z_loss) {
+    const LogitsPlan L = plan_logits(s);
+    if (s.dtype == MOE_DTYPE_BF16) launch_logits<true>(s, L, x, w_router, logits, stream);
+    else launch_logits<false>(s, L, x, w_router, logits, stream);
+    const int nb = route_blocks(s);
+    const int el = (E + kWave - 1) / kWave;
+#define MOE_LSE(EL_)                                                                                \
+  hipLaunchKernelGGL(lse_sq_kernel<EL_>, dim3(nb), dim3(kThreads), 0, stream, logits, L.splits, logit_bias, \
+                     N, E, select_tpb(s), partials)
+    if (el <= 1) MOE_LSE(1);
+    else if (el <= 2) MOE_LSE(2);
+    else if (el <= 4) MOE_LSE(4);
+    else MOE_LSE(8);
+#undef MOE_LSE
+    hipLaunchKernelGGL(sum_f64_kernel, dim3(1), dim3(kWave), 0, stream, partials, nb, 1.0 / N, z_loss);
+  }
+  if (imp) {
+    hipLaunchKernelGGL(importance_kernel, dim3((E + 3) / 4), dim3(kThreads), 0, stream, topk_idx, topk_w,
+                       N * s.top_k, E, imp);
+    if (imp_cv2) hipLaunchKernelGGL(cv2_kernel, dim3(1), dim3(kWave), 0, stream, imp, E, imp_cv2);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_bias_update(const moe_shape& s, const int32_t* counts, float gamma, float* bias,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3((s.n_experts + 255) / 256), dim3(256), 0, stream, counts,
+                     (long long)s.n_tokens * s.top_k, s.n_experts, gamma, bias);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -134,3 +134,20 @@ def test_fp8_entry_points_validate():
     assert fw(shp(n_shared=1, d_ff_shared=128), ctypes.byref(sc)) == N.MOE_ERR_INVALID_ARG
     assert fw(s32, ctypes.byref(sc)) == N.MOE_ERR_UNSUPPORTED
     assert fw(s, ctypes.byref(sc)) == N.MOE_ERR_WORKSPACE  # 16 bytes: validation reaches the workspace check
+
+
+def test_router_aux_entry_points_validate():
+    L = moe.lib()
+    s = shp()
+    big = 1 << 30
+    aux = lambda shape, z, imp, cv2, ws_bytes=big, x=FAKE: L.moe_router_aux(
+        ctypes.byref(shape), x, FAKE, None, FAKE, FAKE, z, imp, cv2, FAKE, ws_bytes, None)
+    assert aux(s, None, None, None) == N.MOE_ERR_INVALID_ARG          # nothing asked for
+    assert aux(s, FAKE, None, None, ws_bytes=16) == N.MOE_ERR_WORKSPACE
+    assert aux(s, FAKE, None, None, x=None) == N.MOE_ERR_INVALID_ARG   # z-loss needs x
+    assert aux(shp(top_k=0), FAKE, None, None) == N.MOE_ERR_INVALID_ARG
+    up = lambda shape, counts, g, b: L.moe_update_select_bias(ctypes.byref(shape), counts, g, b, None)
+    assert up(s, None, 1e-3, FAKE) == N.MOE_ERR_INVALID_ARG
+    assert up(s, FAKE, -1.0, FAKE) == N.MOE_ERR_INVALID_ARG
+    assert up(s, FAKE, float("nan"), FAKE) == N.MOE_ERR_INVALID_ARG
+    assert up(s, FAKE, float("inf"), FAKE) == N.MOE_ERR_INVALID_ARG
