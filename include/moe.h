@@ -143,7 +143,11 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const double* p
  *   w_gate/w_up [G, F, d] (dtype);  w_down [G, d, F] (dtype)
  *   out         [max_rows, d] fp32 out, in grouped order; rows past
  *               offsets[G] are left untouched
- *   ws          >= max_rows * F * sizeof(dtype) + 256 bytes */
+ *   ws          >= max_rows * F * sizeof(dtype) + 256 bytes. Workspace past
+ *               max_rows * F * sizeof(dtype) (rounded up to 256) is used, when
+ *               there is some, to split the last partial round of tiles
+ *               along K (bf16 layers); results stay deterministic for a
+ *               given device and workspace size */
 int moe_grouped_swiglu(const moe_shape* shape, int32_t n_groups, int32_t d_ff,
                        const void* x, const int32_t* perm, int32_t rows_per_token,
                        const int32_t* offsets, int32_t max_rows,

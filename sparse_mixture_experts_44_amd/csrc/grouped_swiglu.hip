@@ -230,6 +230,117 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
+// Where tile T lies: its entry (group of a set), rows and columns.
+struct TileGeom {
+  int si, g;          // set and group
+  int start;          // first row of the segment
+  int m0, mvalid;     // tile rows [m0, m0 + mvalid) of the segment
+  int n0;             // first output column
+};
+
+template <int BM, int BH>
+__device__ __forceinline__ TileGeom tile_geom(const GroupedParams& p, const TableLds& tab, int nent, int G0,
+                                              int T) {
+  TileGeom t;
+  const int ent = find_entry(tab.cum, nent, T);
+  t.si = ent < G0 ? 0 : 1;
+  t.g = t.si ? ent - G0 : ent;
+  t.start = tab.start[ent];
+  const int rows = tab.rows[ent];
+  const int mt = (rows + BM - 1) / BM;
+  const int local = T - tab.cum[ent];
+  const int ntile = local / mt, mtile = local - ntile * mt;
+  // A segment of `rows` rows takes mt = ceil(rows / BM) m-tiles: either BM
+  // rows each and a short last one, or (balance_m) an even split, so that
+  // the tiles sharing a weight tile take the same time.
+  t.m0 = p.balance_m ? (int)((long long)mtile * rows / mt) : mtile * BM;
+  t.mvalid = p.balance_m ? (int)((long long)(mtile + 1) * rows / mt) - t.m0 : min(BM, rows - t.m0);
+  t.n0 = ntile * BH;
+  return t;
+}
+
+// Tail split. With G workgroups, tiles [base, total) form a last, partial
+// round. When workspace is given, each of those `tail` tiles is split along
+// K into S parts (S <= G / tail), so the last round keeps every CU busy.
+// Each part writes its fp32 accumulators to the workspace (after a small
+// header with tail and S); an element-wise kernel adds the S parts in part
+// order into part 0, and a third kernel applies the epilogue to part 0.
+constexpr int kMaxSplit = 8;
+constexpr int kSplitHeader = 64;  // floats before the parts: [0] tail, [1] S (as int32)
+struct SplitPlan {
+  int base, tail, S;
+};
+
+__device__ __forceinline__ SplitPlan split_plan(int total, int G, long long cap_floats, int tile_floats) {
+  SplitPlan sp;
+  sp.base = (total / G) * G;
+  sp.tail = total - sp.base;
+  sp.S = 1;
+  // with four or more full rounds the idle part of the last one costs less
+  // than writing and adding the parts
+  if (sp.tail > 0 && cap_floats > 0 && total < 4 * G) {
+    int S = min(kMaxSplit, G / sp.tail);
+    while (S > 1 && (long long)sp.tail * S * tile_floats > cap_floats) --S;
+    sp.S = max(S, 1);
+  }
+  return sp;
+}
+
+// The epilogue of one tile from its accumulators. acc[i][j][v] holds column
+// (lane & 31) and row 8 (v / 4) + 4 (lane / 32) + (v % 4) of 32x32 block
+// (i, j). Phase 1 writes h = bf16(silu(g) * u), phase 2 writes fp32 O;
+// with FP8 weights each column is first multiplied by its weight row's scale.
+template <int BM, int BN, int WGM, int WGN, bool W8, bool P1, int FM, int NB>
+__device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetView& S, const TileGeom& t,
+                                           int d, int lane, int wm, int wn) {
+  constexpr int TM = BM / WGM;
+  constexpr int BH = P1 ? BN / 2 : BN;
+  constexpr int TN = BH / WGN;
+  constexpr int FN = TN / 32;
+  const int F = S.d_ff;
+  const int ncols = P1 ? F : d;
+  const int g = t.g;
+  const int col0 = t.n0 + wn * TN + (lane & 31);  // this lane's first output column
+  float sc0[FN], sc1[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    sc0[j] = sc1[j] = 1.f;
+    if constexpr (W8) {
+      const int c = min(col0 + j * 32, ncols - 1);
+      if constexpr (P1) {
+        sc0[j] = S.sg[(size_t)g * F + c];
+        sc1[j] = S.su[(size_t)g * F + c];
+      } else {
+        sc0[j] = S.sd[(size_t)g * d + c];
+      }
+    }
+  }
+  int rbase = wm * TM + 4 * (lane >> 5);
+  asm volatile("" : "+v"(rbase));  // per tile: keeps the 64 row offsets from being hoisted (and spilled)
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
+      if (r >= t.mvalid) continue;
+      const size_t row = (size_t)(t.start + t.m0 + r);
+      if constexpr (P1) {
+        bf16_t* hrow = static_cast<bf16_t*>(S.h) + row * F + col0;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (col0 + j * 32 < ncols)
+            hrow[j * 32] = f32_to_bf16(W8 ? silu_mul(acc[i][j][v] * sc0[j], acc[i][j + FN][v] * sc1[j])
+                                          : silu_mul(acc[i][j][v], acc[i][j + FN][v]));
+      } else {
+        float* orow = S.out + row * d + col0;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (col0 + j * 32 < ncols) orow[j * 32] = W8 ? acc[i][j][v] * sc0[j] : acc[i][j][v];
+      }
+    }
+  }
+}
+
 // One grouped GEMM launch (phase 1: gate|up + SiLU*up -> H; phase 2: down -> O).
 // Workgroup tile BM x BN x BK with NS LDS stages, filled by direct global->LDS
 // copies issued NS-1 steps ahead. WGM x WGN waves; wave tile (BM/WGM) x
@@ -285,24 +396,28 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
   const int crowA = lane / PPA, cpcA = lane % PPA;
   const int crowB = lane / PPB, cpcB = lane % PPB;
 
-  for (int T = xcd_block(); T < total; T += gridDim.x) {
-    const int ent = find_entry(tab.cum, nent, T);
-    const int si = ent < G0 ? 0 : 1;
-    const int g = si ? ent - G0 : ent;
+  const SplitPlan sp = split_plan(total, gridDim.x, p.split_cap - kSplitHeader, BM * BN);
+  const int units = sp.base + sp.tail * sp.S;
+  if (p.split_ws && blockIdx.x == 0 && tid == 0) {  // for the part-sum kernel
+    reinterpret_cast<int*>(p.split_ws)[0] = sp.S > 1 ? sp.tail : 0;
+    reinterpret_cast<int*>(p.split_ws)[1] = sp.S;
+  }
+  for (int u = xcd_block(); u < units; u += gridDim.x) {
+    int T = u, part = -1;  // part >= 0: this unit is K-part `part` of a split tail tile
+    if (sp.S > 1 && u >= sp.base) {
+      T = sp.base + (u - sp.base) / sp.S;
+      part = (u - sp.base) % sp.S;
+    }
+    const TileGeom tg = tile_geom<BM, BH>(p, tab, nent, G0, T);
+    const int si = tg.si, g = tg.g;
     const SetView S = pick(p, si);
-    const int start = tab.start[ent], rows = tab.rows[ent];
-    const int mt = (rows + BM - 1) / BM;
-    const int local = T - tab.cum[ent];
-    const int ntile = local / mt, mtile = local - ntile * mt;
-    // A segment of `rows` rows takes mt = ceil(rows / BM) m-tiles: either BM
-    // rows each and a short last one, or (balance_m) an even split, so that
-    // the tiles sharing a weight tile take the same time.
-    const int m0 = p.balance_m ? (int)((long long)mtile * rows / mt) : mtile * BM;
-    const int mvalid = p.balance_m ? (int)((long long)(mtile + 1) * rows / mt) - m0 : min(BM, rows - m0);
-    const int n0 = ntile * BH;
+    const int start = tg.start, m0 = tg.m0, mvalid = tg.mvalid, n0 = tg.n0;
     const int F = S.d_ff;
     const int K = P1 ? d : F;
-    const int nk = K / BK;
+    const int nk_all = K / BK;
+    // this unit's K steps: all of them, or part `part` of sp.S
+    const int k_lo = part < 0 ? 0 : (int)((long long)part * nk_all / sp.S);
+    const int nk = part < 0 ? nk_all : (int)((long long)(part + 1) * nk_all / sp.S) - k_lo;
     const int ncols = P1 ? F : d;
 
     // ---- A sources: rows past the segment (or with a token out of range)
@@ -354,7 +469,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
 
     auto issue = [&](int kt) {
       const int st = kt % NS;
-      const int ko = kt * BK;
+      const int ko = (k_lo + kt) * BK;
 #pragma unroll
       for (int i = 0; i < A_INS; ++i)
         if (i < a_act) dma16(a_base + a_off[i] + ko, a_lds0 + st * STAGE + i * 1024);
@@ -427,48 +542,73 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
 #undef MOE_SOME
 #undef MOE_K_LOOP
 
-    // ---- epilogue. acc[i][j][v]: column (lane & 31), row 8 (v / 4) + 4 (lane / 32) + (v % 4)
-    const int col0 = n0 + wn * TN + (lane & 31);  // this lane's first output column
-    // FP8 weights: output column c takes its weight row's scale (gate, up or down row c)
-    float sc0[FN], sc1[FN];
+    // ---- epilogue
+    if (part >= 0) {
+      // a K-part of a split tail tile: raw accumulators, thread-major, for the reduce kernel
+      float* dst = p.split_ws + kSplitHeader + ((size_t)(T - sp.base) * sp.S + part) * (BM * BN);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      sc0[j] = sc1[j] = 1.f;
-      if constexpr (W8) {
-        const int c = min(col0 + j * 32, ncols - 1);
-        if constexpr (P1) {
-          sc0[j] = S.sg[(size_t)g * F + c];
-          sc1[j] = S.su[(size_t)g * F + c];
-        } else {
-          sc0[j] = S.sd[(size_t)g * d + c];
-        }
-      }
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) dst[((i * NB + j) * 16 + v) * NT + tid] = acc[i][j][v];
+      continue;
     }
-    int rbase = wm * TM + 4 * (lane >> 5);
-    asm volatile("" : "+v"(rbase));  // per tile: keeps the 64 row offsets from being hoisted (and spilled)
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
-        if (r >= mvalid) continue;
-        const size_t row = (size_t)(start + m0 + r);
-        if constexpr (P1) {
-          bf16_t* hrow = static_cast<bf16_t*>(S.h) + row * F + col0;
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            if (col0 + j * 32 < ncols)
-              hrow[j * 32] = f32_to_bf16(W8 ? silu_mul(acc[i][j][v] * sc0[j], acc[i][j + FN][v] * sc1[j])
-                                            : silu_mul(acc[i][j][v], acc[i][j + FN][v]));
-        } else {
-          float* orow = S.out + row * d + col0;
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            if (col0 + j * 32 < ncols) orow[j * 32] = W8 ? acc[i][j][v] * sc0[j] : acc[i][j][v];
-        }
-      }
-    }
+    store_tile<BM, BN, WGM, WGN, W8, P1>(acc, S, tg, d, lane, wm, wn);
   }
+}
+
+// Adds the K-parts of every split tail tile, element by element in part
+// order, into part 0 (grid-stride; the count comes from the header).
+template <int TILE>
+__global__ __launch_bounds__(256) void split_sum_kernel(float* __restrict__ ws) {
+  const int tail = reinterpret_cast<const int*>(ws)[0], S = reinterpret_cast<const int*>(ws)[1];
+  if (tail <= 0 || S <= 1) return;
+  float* parts = ws + kSplitHeader;
+  const size_t n = (size_t)tail * TILE;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
+    float* t0 = parts + (e / TILE) * S * TILE + e % TILE;
+    float a = t0[0];
+    for (int q = 1; q < S; ++q) a += t0[(size_t)q * TILE];
+    t0[0] = a;
+  }
+}
+
+// The epilogue of the split tail tiles of the launch before it (same
+// parameters, `main_grid` workgroups), from part 0: workgroup b finishes
+// tail tile b. Workgroups past the tail exit.
+template <int BM, int BN, int WGM, int WGN, bool W8, bool P1>
+__global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedParams p, int main_grid) {
+  constexpr int TM = BM / WGM, FM = TM / 32;
+  constexpr int BH = P1 ? BN / 2 : BN;
+  constexpr int TN = BH / WGN, FN = TN / 32;
+  constexpr int NB = P1 ? 2 * FN : FN;
+  constexpr int NT = WGM * WGN * kWave;
+  __shared__ TableLds tab;
+  __shared__ int scratch[NT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int d = p.d_model;
+  const int nt0 = ((P1 ? p.set[0].d_ff : d) + BH - 1) / BH;
+  const int nt1 = p.n_sets > 1 ? ((P1 ? p.set[1].d_ff : d) + BH - 1) / BH : 0;
+  const int G0 = p.set[0].n_groups;
+  const int nent = G0 + (p.n_sets > 1 ? p.set[1].n_groups : 0);
+  const int total = build_table<BM, NT>(p, nt0, nt1, tab, scratch);
+  const SplitPlan sp = split_plan(total, main_grid, p.split_cap - kSplitHeader, BM * BN);
+  if (sp.S <= 1 || (int)blockIdx.x >= sp.tail) return;  // whole workgroup: no barrier follows
+  const int T = sp.base + blockIdx.x;
+  const TileGeom tg = tile_geom<BM, BH>(p, tab, nent, G0, T);
+  const SetView S = pick(p, tg.si);
+  f32x16_t acc[FM][NB];
+  const float* src = p.split_ws + kSplitHeader + (size_t)blockIdx.x * sp.S * (BM * BN) + tid;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = src[((size_t)(i * NB + j) * 16 + v) * NT];
+  store_tile<BM, BN, WGM, WGN, W8, P1>(acc, S, tg, d, lane, wm, wn);
 }
 
 // =====================================================================  fp32 SIMT
@@ -590,13 +730,23 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
   else
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, W8, false>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
+  if (p.split_ws && p.split_cap > kSplitHeader) {
+    hipLaunchKernelGGL(split_sum_kernel<BM * BN>, dim3(1024), dim3(256), 0, st, p.split_ws);
+    if (phase == 1)
+      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, W8, true>), dim3(grid), dim3(WGM * WGN * 64),
+                         0, st, p, grid);
+    else
+      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, W8, false>), dim3(grid), dim3(WGM * WGN * 64),
+                         0, st, p, grid);
+  }
 }
+
+// tile height from the mean routed rows per expert segment
+bool large_tiles(long long rows, int groups) { return rows / std::max(1, groups) >= 128; }
 
 template <bool W8>
 void launch_bf16_class(const GroupedParams& p, int phase, hipStream_t stream) {
-  // tile height from the mean routed rows per expert segment
-  const long long avg = (long long)p.set[0].max_rows / std::max(1, p.set[0].n_groups);
-  if (avg >= 128) {
+  if (large_tiles(p.set[0].max_rows, p.set[0].n_groups)) {
     // persistent grid with even m-tiles: the workgroups that share a weight
     // tile run in step, so their copies of it hit in L2
     GroupedParams q = p;
@@ -609,6 +759,13 @@ void launch_bf16_class(const GroupedParams& p, int phase, hipStream_t stream) {
 }
 
 }  // namespace
+
+size_t grouped_split_bytes(long long rows, int groups) {
+  // the parts of one launch fill at most one tile per workgroup: G = CUs x workgroups per CU
+  const bool large = large_tiles(rows, groups);
+  const size_t G = (size_t)num_cus() * (large ? 1 : 2);
+  return G * (large ? 256 * 256 : 64 * 256) * sizeof(float);
+}
 
 int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream) {
   if (p.dtype == MOE_DTYPE_F32) {

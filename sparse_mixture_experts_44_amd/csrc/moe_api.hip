@@ -35,7 +35,7 @@ int check_shape(const moe_shape* sp) {
 
 // Workspace layout shared by the entry points (byte offsets, 256-aligned).
 struct Layout {
-  size_t partials, logits, hist, base, aux, h_routed, h_shared, o, total;
+  size_t partials, logits, hist, base, aux, split, h_routed, h_shared, o, total;
 };
 
 Layout layout(const moe_shape& s) {
@@ -53,6 +53,8 @@ Layout layout(const moe_shape& s) {
   off += align256((size_t)permute_chunks(s) * E * sizeof(int32_t));
   L.aux = off;  // router statistics: importance when the caller does not keep it
   off += align256(E * sizeof(double));
+  L.split = off;  // K-parts of the grouped GEMMs' split tail tiles (bf16 layers)
+  off += align256(s.dtype == MOE_DTYPE_BF16 && N > 0 ? grouped_split_bytes((long long)NK, s.n_experts) : 0);
   L.h_routed = off;
   off += align256(NK * s.d_ff * esize(s));
   L.h_shared = off;
@@ -112,6 +114,10 @@ int grouped_impl(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const v
   p.d_model = s.d_model;
   p.dtype = s.dtype;
   p.w8 = sc_gate != nullptr;
+  if (s.dtype == MOE_DTYPE_BF16 && ws_bytes >= need + 256) {  // workspace past h: tail-tile K-parts
+    p.split_ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + need);
+    p.split_cap = (long long)((ws_bytes - need) / sizeof(float));
+  }
   SegSet& S = p.set[0];
   S.offsets = offsets;
   S.perm = perm;
@@ -259,6 +265,10 @@ static int forward_impl(const moe_shape* shape, const void* x, const void* w_rou
     p.d_model = s.d_model;
     p.dtype = s.dtype;
     p.n_sets = s.n_shared > 0 ? 2 : 1;
+    if (s.dtype == MOE_DTYPE_BF16 && L.h_routed > L.split) {
+      p.split_ws = reinterpret_cast<float*>(at(ws, L.split));
+      p.split_cap = (long long)((L.h_routed - L.split) / sizeof(float));
+    }
     SegSet& R = p.set[0];
     R.offsets = offsets;
     R.perm = perm;

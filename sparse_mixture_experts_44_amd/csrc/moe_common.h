@@ -83,7 +83,13 @@ struct GroupedParams {
   int32_t dtype;
   int32_t balance_m;       // 1: split each segment into equal m-tiles (else BM rows and a short last tile)
   int32_t w8;              // 1: expert weights are FP8 E4M3 codes with per-row scales (x and h bf16)
+  float* split_ws;         // workspace for the K-parts of split tail tiles (bf16 path), or NULL
+  long long split_cap;     // its size in floats (0: no split)
 };
+
+// Workspace bytes that let every launch split its tail tiles (grouped_split_bytes(rows, groups) for
+// a launch whose routed set has `rows` rows over `groups` groups).
+size_t grouped_split_bytes(long long rows, int groups);
 
 // Phase 1: h = silu(x Wg^T) * (x Wu^T) per segment; phase 2: out = h Wd^T.
 int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream);

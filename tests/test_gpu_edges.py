@@ -105,11 +105,11 @@ def _grouped_case(sizes, d, F, dtype, identity=False):
     return cfg, lay, x, offs, perm
 
 
-def _run_grouped(cfg, lay, x, offs, perm, rpt, max_rows):
+def _run_grouped(cfg, lay, x, offs, perm, rpt, max_rows, extra_ws=0):
     shape = moe.shape_for(cfg)
     F = cfg.d_ff
     esz = 2 if cfg.dtype == "bf16" else 4
-    ws = torch.empty(max(256, ((max_rows * F * esz + 255) // 256) * 256), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(max(256, ((max_rows * F * esz + 255) // 256) * 256) + extra_ws, dtype=torch.uint8, device=DEV)
     out = torch.full((max(1, max_rows), cfg.d_model), float("nan"), dtype=torch.float32, device=DEV)
     dv = lambda a: to_device(a, DEV)
     moe.moe_grouped_swiglu(shape, len(offs) - 1, F, dv(x), dv(perm) if perm is not None else None,
@@ -119,16 +119,18 @@ def _run_grouped(cfg, lay, x, offs, perm, rpt, max_rows):
     return P.to_host(out)
 
 
-@pytest.mark.parametrize("dtype,sizes", [
-    ("bf16", [0, 1, 255, 256, 257, 0, 513, 2, 300]),   # mean >= 128 rows: 256-row tiles
-    ("bf16", [0, 1, 63, 64, 65, 0, 3, 127, 0, 0]),       # small mean: 64-row tiles
-    ("f32", [0, 1, 31, 32, 33, 0, 65]),
+@pytest.mark.parametrize("dtype,sizes,extra_ws", [
+    ("bf16", [0, 1, 255, 256, 257, 0, 513, 2, 300], 0),          # mean >= 128 rows: 256-row tiles
+    ("bf16", [0, 1, 63, 64, 65, 0, 3, 127, 0, 0], 0),            # small mean: 64-row tiles
+    ("bf16", [0, 1, 255, 256, 257, 0, 513, 2, 300], 64 << 20),   # the same, tail tiles split along K
+    ("bf16", [0, 1, 63, 64, 65, 0, 3, 127, 0, 0], 1 << 20),      # split, workspace for a few parts only
+    ("f32", [0, 1, 31, 32, 33, 0, 65], 1 << 20),                 # fp32: never split
 ])
-def test_grouped_segment_edges(dtype, sizes):
+def test_grouped_segment_edges(dtype, sizes, extra_ws):
     d, F = 128, 256
     cfg, lay, x, offs, perm = _grouped_case(sizes, d, F, dtype)
     rpt = 3
-    out = _run_grouped(cfg, lay, x, offs, perm, rpt, int(offs[-1]))
+    out = _run_grouped(cfg, lay, x, offs, perm, rpt, int(offs[-1]), extra_ws)
     x64 = mi.to_f64(x)
     ref = np.zeros((int(offs[-1]), d))
     for g in range(len(sizes)):
