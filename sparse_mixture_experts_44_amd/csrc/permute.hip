@@ -16,15 +16,13 @@
 //   2. colscan: one wavefront per expert scans the chunk histograms, giving
 //               each chunk's base rank within the expert and the expert's
 //               total count (integer sums, so exact in any order).
-//   3. scatter: one wavefront per chunk.
+//   3. scatter: one workgroup per chunk, one thread per copy.
 //               - It loads the counts and forms kept = min(count, C) and
 //                 offsets = exclusive scan of kept in LDS. Workgroup 0 also
 //                 writes offsets and the balance statistic.
-//               - It then walks its copies 64 at a time, in copy order. A
-//                 copy's rank within its expert = the chunk base + the copies
-//                 of that expert already seen in this chunk + the lower lanes
-//                 of this step with the same expert. Each lane counts those
-//                 by scanning the step's 64 experts in LDS.
+//               - A copy's rank within its expert = the chunk base + the
+//                 earlier copies of the chunk with that expert, which each
+//                 thread counts by scanning the chunk's experts in LDS.
 //               - Rank < C keeps the copy at offsets[e] + rank.
 // Every output is a pure function of topk_idx: there are no races and no
 // order-dependent atomics.
@@ -77,131 +75,103 @@ __global__ __launch_bounds__(256) void colscan_kernel(const int32_t* __restrict_
   if (lane == 0) counts[e] = run;
 }
 
-// The workgroup is one wavefront, whose LDS accesses complete in issue order.
-// Between the steps it only waits for its own LDS accesses: __syncthreads
-// would also wait for the perm and slot_pos stores of the step before.
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
+// One workgroup per chunk, one thread per copy (kChunk threads).
 // base == nullptr: a single chunk holds every copy. Then this kernel also
 // counts (the chunk's histogram is the expert counts, and every base is 0),
 // in place of hist_kernel and colscan_kernel.
-__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ idx, int NK, int E,
-                                                     int C, int N, int k,
-                                                     const int32_t* __restrict__ base,
-                                                     int32_t* __restrict__ counts,
-                                                     int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ perm,
-                                                     int32_t* __restrict__ slot_pos,
-                                                     const double* __restrict__ prob_sum,
-                                                     double* __restrict__ stat) {
-  constexpr int kSteps = kChunk / kWave;
+constexpr int kScatterThreads = kChunk;
+
+__global__ __launch_bounds__(kScatterThreads) void scatter_kernel(const int32_t* __restrict__ idx, int NK,
+                                                                  int E, int C, int N, int k,
+                                                                  const int32_t* __restrict__ base,
+                                                                  int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ perm,
+                                                                  int32_t* __restrict__ slot_pos,
+                                                                  const double* __restrict__ prob_sum,
+                                                                  double* __restrict__ stat) {
   __shared__ int32_t s_run[kMaxExperts];
   __shared__ int32_t s_cnt[kMaxExperts];
   __shared__ int32_t s_off[kMaxExperts + 1];
-  __shared__ __attribute__((aligned(16))) int32_t s_step[kWave];
-  const int lane = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) int32_t s_e[kChunk];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const bool single = base == nullptr;
   const int c0 = blockIdx.x * kChunk;
-  const int c1 = min(NK, c0 + kChunk);
-  // this chunk's experts, all loaded up front (-1: past the end or out of range)
-  int ev[kSteps];
-#pragma unroll
-  for (int q = 0; q < kSteps; ++q) {
-    const int c = c0 + q * kWave + lane;
-    const int e = c < c1 ? idx[c] : -1;
-    ev[q] = (unsigned)e < (unsigned)E ? e : -1;
+  const int c = c0 + tid;
+  const bool in = c < NK;
+  int e = in ? idx[c] : -1;
+  if ((unsigned)e >= (unsigned)E) e = -1;  // past the end, or out of range: no expert
+  s_e[tid] = e;
+  for (int x = tid; x < E; x += kScatterThreads) {
+    s_cnt[x] = single ? 0 : counts[x];
+    s_run[x] = single ? 0 : base[(size_t)blockIdx.x * E + x];
   }
+  __syncthreads();
   if (single) {
-    for (int e = lane; e < E; e += kWave) s_cnt[e] = 0;
+    if (e >= 0) atomicAdd(&s_cnt[e], 1);  // the order of the additions does not matter
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < kSteps; ++q)
-      if (ev[q] >= 0) atomicAdd(&s_cnt[ev[q]], 1);
-    __syncthreads();
-    for (int e = lane; e < E; e += kWave) {
-      counts[e] = s_cnt[e];
-      s_run[e] = 0;
-    }
-  } else {
-    for (int e = lane; e < E; e += kWave) {
-      s_cnt[e] = counts[e];
-      s_run[e] = base[(size_t)blockIdx.x * E + e];
-    }
+    for (int x = tid; x < E; x += kScatterThreads) counts[x] = s_cnt[x];
   }
-  __syncthreads();
-  // offsets = exclusive scan of kept = min(counts, C), lane l owning experts [l*per, (l+1)*per)
-  const int per = (E + kWave - 1) / kWave;
-  int sum = 0;
-  for (int q = 0; q < per; ++q) {
-    const int e = lane * per + q;
-    if (e < E) {
-      const int c = s_cnt[e];
-      const int kept = (C > 0 && c > C) ? C : c;
-      s_off[e] = kept;
-      sum += kept;
+  // offsets = exclusive scan of kept = min(counts, C): wave 0, lane l owning experts [l*per, (l+1)*per)
+  if (wave == 0) {
+    const int per = (E + kWave - 1) / kWave;
+    int sum = 0;
+    for (int q = 0; q < per; ++q) {
+      const int x = lane * per + q;
+      if (x < E) {
+        const int cnt = s_cnt[x];
+        const int kept = (C > 0 && cnt > C) ? C : cnt;
+        s_off[x] = kept;
+        sum += kept;
+      }
     }
-  }
-  const int incl = wave_incl_scan(sum, lane);
-  int run = incl - sum;
-  for (int q = 0; q < per; ++q) {
-    const int e = lane * per + q;
-    if (e < E) {
-      const int kept = s_off[e];
-      s_off[e] = run;
-      run += kept;
+    const int incl = wave_incl_scan(sum, lane);
+    int run = incl - sum;
+    for (int q = 0; q < per; ++q) {
+      const int x = lane * per + q;
+      if (x < E) {
+        const int kept = s_off[x];
+        s_off[x] = run;
+        run += kept;
+      }
     }
-  }
-  if (lane == kWave - 1) s_off[E] = incl;
-  __syncthreads();
-  if (blockIdx.x == 0) {
-    for (int e = lane; e <= E; e += kWave) offsets[e] = s_off[e];
-    if (stat) {
+    if (lane == kWave - 1) s_off[E] = incl;
+    if (blockIdx.x == 0 && stat) {
       // E * sum_e (counts_e / (N k)) (prob_sum_e / N): lane-strided sums, then a fixed butterfly
       // (no copies: the statistic is defined as 0)
       const double nk = (double)N * (double)k, n = (double)N;
       double a = 0.0;
       if (N > 0)
-        for (int e = lane; e < E; e += kWave) a += ((double)s_cnt[e] / nk) * (prob_sum[e] / n);
+        for (int x = lane; x < E; x += kWave) a += ((double)s_cnt[x] / nk) * (prob_sum[x] / n);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
       if (lane == 0) *stat = (double)E * a;
     }
   }
-#pragma unroll
-  for (int q = 0; q < kSteps; ++q) {
-    const int c = c0 + q * kWave + lane;
-    if (c0 + q * kWave >= c1) break;  // uniform: the chunk's last step is done
-    const bool in = c < c1;
-    const int e = ev[q];
-    const bool valid = e >= 0;
-    // rank among this step's copies: lanes below with the same expert (and
-    // how many lanes of the step share it), from one pass over the step's
-    // experts in LDS
-    s_step[lane] = e;
-    wave_lds_sync();
-    int below = 0, same = 0;
-#pragma unroll 4
-    for (int j = 0; j < kWave; j += 4) {
-      const int4 v = *reinterpret_cast<const int4*>(&s_step[j]);
-      below += (v.x == e && j < lane) + (v.y == e && j + 1 < lane) + (v.z == e && j + 2 < lane) +
-               (v.w == e && j + 3 < lane);
-      same += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
-    }
-    const int rank = valid ? s_run[e] + below : 0;
-    wave_lds_sync();  // every lane has read s_run and s_step before they change
-    if (valid && below == same - 1) s_run[e] += same;  // the step's last copy of e
-    wave_lds_sync();
-    if (in) {
-      if (!valid) {
-        slot_pos[c] = -1;
-      } else if (C > 0 && rank >= C) {
-        slot_pos[c] = -1;
-      } else {
-        const int pos = s_off[e] + rank;
-        perm[pos] = c;
-        slot_pos[c] = pos;
-      }
-    }
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int x = tid; x <= E; x += kScatterThreads) offsets[x] = s_off[x];
+  if (!in) return;  // no barrier follows
+  if (e < 0) {
+    slot_pos[c] = -1;
+    return;
+  }
+  // rank within the expert: the chunk's base plus the earlier copies of this
+  // chunk with the same expert (a scan of the chunk's experts in LDS)
+  int rank = s_run[e];
+  const int full = tid & ~3;
+  for (int j = 0; j < full; j += 4) {
+    const int4 v = *reinterpret_cast<const int4*>(&s_e[j]);
+    rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+  }
+  for (int j = full; j < tid; ++j) rank += s_e[j] == e;
+  if (C > 0 && rank >= C) {
+    slot_pos[c] = -1;
+  } else {
+    const int pos = s_off[e] + rank;
+    perm[pos] = c;
+    slot_pos[c] = pos;
   }
 }
 
@@ -235,7 +205,7 @@ int launch_permute(const moe_shape& s, const int32_t* topk_idx, const double* pr
       hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(256), 0, stream, topk_idx, NK, E, hist);
       hipLaunchKernelGGL(colscan_kernel, dim3((E + 3) / 4), dim3(256), 0, stream, hist, nch, E, base, counts);
     }
-    hipLaunchKernelGGL(scatter_kernel, dim3(nch), dim3(kWave), 0, stream, topk_idx, NK, E, C,
+    hipLaunchKernelGGL(scatter_kernel, dim3(nch), dim3(kScatterThreads), 0, stream, topk_idx, NK, E, C,
                        s.n_tokens, s.top_k, nch > 1 ? base : nullptr, counts, offsets, perm, slot_pos,
                        prob_sum, balance_stat);
   }
