@@ -436,7 +436,7 @@ LogitsPlan plan_logits(const moe_shape& s) {
   if (E <= 8) { L.eg = 8; L.ept = 1; L.tpt = 4; }
   else if (E <= 32) { L.eg = 32; L.ept = 1; L.tpt = 4; }
   else if (E <= 64) { L.eg = 32; L.ept = 2; L.tpt = 4; }
-  else if (E <= 128) { L.eg = 32; L.ept = 4; L.tpt = 4; }
+  else if (E <= 128) { L.eg = 32; L.ept = 4; L.tpt = s.n_tokens >= 8192 ? 8 : 4; }  // 8 tokens: fewer LDS reads per dot
   else if (E <= 256) { L.eg = 32; L.ept = 8; L.tpt = 4; }
   else { L.eg = 32; L.ept = 16; L.tpt = 2; }
   L.tt = (kThreads / L.eg) * L.tpt;
@@ -483,6 +483,7 @@ void launch_logits(const moe_shape& s, const LogitsPlan& L, const void* x, const
   } else if (L.eg == 8) launch_logits_t<BF16, 8, 1, 4>(s, L, x, w, part, st);
   else if (L.ept == 1) launch_logits_t<BF16, 32, 1, 4>(s, L, x, w, part, st);
   else if (L.ept == 2) launch_logits_t<BF16, 32, 2, 4>(s, L, x, w, part, st);
+  else if (L.ept == 4 && L.tpt == 8) launch_logits_t<BF16, 32, 4, 8>(s, L, x, w, part, st);
   else if (L.ept == 4) launch_logits_t<BF16, 32, 4, 4>(s, L, x, w, part, st);
   else if (L.ept == 8) launch_logits_t<BF16, 32, 8, 4>(s, L, x, w, part, st);
   else launch_logits_t<BF16, 32, 16, 2>(s, L, x, w, part, st);
