@@ -22,8 +22,9 @@
 //     128 or 256 bytes per clock.
 //   - A persistent grid walks a tile list built on the device from the
 //     segment offsets, so no host round trip is needed.
-//       * Tiles go (segment, n-tile, m-tile), with the m-tile fastest, so
-//         that neighbouring tiles share a weight tile.
+//       * Tiles go (segment, band of 8 m-tiles, n-tile, m-tile), with the
+//         m-tile fastest, so that neighbouring tiles share a weight tile and
+//         a run of them shares a few row tiles.
 //       * Workgroup ids are remapped so that each XCD (and its L2) works on
 //         a contiguous run of tiles.
 //       * Empty segments produce no tiles.
@@ -239,6 +240,8 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
+constexpr int kBandM = 8;  // m-tiles per band of the tile order
+
 // Where tile T lies: its entry (group of a set), rows and columns.
 struct TileGeom {
   int si, g;          // set and group
@@ -257,8 +260,25 @@ __device__ __forceinline__ TileGeom tile_geom(const GroupedParams& p, const Tabl
   t.start = tab.start[ent];
   const int rows = tab.rows[ent];
   const int mt = (rows + BM - 1) / BM;
+  const int nt = (tab.cum[ent + 1] - tab.cum[ent]) / max(mt, 1);
   const int local = T - tab.cum[ent];
-  const int ntile = local / mt, mtile = local - ntile * mt;
+  // Tiles go m-fastest within bands of kBandM m-tiles, then n, then band: a
+  // run of consecutive tiles (one XCD's share of a round) then covers a few
+  // m-tiles times a few n-tiles, so its L2 holds both operands' slices,
+  // instead of one n-tile times every m-tile of a tall segment (which makes
+  // every XCD stream all of that segment's rows for each n-tile).
+  const int full_bands = mt / kBandM;
+  const int in_full = full_bands * kBandM * nt;
+  int ntile, mtile;
+  if (local < in_full) {
+    const int band = local / (kBandM * nt), in = local - band * (kBandM * nt);
+    ntile = in / kBandM;
+    mtile = band * kBandM + (in - ntile * kBandM);
+  } else {
+    const int rem = mt - full_bands * kBandM, in = local - in_full;
+    ntile = in / rem;
+    mtile = full_bands * kBandM + (in - ntile * rem);
+  }
   // A segment of `rows` rows takes mt = ceil(rows / BM) m-tiles: either BM
   // rows each and a short last one, or (balance_m) an even split, so that
   // the tiles sharing a weight tile take the same time.
