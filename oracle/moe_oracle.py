@@ -54,6 +54,19 @@ of each weight matrix (scale = row max |w| / 448), codes by round-to-nearest-
 even of w / scale, both divisions in fp32. The quantised layer is the bf16
 layer with every expert weight replaced by scale * decode(code).
 
+Int4 expert weights (W4A16) follow the notes "混合专家模型 (MoE)：大规模稀疏条件
+计算的架构与工程实践", section 五.1: INT4 weights for the expert layers only,
+activations in 16 bits, the product taken on the dequantised weights. No
+granularity or rounding is given. The readings: one fp32 scale per output row
+(scale = row max |w| / 7), codes q = nearest integer, ties to even, of the
+fp32 quotient w / scale, in [-7, 7]. The quantised layer is the bf16 layer
+with every expert weight replaced by scale * q. The packed storage
+(pack_int4_rows) is the library's layout, not the pages'. Pins: the
+quantisation against a nearest-integer brute force and its invariants (the
+row maximum maps to 7, the error is within half a step), the packing against
+a block worked out by hand (tests/golden/int4_block.txt) and a round trip, and
+a dense layer rebuilt from the dequantised weights.
+
 Training-side router statistics (z-loss, importance, the selection-bias
 update) are readings of passages whose formulas were lost; each function
 states its reading. Pins: closed forms (equal logits, one-hot and uniform
@@ -137,6 +150,59 @@ def quantize_fp8_rows(w) -> tuple:
 def dequantize_fp8_rows(codes, scales) -> np.ndarray:
     """scale_r * decode(code) in fp64 (exact)."""
     return fp8_e4m3_decode(codes) * np.asarray(scales, dtype=F64)[:, None]
+
+
+# ---------------------------------------------------------------- int4 weights (W4A16)
+
+INT4_MAX = 7
+_INT4_NIBBLE = np.array([0, 4, 1, 5, 2, 6, 3, 7])  # nibble holding code j of a packed word
+
+
+def quantize_int4_rows(w) -> tuple:
+    """Per-output-row int4 quantisation of one weight matrix [rows, cols]:
+    scale_r = fp32(max_c |w[r, c]|) / 7 in fp32; q = the nearest integer to
+    fp32(w / scale_r), ties to even, clamped to [-7, 7]; an all-zero row has
+    scale 0 and codes 0. Returns (codes int8, scales fp32)."""
+    w32 = np.asarray(w, dtype=np.float32)
+    amax = np.max(np.abs(w32), axis=1)
+    scale = (amax / np.float32(INT4_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    ratio = (w32 / safe[:, None]).astype(np.float32)
+    q = np.clip(np.rint(ratio.astype(F64)), -INT4_MAX, INT4_MAX).astype(np.int8)
+    q[scale == 0] = 0
+    return q, scale
+
+
+def dequantize_int4_rows(codes, scales) -> np.ndarray:
+    """scale_r * q in fp64 (exact)."""
+    return np.asarray(codes, dtype=F64) * np.asarray(scales, dtype=F64)[:, None]
+
+
+def pack_int4_rows(codes) -> np.ndarray:
+    """The packed storage of int4 codes [rows, cols] (cols a multiple of 64):
+    per block of 64 codes, the little-endian 32-bit word at byte 16 h + 4 s
+    holds codes 16 s + 8 h + j (j = 0..7) as q + 8, code j in nibble j / 2 (j
+    even) or 4 + j / 2 (j odd). Returns uint8 [rows, cols / 2]."""
+    q = np.asarray(codes, dtype=np.int64)
+    rows, cols = q.shape
+    u = (q + 8).reshape(rows, cols // 64, 4, 2, 8).astype(np.uint64)   # [row, block, s, h, j]
+    words = np.zeros((rows, cols // 64, 4, 2), dtype=np.uint64)
+    for j in range(8):
+        words |= u[..., j] << np.uint64(4 * _INT4_NIBBLE[j])
+    words = words.transpose(0, 1, 3, 2)                                # [row, block, h, s]
+    return np.ascontiguousarray(words.astype("<u4")).view(np.uint8).reshape(rows, cols // 2)
+
+
+def unpack_int4_rows(packed, cols: int) -> np.ndarray:
+    """Codes [rows, cols] (int8) from their packed storage (inverse of pack_int4_rows)."""
+    b = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
+    rows = b.shape[0]
+    words = b.reshape(rows, cols // 2).view("<u4").reshape(rows, cols // 64, 2, 4)  # [row, block, h, s]
+    words = words.transpose(0, 1, 3, 2).astype(np.int64)                           # [row, block, s, h]
+    q = np.zeros((rows, cols // 64, 4, 2, 8), dtype=np.int64)
+    for j in range(8):
+        q[..., j] = ((words >> (4 * int(_INT4_NIBBLE[j]))) & 0xF) - 8
+    return q.reshape(rows, cols).astype(np.int8)
 
 
 

@@ -146,3 +146,33 @@ def test_bias_update_wrong_direction_is_caught(monkeypatch):
     orig = O.update_select_bias
     monkeypatch.setattr(O, "update_select_bias", lambda b, c, n, k, g: orig(b, c, n, k, -g))
     _fails(pins.test_select_bias_update_bruteforce)
+
+
+def test_int4_ties_away_from_zero_is_caught(monkeypatch):
+    orig = O.quantize_int4_rows
+
+    def bad(w):
+        q, s = orig(w)
+        w32 = np.asarray(w, dtype=np.float32)
+        r = (w32 / np.where(s > 0, s, np.float32(1))[:, None]).astype(np.float64)
+        half = np.abs(r - np.trunc(r)) == 0.5
+        q = np.where(half & (s[:, None] > 0), np.clip(np.trunc(r) + np.sign(r), -7, 7), q).astype(np.int8)
+        return q, s
+    monkeypatch.setattr(O, "quantize_int4_rows", bad)
+    _fails(pins.test_int4_quantisation_is_nearest_even_bruteforce)
+
+
+def test_int4_scale_over_eight_is_caught(monkeypatch):
+    # reading the int4 range as [-8, 7] with scale = max / 8
+    def bad(w):
+        w32 = np.asarray(w, dtype=np.float32)
+        s = (np.max(np.abs(w32), axis=1) / np.float32(8)).astype(np.float32)
+        r = w32 / np.where(s > 0, s, np.float32(1))[:, None]
+        return np.clip(np.rint(r), -8, 7).astype(np.int8), s
+    monkeypatch.setattr(O, "quantize_int4_rows", bad)
+    _fails(pins.test_int4_row_quantisation_invariants)
+
+
+def test_int4_natural_nibble_order_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "_INT4_NIBBLE", np.arange(8))
+    _fails(pins.test_int4_packing_matches_worked_block_and_round_trips)

@@ -532,3 +532,84 @@ def test_select_bias_update_bruteforce():
         else:
             expect = b[e]
         assert out[e] == expect, e
+
+
+# ------------------------------------------------------------------ int4 expert weights (W4A16)
+
+def _int4_test_rows(rng):
+    w = mi.bf16_bits_to_f32(mi.f32_to_bf16_bits((rng.standard_normal((64, 128)) *
+                                                 np.exp2(rng.uniform(-8, 4, (64, 1)))).astype(np.float32)))
+    w[5] = 0.0                                               # an all-zero row
+    w[7] = 0.0
+    w[7, :8] = [7.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5]    # scale 1: every other entry an exact tie
+    w[9] = 0.0
+    w[9, 3] = -3.0                                           # a negative maximum, alone in its row
+    return w
+
+
+def test_int4_quantisation_is_nearest_even_bruteforce():
+    w = _int4_test_rows(np.random.default_rng(40))
+    q, s = O.quantize_int4_rows(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    nz = s > 0
+    ratio = (w.astype(np.float32) / np.where(nz, s, np.float32(1))[:, None]).astype(np.float32).astype(np.float64)
+    cand = np.arange(-7, 8, dtype=np.float64)
+    dist = np.abs(ratio[..., None] - cand)                   # distance to every code
+    best = dist.min(axis=-1, keepdims=True)
+    tied = dist == best
+    # among the nearest codes take the even one (a tie is between neighbours, so exactly one is even)
+    pick = np.where(tied.sum(-1) > 1, np.argmax(tied & (cand % 2 == 0), axis=-1), np.argmax(tied, axis=-1))
+    expect = cand[pick].astype(np.int8)
+    expect[~nz] = 0
+    np.testing.assert_array_equal(q, expect)
+    np.testing.assert_array_equal(q[7, :8], [7, 0, 2, 2, 0, -2, -2, 4])
+    assert s[7] == 1.0 and s[5] == 0 and not q[5].any()
+
+
+def test_int4_row_quantisation_invariants():
+    w = _int4_test_rows(np.random.default_rng(41))
+    q, s = O.quantize_int4_rows(w)
+    assert np.all(np.abs(q) <= 7)
+    nz = s > 0
+    amax_col = np.argmax(np.abs(w), axis=1)
+    top = q[np.arange(64), amax_col].astype(np.int64)
+    np.testing.assert_array_equal(np.abs(top)[nz], 7)        # the row maximum maps to +-7
+    np.testing.assert_array_equal(np.sign(top)[nz], np.sign(w[np.arange(64), amax_col])[nz])
+    assert q[9, 3] == -7 and s[9] == np.float32(3.0) / np.float32(7.0)
+    deq = O.dequantize_int4_rows(q, s)
+    err = np.abs(deq - w)
+    assert np.all(err[nz] <= (0.5 * s[nz, None].astype(np.float64)) * (1 + 1e-6) + 1e-12)
+
+
+def test_int4_packing_matches_worked_block_and_round_trips():
+    k = np.arange(64)
+    q = ((k % 15) - 7).astype(np.int8)[None]
+    packed = O.pack_int4_rows(q)
+    assert packed.shape == (1, 32) and packed.dtype == np.uint8
+    for line in open(os.path.join(GOLDEN, "int4_block.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        off, hexbytes = line.split(":")
+        want = [int(b, 16) for b in hexbytes.split()]
+        np.testing.assert_array_equal(packed[0, int(off):int(off) + len(want)], want)
+    rng = np.random.default_rng(42)
+    qq = rng.integers(-8, 8, (6, 192)).astype(np.int8)
+    np.testing.assert_array_equal(O.unpack_int4_rows(O.pack_int4_rows(qq), 192), qq)
+    # all-zero codes are bytes 0x88
+    assert np.all(O.pack_int4_rows(np.zeros((2, 64), np.int8)) == 0x88)
+
+
+def test_int4_layer_is_dense_ffn_with_dequantised_weights():
+    # E=1, k=1 with int4 weights: the dense SwiGLU FFN on weights rebuilt as code * scale by torch
+    rng = np.random.default_rng(43)
+    N, d, f = 17, 64, 128
+    x = rng.standard_normal((N, d))
+    wg, wu, wd, _ = rand_layer(rng, 1, d, f)
+    deq, tdeq = [], []
+    for w in (wg[0], wu[0], wd[0]):
+        q, s = O.quantize_int4_rows(w)
+        deq.append(O.dequantize_int4_rows(q, s)[None])
+        tdeq.append((torch.from_numpy(q.astype(np.int64)).double() * torch.from_numpy(s.astype(np.float64))[:, None]).numpy())
+    lr = O.moe_layer(x, rng.standard_normal((1, d)), deq[0], deq[1], deq[2], 1)
+    np.testing.assert_allclose(lr.y, torch_swiglu(x, tdeq[0], tdeq[1], tdeq[2]), rtol=1e-12, atol=1e-13)
