@@ -227,7 +227,7 @@ int moe_update_select_bias(const moe_shape* shape, const int32_t* counts, float 
  * dtype must be MOE_DTYPE_BF16 (else MOE_ERR_UNSUPPORTED).
  * --------------------------------------------------------------------- */
 
-/* Row scales of the FP8 expert weights (device pointers, fp32). */
+/* Row scales of quantised expert weights, FP8 or int4 (device pointers, fp32). */
 typedef struct {
   const float* gate;    /* [E, F]: scale of w_gate row (e, f) */
   const float* up;      /* [E, F] */
@@ -235,7 +235,8 @@ typedef struct {
   const float* s_gate;  /* [S, Fs]; NULL allowed only when S == 0 */
   const float* s_up;    /* [S, Fs] */
   const float* s_down;  /* [S, d] */
-} moe_fp8_scales;
+} moe_weight_scales;
+typedef moe_weight_scales moe_fp8_scales;
 
 /* Quantise a bf16 matrix [rows, cols], row by row:
  *   scales[r]   = max_c |w[r, c]| / 448                     (fp32 division)
@@ -268,6 +269,57 @@ int moe_forward_fp8(const moe_shape* shape, const void* x, const void* w_router,
                     float* y, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                     int32_t* perm, int32_t* slot_pos, double* prob_sum, double* balance_stat,
                     void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * Int4 expert weights (W4A16). The notes "混合专家模型 (MoE)：大规模稀疏条件
+ * 计算的架构与工程实践", section 五.1 (the memory wall of inference), suggest
+ * INT4 weights with FP16/BF16 activations for the expert layers only, the
+ * product taken on the dequantised weights. They give no scale granularity
+ * or rounding; these calls use one fp32 scale per output row of each weight
+ * matrix and symmetric codes q in [-7, 7]. The layer they compute is the
+ * bf16 layer with every expert weight replaced by scale[row] * q. x, the
+ * router and h stay bf16; the shape's dtype must be MOE_DTYPE_BF16 (else
+ * MOE_ERR_UNSUPPORTED). These layers never split tail tiles along K.
+ *
+ * Packed format: a row of K codes is K/2 bytes, in blocks of 64 codes (32
+ * bytes). In the block of codes [k0, k0 + 64), the little-endian 32-bit
+ * word at byte 16*h + 4*s (h = 0, 1; s = 0..3) holds codes
+ * k0 + 16*s + 8*h + j, j = 0..7, each as u = q + 8 in a 4-bit field: code j
+ * in nibble j/2 when j is even and in nibble 4 + j/2 when j is odd (nibble
+ * n = bits [4n, 4n + 4)). K must be a multiple of 64.
+ * --------------------------------------------------------------------- */
+
+/* Quantise a bf16 matrix [rows, cols], row by row:
+ *   scales[r] = max_c |w[r, c]| / 7                             (fp32 division)
+ *   q[r, c]   = w[r, c] / scales[r] rounded to the nearest integer, ties to
+ *               even (fp32 division), clamped to [-7, 7]
+ * An all-zero row gets scale 0 and codes 0 (bytes 0x88).
+ *   w_bf16 [rows, cols] bf16 in;  packed [rows, cols/2] uint8 out (format
+ *   above);  scales [rows] fp32 out
+ * cols must be a multiple of 64 and rows < 2^31 (else MOE_ERR_UNSUPPORTED). */
+int moe_quantize_int4(int64_t rows, int32_t cols, const void* w_bf16, uint8_t* packed, float* scales,
+                      hipStream_t stream);
+
+/* moe_grouped_swiglu with int4 weights: w_gate/w_up [G, F, d/2] and w_down
+ * [G, d, F/2] packed as above; sc_gate/sc_up [G, F] and sc_down [G, d] their
+ * row scales. Everything else as in moe_grouped_swiglu (bf16 x and h). */
+int moe_grouped_swiglu_int4(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const void* x,
+                            const int32_t* perm, int32_t rows_per_token, const int32_t* offsets,
+                            int32_t max_rows, const uint8_t* w_gate, const uint8_t* w_up,
+                            const uint8_t* w_down, const float* sc_gate, const float* sc_up,
+                            const float* sc_down, float* out, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* moe_forward with int4 routed and shared expert weights (packed) and their
+ * row scales. The router weights stay bf16. Outputs, workspace and events
+ * as in moe_forward. */
+int moe_forward_int4(const moe_shape* shape, const void* x, const void* w_router,
+                     const float* logit_bias, const float* select_bias, const uint8_t* w_gate,
+                     const uint8_t* w_up, const uint8_t* w_down, const uint8_t* s_gate,
+                     const uint8_t* s_up, const uint8_t* s_down, const moe_weight_scales* scales,
+                     float* y, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                     int32_t* perm, int32_t* slot_pos, double* prob_sum, double* balance_stat,
+                     void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -38,9 +38,13 @@ class MoEShape(ctypes.Structure):
                    int(bool(renormalize)), dtype)
 
 
-class MoEFp8Scales(ctypes.Structure):
-    """moe_fp8_scales: device pointers to the fp32 row scales of the FP8 expert weights."""
+class MoEWeightScales(ctypes.Structure):
+    """moe_weight_scales (alias moe_fp8_scales): device pointers to the fp32 row scales of the
+    quantised (FP8 or int4) expert weights."""
     _fields_ = [(n, ctypes.c_void_p) for n in ("gate", "up", "down", "s_gate", "s_up", "s_down")]
+
+
+MoEFp8Scales = MoEWeightScales
 
 
 _lib = None
@@ -65,8 +69,14 @@ _SIGS = {
     "moe_grouped_swiglu_fp8": (ctypes.c_int, [_SHP, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P,
                                               _P, _P, _P, _SZ, _P]),
     "moe_forward_fp8": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                       ctypes.POINTER(MoEFp8Scales), _P, _P, _P, _P, _P, _P, _P,
+                                       ctypes.POINTER(MoEWeightScales), _P, _P, _P, _P, _P, _P, _P,
                                        _P, _P, _P, _SZ, _P, _P]),
+    "moe_quantize_int4": (ctypes.c_int, [ctypes.c_int64, _I, _P, _P, _P, _P]),
+    "moe_grouped_swiglu_int4": (ctypes.c_int, [_SHP, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P,
+                                               _P, _P, _P, _SZ, _P]),
+    "moe_forward_int4": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        ctypes.POINTER(MoEWeightScales), _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P, _P, _SZ, _P, _P]),
 }
 
 
@@ -176,20 +186,36 @@ def moe_grouped_swiglu_fp8(shape, n_groups, d_ff, x, perm, rows_per_token, offse
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
 
 
-def fp8_scales(gate, up, down, s_gate=None, s_up=None, s_down=None) -> MoEFp8Scales:
-    return MoEFp8Scales(*[_ptr(t) for t in (gate, up, down, s_gate, s_up, s_down)])
+def weight_scales(gate, up, down, s_gate=None, s_up=None, s_down=None) -> MoEWeightScales:
+    return MoEWeightScales(*[_ptr(t) for t in (gate, up, down, s_gate, s_up, s_down)])
 
 
-def moe_forward_fp8(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate,
-                    s_up, s_down, scales: MoEFp8Scales, y, topk_idx, topk_w, counts, offsets, perm,
-                    slot_pos, prob_sum, balance_stat, ws,
-                    stage_events: Optional[Sequence[int]] = None, stream=None):
+fp8_scales = weight_scales
+
+
+def moe_quantize_int4(rows, cols, w_bf16, packed, scales, stream=None):
+    _check("moe_quantize_int4", lib().moe_quantize_int4(
+        int(rows), int(cols), _ptr(w_bf16), _ptr(packed), _ptr(scales), _stream(stream)))
+
+
+def moe_grouped_swiglu_int4(shape, n_groups, d_ff, x, perm, rows_per_token, offsets, max_rows,
+                            w_gate, w_up, w_down, sc_gate, sc_up, sc_down, out, ws, stream=None):
+    _check("moe_grouped_swiglu_int4", lib().moe_grouped_swiglu_int4(
+        ctypes.byref(shape), int(n_groups), int(d_ff), _ptr(x), _ptr(perm), int(rows_per_token),
+        _ptr(offsets), int(max_rows), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sc_gate),
+        _ptr(sc_up), _ptr(sc_down), _ptr(out), _ptr(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def _forward_quantised(name, shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down,
+                       s_gate, s_up, s_down, scales, y, topk_idx, topk_w, counts, offsets, perm,
+                       slot_pos, prob_sum, balance_stat, ws, stage_events, stream):
     ev = None
     if stage_events is not None:
         if len(stage_events) != MOE_STAGE_EVENTS:
             raise ValueError(f"stage_events needs {MOE_STAGE_EVENTS} hipEvent_t handles")
         ev = (ctypes.c_void_p * MOE_STAGE_EVENTS)(*stage_events)
-    _check("moe_forward_fp8", lib().moe_forward_fp8(
+    _check(name, getattr(lib(), name)(
         ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias),
         _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down),
         ctypes.byref(scales) if scales is not None else None, _ptr(y),
@@ -197,6 +223,24 @@ def moe_forward_fp8(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w
         _ptr(prob_sum), _ptr(balance_stat), _ptr(ws),
         ws.numel() * ws.element_size() if ws is not None else 0,
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)))
+
+
+def moe_forward_fp8(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate,
+                    s_up, s_down, scales: MoEWeightScales, y, topk_idx, topk_w, counts, offsets, perm,
+                    slot_pos, prob_sum, balance_stat, ws,
+                    stage_events: Optional[Sequence[int]] = None, stream=None):
+    _forward_quantised("moe_forward_fp8", shape, x, w_router, logit_bias, select_bias, w_gate, w_up,
+                       w_down, s_gate, s_up, s_down, scales, y, topk_idx, topk_w, counts, offsets, perm,
+                       slot_pos, prob_sum, balance_stat, ws, stage_events, stream)
+
+
+def moe_forward_int4(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate,
+                     s_up, s_down, scales: MoEWeightScales, y, topk_idx, topk_w, counts, offsets, perm,
+                     slot_pos, prob_sum, balance_stat, ws,
+                     stage_events: Optional[Sequence[int]] = None, stream=None):
+    _forward_quantised("moe_forward_int4", shape, x, w_router, logit_bias, select_bias, w_gate, w_up,
+                       w_down, s_gate, s_up, s_down, scales, y, topk_idx, topk_w, counts, offsets, perm,
+                       slot_pos, prob_sum, balance_stat, ws, stage_events, stream)
 
 
 def moe_router_aux(shape, x, w_router, logit_bias, topk_idx, topk_w, z_loss, importance,

@@ -178,10 +178,13 @@ __device__ __forceinline__ bf16_t silu_mul_bf16(float g, float u) {
 // bytes per clock) over distinct banks:
 //   PPR = 8 (128-byte rows): g(r) = (r & 7) ^ ((r >> 3) & 1)
 //   PPR = 4 (64-byte rows):  g(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1)
+//   PPR = 2 (32-byte rows of int4 weights, read 16 bytes per lane per step):
+//                            g(r) = ((r >> 2) ^ (r >> 3)) & 1
 template <int PPR>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (PPR == 8) return (row & 7) ^ ((row >> 3) & 1);
-  else return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+  else if constexpr (PPR == 4) return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+  else return ((row >> 2) ^ (row >> 3)) & 1;
 }
 
 // Copy 16 bytes per lane from global memory straight into LDS at
@@ -241,6 +244,23 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 }
 
 constexpr int kBandM = 8;  // m-tiles per band of the tile order
+
+// Int4 weights: 8 offset-binary codes u = q + 8 (nibbles of w) -> the bf16
+// values 128 + u, exactly (a bf16 with exponent 2^7 steps by 1 up to 255):
+// each nibble goes into the low mantissa bits of 0x4300 (= 128). Element 2i
+// takes nibble i and element 2i + 1 nibble i + 4, which fixes the packing.
+// The MFMA then sums x * (q + 136); the 136 * sum(x) part is removed in the
+// epilogue (an extra MFMA per row block against a fragment of 136s).
+__device__ __forceinline__ bf16x8_t int4x8_to_bf16_biased(uint32_t w) {
+  constexpr uint32_t kMask = 0x000F000Fu, kExp = 0x43004300u;
+  u32x4_t r;
+  r.x = (w & kMask) | kExp;
+  r.y = ((w >> 4) & kMask) | kExp;
+  r.z = ((w >> 8) & kMask) | kExp;
+  r.w = ((w >> 12) & kMask) | kExp;
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+constexpr uint32_t kBf16Of136 = 0x4308u;  // 136 = 128 + 8: the offset of the biased int4 values
 
 // Where tile T lies: its entry (group of a set), rows and columns.
 struct TileGeom {
@@ -318,10 +338,13 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int G, long long cap_
 // The epilogue of one tile from its accumulators. acc[i][j][v] holds column
 // (lane & 31) and row 8 (v / 4) + 4 (lane / 32) + (v % 4) of 32x32 block
 // (i, j). Phase 1 writes h = bf16(silu(g) * u), phase 2 writes fp32 O;
-// with FP8 weights each column is first multiplied by its weight row's scale.
-template <int BM, int BN, int WGM, int WGN, bool W8, bool P1, int FM, int NB>
+// with quantised weights (WQ = 8: FP8, 4: int4) each column is first
+// multiplied by its weight row's scale, and with int4 weights the offset
+// sums corr[i] (136 * sum(x) of each row) are subtracted before that.
+template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, int FM, int NB>
 __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetView& S, const TileGeom& t,
-                                           int d, int lane, int wm, int wn) {
+                                           int d, int lane, int wm, int wn, const f32x16_t* corr = nullptr) {
+  constexpr bool WS = WQ != 0, W4 = WQ == 4;
   constexpr int TM = BM / WGM;
   constexpr int BH = P1 ? BN / 2 : BN;
   constexpr int TN = BH / WGN;
@@ -334,7 +357,7 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     sc0[j] = sc1[j] = 1.f;
-    if constexpr (W8) {
+    if constexpr (WS) {
       const int c = min(col0 + j * 32, ncols - 1);
       if constexpr (P1) {
         sc0[j] = S.sg[(size_t)g * F + c];
@@ -354,18 +377,20 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
         const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
         if (decltype(check)::value && r >= t.mvalid) continue;
         const size_t row = (size_t)(t.start + t.m0 + r);
+        float c = 0.f;
+        if constexpr (W4) c = corr[i][v];
         if constexpr (P1) {
           bf16_t* hrow = static_cast<bf16_t*>(S.h) + row * F + col0;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             if (col0 + j * 32 < ncols)
-              hrow[j * 32] = W8 ? silu_mul_bf16(acc[i][j][v] * sc0[j], acc[i][j + FN][v] * sc1[j])
+              hrow[j * 32] = WS ? silu_mul_bf16((acc[i][j][v] - c) * sc0[j], (acc[i][j + FN][v] - c) * sc1[j])
                                 : silu_mul_bf16(acc[i][j][v], acc[i][j + FN][v]);
         } else {
           float* orow = S.out + row * d + col0;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            if (col0 + j * 32 < ncols) orow[j * 32] = W8 ? acc[i][j][v] * sc0[j] : acc[i][j][v];
+            if (col0 + j * 32 < ncols) orow[j * 32] = WS ? (acc[i][j][v] - c) * sc0[j] : acc[i][j][v];
         }
       }
     }
@@ -379,18 +404,25 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
 // Workgroup tile BM x BN x BK with NS LDS stages, filled by direct global->LDS
 // copies issued NS-1 steps ahead. WGM x WGN waves; wave tile (BM/WGM) x
 // (BN/WGN) of v_mfma_f32_32x32x16_bf16 blocks with fp32 accumulators.
-// W8: the weights (B) are FP8 E4M3 codes. They are copied to LDS as codes
-// (half the bytes), widened to bf16 exactly as each fragment is read, and
-// each output column is multiplied by its weight row's scale in the epilogue.
+// WQ = 8: the weights (B) are FP8 E4M3 codes. They are copied to LDS as
+// codes (half the bytes), widened to bf16 exactly as each fragment is read,
+// and each output column is multiplied by its weight row's scale in the
+// epilogue. WQ = 4: int4 codes, two per byte (a quarter of the bytes). Each
+// lane reads its 16 bytes of a B row once per step (the 4 words of its 4
+// k16 steps) and widens a word per k16 step to the biased values 128 + u;
+// an extra MFMA per row block accumulates 136 * sum(x), which the epilogue
+// subtracts before the scale.
 // SPREAD: the copies that refill a stage go out in equal pieces, one before
 // each k16 step of the first half of the step, instead of all at its start,
 // so that fewer copies queue at once behind the barrier (3-5% faster on
 // 256 x 256 tiles; the second half of the step still covers their latency).
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB, bool W8, bool P1, bool SPREAD>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB, int WQ, bool P1, bool SPREAD>
 __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(GroupedParams p) {
-  using BT = typename std::conditional<W8, uint8_t, bf16_t>::type;  // weight element
+  constexpr bool W8 = WQ == 8, W4 = WQ == 4, WS = WQ != 0;
+  using BT = typename std::conditional<WS, uint8_t, bf16_t>::type;  // weight storage unit
+  constexpr int KDIV = W4 ? 2 : 1;            // K values per BT unit of a weight row
   constexpr int ROWA = BK * 2;                // LDS bytes per A row (bf16)
-  constexpr int ROWB = BK * (int)sizeof(BT);  // LDS bytes per B row
+  constexpr int ROWB = BK * (int)sizeof(BT) / KDIV;  // LDS bytes per B row
   constexpr int PPA = ROWA / 16, PPB = ROWB / 16;        // 16-byte pieces per row
   constexpr int RPIA = kWave / PPA, RPIB = kWave / PPB;  // rows per 1 KB copy instruction
   constexpr int EPP = 16 / (int)sizeof(BT);   // B elements per 16-byte piece
@@ -407,7 +439,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
   constexpr int L = A_INS + B_INS;          // vector-memory ops per wave per stage
   constexpr int STAGE_A = BM * ROWA, STAGE = STAGE_A + BN * ROWB;
   static_assert(BK == 32 || BK == 64, "K step");
-  static_assert(!W8 || BK == 64, "FP8 weights: 64-byte rows");
+  static_assert(!WS || BK == 64, "quantised weights: 64 K values per row per stage");
   static_assert(A_INS >= 1 && B_INS >= 1 && FM >= 1 && FN >= 1 && NS >= 2 && NS <= 6, "tile shape");
   static_assert(A_INS * RPIA * WAVES == BM && B_INS * RPIB * WAVES == BN, "copy slots cover the tile");
   static_assert(!P1 || (BN / 2) % (RPIB * B_INS) == 0, "a wave's B rows come from one matrix");
@@ -483,16 +515,16 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     const BT* b_base;
     if constexpr (P1) {
       const bool up = wave * B_INS * RPIB >= BN / 2;
-      b_base = static_cast<const BT*>(up ? S.wu : S.wg) + (size_t)g * F * d;
+      b_base = static_cast<const BT*>(up ? S.wu : S.wg) + (size_t)g * F * d / KDIV;
     } else {
-      b_base = static_cast<const BT*>(S.wd) + (size_t)g * d * F;
+      b_base = static_cast<const BT*>(S.wd) + (size_t)g * d * F / KDIV;
     }
     uint32_t b_off[B_INS];
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
       const int r = (wave * B_INS + i) * RPIB + crowB;    // tile row
       const int mr = P1 ? (r % (BN / 2)) : r;              // row within its weight matrix tile
-      b_off[i] = (uint32_t)(n0 + min(mr, lastq)) * (uint32_t)K + (uint32_t)((cpcB ^ swz<PPB>(r)) * EPP);
+      b_off[i] = (uint32_t)(n0 + min(mr, lastq)) * (uint32_t)(K / KDIV) + (uint32_t)((cpcB ^ swz<PPB>(r)) * EPP);
     }
     const uint32_t a_lds0 = lds_addr(&s_tile[0][(wave * A_INS) * 1024]);
     const uint32_t b_lds0 = lds_addr(&s_tile[0][STAGE_A + (wave * B_INS) * 1024]);
@@ -512,7 +544,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
       for (int i = 0; i < A_INS; ++i)
         if (i < a_act) dma16(a_base + a_off[i] + ko, a_lds0 + st * STAGE + i * 1024);
 #pragma unroll
-      for (int i = 0; i < B_INS; ++i) dma16(b_base + b_off[i] + ko, b_lds0 + st * STAGE + i * 1024);
+      for (int i = 0; i < B_INS; ++i) dma16(b_base + b_off[i] + ko / KDIV, b_lds0 + st * STAGE + i * 1024);
     };
     // copies [c0, c1) of stage kt, in the order A (active ones) then B
     auto issue_part = [&](int kt, int c0, int c1) {
@@ -524,18 +556,23 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
         if (c < A_INS) {
           if (c < a_act) dma16(a_base + a_off[c] + ko, a_lds0 + st * STAGE + c * 1024);
         } else {
-          dma16(b_base + b_off[c - A_INS] + ko, b_lds0 + st * STAGE + (c - A_INS) * 1024);
+          dma16(b_base + b_off[c - A_INS] + ko / KDIV, b_lds0 + st * STAGE + (c - A_INS) * 1024);
         }
       }
     };
 
     f32x16_t acc[FM][NB];
+    f32x16_t corr[W4 ? FM : 1];  // int4: 136 * sum(x) per row
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+      if constexpr (W4)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) corr[i][v] = 0.f;
+    }
 
     // 32-row MFMA blocks of this wave that hold segment rows: a segment's last
     // tile is often short, and its empty blocks skip their reads and MFMAs.
@@ -551,6 +588,15 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
       if (!SPREAD && kt + NS - 1 < nk) issue(kt + NS - 1); /* refills the stage read in step kt-1 */ \
       const uint8_t* sa = &s_tile[kt % NS][0];                                                   \
       const uint8_t* sb = sa + STAGE_A;                                                          \
+      u32x4_t wq[W4 ? NB : 1]; /* int4: this lane's 4 words (one per k16 step) of each B row */  \
+      if constexpr (W4) {                                                                        \
+        _Pragma("unroll") for (int j = 0; j < NB; ++j) {                                         \
+          const int jj = P1 ? (j % FN) : j;                                                      \
+          const int half = P1 ? (j / FN) * (BN / 2) : 0;                                         \
+          const int r = half + wn * TN + jj * 32 + (lane & 31);                                  \
+          wq[j] = *reinterpret_cast<const u32x4_t*>(sb + r * ROWB + (((lane >> 5) ^ swz<PPB>(r)) << 4)); \
+        }                                                                                        \
+      }                                                                                          \
       _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                   \
         if constexpr (SPREAD) {                                                                  \
           /* the refill's copies, spread over the first half of the k16 steps */                 \
@@ -570,7 +616,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
           const int jj = P1 ? (j % FN) : j;                                                      \
           const int half = P1 ? (j / FN) * (BN / 2) : 0;                                         \
           const int r = half + wn * TN + jj * 32 + (lane & 31);                                  \
-          if constexpr (W8) {                                                                    \
+          if constexpr (W4) {                                                                    \
+            bfr[j] = int4x8_to_bf16_biased(wq[j][ks]);                                           \
+          } else if constexpr (W8) {                                                             \
             /* piece ks holds the 16 codes of this k16 step; lanes 32-63 take its upper 8 */     \
             const u32x2_t q = *reinterpret_cast<const u32x2_t*>(sb + r * ROWB + ((ks ^ swz<PPB>(r)) << 4) + ((lane >> 5) << 3)); \
             bfr[j] = fp8x8_to_bf16(q.x, q.y);                                                    \
@@ -582,6 +630,11 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
           if (!(ACTIVE(i))) continue;                                                            \
           _Pragma("unroll") for (int j = 0; j < NB; ++j)                                         \
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0); \
+          if constexpr (W4) {                                                                    \
+            const u32x4_t k136 = {kBf16Of136 * 0x10001u, kBf16Of136 * 0x10001u,                  \
+                                  kBf16Of136 * 0x10001u, kBf16Of136 * 0x10001u};                \
+            corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], __builtin_bit_cast(bf16x8_t, k136), corr[i], 0, 0, 0); \
+          }                                                                                      \
         }                                                                                        \
       }                                                                                          \
     }
@@ -612,7 +665,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
           for (int v = 0; v < 16; ++v) dst[((i * NB + j) * 16 + v) * NT + tid] = acc[i][j][v];
       continue;
     }
-    store_tile<BM, BN, WGM, WGN, W8, P1>(acc, S, tg, d, lane, wm, wn);
+    store_tile<BM, BN, WGM, WGN, WQ, P1>(acc, S, tg, d, lane, wm, wn, corr);
   }
 }
 
@@ -635,8 +688,9 @@ __global__ __launch_bounds__(256) void split_sum_kernel(float* __restrict__ ws) 
 // The epilogue of the split tail tiles of the launch before it (same
 // parameters, `main_grid` workgroups), from part 0: workgroup b finishes
 // tail tile b. Workgroups past the tail exit.
-template <int BM, int BN, int WGM, int WGN, bool W8, bool P1>
+template <int BM, int BN, int WGM, int WGN, int WQ, bool P1>
 __global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedParams p, int main_grid) {
+  static_assert(WQ != 4, "int4 layers do not split");
   constexpr int TM = BM / WGM, FM = TM / 32;
   constexpr int BH = P1 ? BN / 2 : BN;
   constexpr int TN = BH / WGN, FN = TN / 32;
@@ -666,7 +720,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedPar
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = src[((size_t)(i * NB + j) * 16 + v) * NT];
-  store_tile<BM, BN, WGM, WGN, W8, P1>(acc, S, tg, d, lane, wm, wn);
+  store_tile<BM, BN, WGM, WGN, WQ, P1>(acc, S, tg, d, lane, wm, wn);
 }
 
 // =====================================================================  fp32 SIMT
@@ -778,41 +832,50 @@ int grid_for(long long ub, int per_cu) {
 // per_cu: workgroups launched per CU at most. 1 is a persistent grid (each
 // workgroup walks the tile list with stride gridDim.x); a large value
 // launches about one workgroup per tile.
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, bool W8, bool SPREAD = false, int MINB = 1>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int WQ, bool SPREAD = false, int MINB = 1>
 void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) {
   const int BH = phase == 1 ? BN / 2 : BN;
   const int grid = grid_for(tiles_upper_bound(p, phase, BM, BH), per_cu);
   if (phase == 1)
-    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, W8, true, SPREAD>), dim3(grid),
+    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
   else
-    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, W8, false, SPREAD>), dim3(grid),
+    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
-  if (p.split_ws && p.split_cap > kSplitHeader) {
-    hipLaunchKernelGGL(split_sum_kernel<BM * BN>, dim3(1024), dim3(256), 0, st, p.split_ws);
-    if (phase == 1)
-      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, W8, true>), dim3(grid), dim3(WGM * WGN * 64),
-                         0, st, p, grid);
-    else
-      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, W8, false>), dim3(grid), dim3(WGM * WGN * 64),
-                         0, st, p, grid);
+  if constexpr (WQ != 4) {  // int4 launches get no split workspace
+    if (p.split_ws && p.split_cap > kSplitHeader) {
+      hipLaunchKernelGGL(split_sum_kernel<BM * BN>, dim3(1024), dim3(256), 0, st, p.split_ws);
+      if (phase == 1)
+        hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, true>), dim3(grid), dim3(WGM * WGN * 64),
+                           0, st, p, grid);
+      else
+        hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false>), dim3(grid), dim3(WGM * WGN * 64),
+                           0, st, p, grid);
+    }
   }
 }
 
 // tile height from the mean routed rows per expert segment
 bool large_tiles(long long rows, int groups) { return rows / std::max(1, groups) >= 128; }
 
-template <bool W8>
-void launch_bf16_class(const GroupedParams& p, int phase, hipStream_t stream) {
-  if (large_tiles(p.set[0].max_rows, p.set[0].n_groups)) {
+template <int WQ>
+void launch_class(const GroupedParams& p, int phase, hipStream_t stream) {
+  if constexpr (WQ == 4) {
+    // int4 weights (a decode format): 64 x 256 tiles, 16 KB stages, two
+    // workgroups per CU; no split tail tiles
+    GroupedParams q = p;
+    q.split_ws = nullptr;
+    q.split_cap = 0;
+    launch_mfma<64, 256, 64, 1, 4, 4, 4, false, 2>(q, phase, 2, stream);
+  } else if (large_tiles(p.set[0].max_rows, p.set[0].n_groups)) {
     // persistent grid with even m-tiles: the workgroups that share a weight
     // tile run in step, so their copies of it hit in L2
     GroupedParams q = p;
     q.balance_m = 1;
-    launch_mfma<256, 256, 64, 2, 4, 2, W8, true>(q, phase, 1, stream);
+    launch_mfma<256, 256, 64, 2, 4, 2, WQ, true>(q, phase, 1, stream);
   } else {
     // FP8 weights halve the B stages (80 KB of LDS in all), so two workgroups share a CU
-    launch_mfma<64, 256, 64, 1, 4, 3, W8>(p, phase, W8 ? 2 : 1, stream);
+    launch_mfma<64, 256, 64, 1, 4, 3, WQ>(p, phase, WQ == 8 ? 2 : 1, stream);
   }
 }
 
@@ -832,10 +895,12 @@ int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream) {
       hipLaunchKernelGGL(grouped_f32_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, p);
     else
       hipLaunchKernelGGL(grouped_f32_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, p);
-  } else if (p.w8) {
-    launch_bf16_class<true>(p, phase, stream);
+  } else if (p.wq == 8) {
+    launch_class<8>(p, phase, stream);
+  } else if (p.wq == 4) {
+    launch_class<4>(p, phase, stream);
   } else {
-    launch_bf16_class<false>(p, phase, stream);
+    launch_class<0>(p, phase, stream);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -91,9 +91,10 @@ int do_permute(const moe_shape& s, const int32_t* idx, const double* prob_sum, i
                         reinterpret_cast<int32_t*>(at(ws, L.base)), st);
 }
 
+// wq: expert weight format (0 bf16/fp32, 8 FP8 codes, 4 packed int4 codes; the last two with row scales)
 int grouped_impl(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const void* x,
                  const int32_t* perm, int32_t rows_per_token, const int32_t* offsets, int32_t max_rows,
-                 const void* w_gate, const void* w_up, const void* w_down, const float* sc_gate,
+                 const void* w_gate, const void* w_up, const void* w_down, int wq, const float* sc_gate,
                  const float* sc_up, const float* sc_down, float* out, void* ws, size_t ws_bytes,
                  hipStream_t stream) {
   if (!shape) return MOE_ERR_INVALID_ARG;
@@ -113,7 +114,7 @@ int grouped_impl(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const v
   p.n_tokens = s.n_tokens;
   p.d_model = s.d_model;
   p.dtype = s.dtype;
-  p.w8 = sc_gate != nullptr;
+  p.wq = wq;
   if (s.dtype == MOE_DTYPE_BF16 && ws_bytes >= need + 256) {  // workspace past h: tail-tile K-parts
     p.split_ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + need);
     p.split_cap = (long long)((ws_bytes - need) / sizeof(float));
@@ -191,7 +192,7 @@ int moe_grouped_swiglu(const moe_shape* shape, int32_t n_groups, int32_t d_ff, c
                        int32_t max_rows, const void* w_gate, const void* w_up, const void* w_down,
                        float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   return grouped_impl(shape, n_groups, d_ff, x, perm, rows_per_token, offsets, max_rows, w_gate, w_up,
-                      w_down, nullptr, nullptr, nullptr, out, ws, ws_bytes, stream);
+                      w_down, 0, nullptr, nullptr, nullptr, out, ws, ws_bytes, stream);
 }
 
 int moe_grouped_swiglu_fp8(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const void* x,
@@ -204,7 +205,28 @@ int moe_grouped_swiglu_fp8(const moe_shape* shape, int32_t n_groups, int32_t d_f
   if (!sc_gate || !sc_up || !sc_down) return MOE_ERR_INVALID_ARG;
   if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   return grouped_impl(shape, n_groups, d_ff, x, perm, rows_per_token, offsets, max_rows, w_gate, w_up,
-                      w_down, sc_gate, sc_up, sc_down, out, ws, ws_bytes, stream);
+                      w_down, 8, sc_gate, sc_up, sc_down, out, ws, ws_bytes, stream);
+}
+
+int moe_grouped_swiglu_int4(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const void* x,
+                            const int32_t* perm, int32_t rows_per_token, const int32_t* offsets,
+                            int32_t max_rows, const uint8_t* w_gate, const uint8_t* w_up,
+                            const uint8_t* w_down, const float* sc_gate, const float* sc_up,
+                            const float* sc_down, float* out, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (!shape) return MOE_ERR_INVALID_ARG;
+  if (!sc_gate || !sc_up || !sc_down) return MOE_ERR_INVALID_ARG;
+  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  return grouped_impl(shape, n_groups, d_ff, x, perm, rows_per_token, offsets, max_rows, w_gate, w_up,
+                      w_down, 4, sc_gate, sc_up, sc_down, out, ws, ws_bytes, stream);
+}
+
+int moe_quantize_int4(int64_t rows, int32_t cols, const void* w_bf16, uint8_t* packed, float* scales,
+                      hipStream_t stream) {
+  if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!w_bf16 || !packed || !scales)) return MOE_ERR_INVALID_ARG;
+  if (cols % 64 || rows >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  return launch_quantize_int4(rows, cols, w_bf16, packed, scales, stream);
 }
 
 int moe_quantize_fp8(int64_t rows, int32_t cols, const void* w_bf16, uint8_t* codes, float* scales,
@@ -229,7 +251,7 @@ int moe_combine(const moe_shape* shape, const float* expert_out, const int32_t* 
 static int forward_impl(const moe_shape* shape, const void* x, const void* w_router,
                         const float* logit_bias, const float* select_bias, const void* w_gate,
                         const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
-                        const void* s_down, const moe_fp8_scales* sc, float* y, int32_t* topk_idx,
+                        const void* s_down, int wq, const moe_weight_scales* sc, float* y, int32_t* topk_idx,
                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* slot_pos, double* prob_sum, double* balance_stat, void* ws,
                         size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
@@ -280,7 +302,7 @@ static int forward_impl(const moe_shape* shape, const void* x, const void* w_rou
     R.w_up = w_up;
     R.w_down = w_down;
     if (sc) {
-      p.w8 = 1;
+      p.wq = wq;
       R.sc_gate = sc->gate;
       R.sc_up = sc->up;
       R.sc_down = sc->down;
@@ -325,7 +347,23 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
                 int32_t* slot_pos, double* prob_sum, double* balance_stat, void* ws,
                 size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
   return forward_impl(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
-                      s_down, nullptr, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
+                      s_down, 0, nullptr, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
+                      balance_stat, ws, ws_bytes, stage_events, stream);
+}
+
+static int forward_quantised(int wq, const moe_shape* shape, const void* x, const void* w_router,
+                             const float* logit_bias, const float* select_bias, const uint8_t* w_gate,
+                             const uint8_t* w_up, const uint8_t* w_down, const uint8_t* s_gate,
+                             const uint8_t* s_up, const uint8_t* s_down, const moe_weight_scales* scales,
+                             float* y, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* perm, int32_t* slot_pos, double* prob_sum, double* balance_stat,
+                             void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+  if (!shape || !scales) return MOE_ERR_INVALID_ARG;
+  if (!scales->gate || !scales->up || !scales->down) return MOE_ERR_INVALID_ARG;
+  if (shape->n_shared > 0 && (!scales->s_gate || !scales->s_up || !scales->s_down)) return MOE_ERR_INVALID_ARG;
+  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  return forward_impl(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
+                      s_down, wq, scales, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
                       balance_stat, ws, ws_bytes, stage_events, stream);
 }
 
@@ -336,13 +374,21 @@ int moe_forward_fp8(const moe_shape* shape, const void* x, const void* w_router,
                     float* y, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                     int32_t* perm, int32_t* slot_pos, double* prob_sum, double* balance_stat,
                     void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
-  if (!shape || !scales) return MOE_ERR_INVALID_ARG;
-  if (!scales->gate || !scales->up || !scales->down) return MOE_ERR_INVALID_ARG;
-  if (shape->n_shared > 0 && (!scales->s_gate || !scales->s_up || !scales->s_down)) return MOE_ERR_INVALID_ARG;
-  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
-  return forward_impl(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
-                      s_down, scales, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
-                      balance_stat, ws, ws_bytes, stage_events, stream);
+  return forward_quantised(8, shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
+                           s_down, scales, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
+                           balance_stat, ws, ws_bytes, stage_events, stream);
+}
+
+int moe_forward_int4(const moe_shape* shape, const void* x, const void* w_router,
+                     const float* logit_bias, const float* select_bias, const uint8_t* w_gate,
+                     const uint8_t* w_up, const uint8_t* w_down, const uint8_t* s_gate,
+                     const uint8_t* s_up, const uint8_t* s_down, const moe_weight_scales* scales,
+                     float* y, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                     int32_t* perm, int32_t* slot_pos, double* prob_sum, double* balance_stat,
+                     void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+  return forward_quantised(4, shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
+                           s_down, scales, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
+                           balance_stat, ws, ws_bytes, stage_events, stream);
 }
 
 int moe_router_aux(const moe_shape* shape, const void* x, const void* w_router, const float* logit_bias,

@@ -64,10 +64,10 @@ struct SegSet {
   int32_t rows_per_token;
   int32_t max_rows;        // rows at or past this are never computed
   int32_t d_ff;
-  const void* w_gate;      // [G, d_ff, d]  (bf16, fp32, or FP8 E4M3 codes)
+  const void* w_gate;      // [G, d_ff, d]  (bf16, fp32, FP8 E4M3 codes, or [G, d_ff, d/2] packed int4)
   const void* w_up;        // [G, d_ff, d]
   const void* w_down;      // [G, d, d_ff]
-  const float* sc_gate;    // FP8 weights only: [G, d_ff] row scales of w_gate
+  const float* sc_gate;    // quantised weights only: [G, d_ff] row scales of w_gate
   const float* sc_up;      // [G, d_ff]
   const float* sc_down;    // [G, d]
   void* h;                 // [max_rows, d_ff]: gate|up output, down input
@@ -82,7 +82,8 @@ struct GroupedParams {
   int32_t d_model;
   int32_t dtype;
   int32_t balance_m;       // 1: split each segment into equal m-tiles (else BM rows and a short last tile)
-  int32_t w8;              // 1: expert weights are FP8 E4M3 codes with per-row scales (x and h bf16)
+  int32_t wq;              // expert weights: 0 bf16/fp32, 8 FP8 E4M3 codes, 4 packed int4 codes (both with
+                           // per-row scales; x and h bf16)
   float* split_ws;         // workspace for the K-parts of split tail tiles (bf16 path), or NULL
   long long split_cap;     // its size in floats (0: no split)
 };
@@ -98,6 +99,11 @@ int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream);
 // codes[r, c] = e4m3(w[r, c] / scales[r]), scales[r] = max_c |w[r, c]| / 448 (fp32).
 int launch_quantize_fp8(long long rows, int cols, const void* w_bf16, uint8_t* codes, float* scales,
                         hipStream_t stream);
+// ------------------------------------------------------------------ int4 weights
+// q[r, c] = clamp(rint(w[r, c] / scales[r]), -7, 7), scales[r] = max_c |w[r, c]| / 7 (fp32), packed as
+// the grouped GEMM reads it (quant_int4.hip states the layout).
+int launch_quantize_int4(long long rows, int cols, const void* w_bf16, uint8_t* packed, float* scales,
+                         hipStream_t stream);
 
 // ------------------------------------------------------------------ combine
 int launch_combine(const moe_shape& s, const float* expert_out, const int32_t* slot_pos,

@@ -80,14 +80,14 @@ class MoELayer:
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.out = Outputs.empty(s.n_tokens, s.d_model, s.n_experts, s.top_k, self.device)
 
-    fp8 = None  # after quantize_fp8(): codes and row scales of every expert weight
+    fp8 = None   # after quantize_fp8(): codes and row scales of every expert weight
+    int4 = None  # after quantize_int4(): packed codes and row scales of every expert weight
 
-    def quantize_fp8(self, keep_bf16: bool = False):
-        """Quantise every expert weight (routed and shared) to FP8 E4M3 codes with
-        per-row fp32 scales on the device (moe_quantize_fp8); forward then runs
-        moe_forward_fp8. The bf16 expert weights are dropped unless keep_bf16."""
+    def _quantize(self, kind: str, keep_bf16: bool):
         if self.shape.dtype != N.MOE_DTYPE_BF16:
-            raise ValueError("FP8 expert weights need a bf16 layer")
+            raise ValueError(f"{kind} expert weights need a bf16 layer")
+        if self.fp8 is not None or self.int4 is not None:
+            raise ValueError("the expert weights are already quantised")
         q = {}
         for name in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down"):
             w = getattr(self, name)
@@ -95,29 +95,47 @@ class MoELayer:
                 q[name] = q["sc_" + name] = None
                 continue
             rows, cols = w.numel() // w.shape[-1], w.shape[-1]
-            codes = torch.empty(w.shape, dtype=torch.uint8, device=self.device)
             scales = torch.empty(w.shape[:-1], dtype=torch.float32, device=self.device)
-            N.moe_quantize_fp8(rows, cols, w, codes, scales)
+            if kind == "fp8":
+                codes = torch.empty(w.shape, dtype=torch.uint8, device=self.device)
+                N.moe_quantize_fp8(rows, cols, w, codes, scales)
+            else:
+                codes = torch.empty(tuple(w.shape[:-1]) + (cols // 2,), dtype=torch.uint8, device=self.device)
+                N.moe_quantize_int4(rows, cols, w, codes, scales)
             q[name], q["sc_" + name] = codes, scales
             if not keep_bf16:
                 setattr(self, name, None)
-        self.fp8 = q
         return q
+
+    def quantize_fp8(self, keep_bf16: bool = False):
+        """Quantise every expert weight (routed and shared) to FP8 E4M3 codes with
+        per-row fp32 scales on the device (moe_quantize_fp8); forward then runs
+        moe_forward_fp8. The bf16 expert weights are dropped unless keep_bf16."""
+        self.fp8 = self._quantize("fp8", keep_bf16)
+        return self.fp8
+
+    def quantize_int4(self, keep_bf16: bool = False):
+        """Quantise every expert weight (routed and shared) to packed int4 codes with
+        per-row fp32 scales on the device (moe_quantize_int4); forward then runs
+        moe_forward_int4. The bf16 expert weights are dropped unless keep_bf16."""
+        self.int4 = self._quantize("int4", keep_bf16)
+        return self.int4
 
     def forward(self, x: torch.Tensor, stage_events=None, stream=None) -> Outputs:
         if x.shape[0] != self.shape.n_tokens:
             self.shape.n_tokens = x.shape[0]
             self._alloc()
         o = self.out
-        if self.fp8 is not None:
-            q = self.fp8
-            sc = N.fp8_scales(q["sc_w_gate"], q["sc_w_up"], q["sc_w_down"], q["sc_s_gate"],
-                              q["sc_s_up"], q["sc_s_down"])
-            N.moe_forward_fp8(self.shape, x, self.w_router, self.logit_bias, self.select_bias,
-                              q["w_gate"], q["w_up"], q["w_down"], q["s_gate"], q["s_up"],
-                              q["s_down"], sc, o.y, o.topk_idx, o.topk_w, o.counts, o.offsets,
-                              o.perm, o.slot_pos, o.prob_sum, o.balance_stat, self.ws,
-                              stage_events=stage_events, stream=stream)
+        if self.fp8 is not None or self.int4 is not None:
+            q = self.fp8 if self.fp8 is not None else self.int4
+            fwd = N.moe_forward_fp8 if self.fp8 is not None else N.moe_forward_int4
+            sc = N.weight_scales(q["sc_w_gate"], q["sc_w_up"], q["sc_w_down"], q["sc_s_gate"],
+                                 q["sc_s_up"], q["sc_s_down"])
+            fwd(self.shape, x, self.w_router, self.logit_bias, self.select_bias,
+                q["w_gate"], q["w_up"], q["w_down"], q["s_gate"], q["s_up"],
+                q["s_down"], sc, o.y, o.topk_idx, o.topk_w, o.counts, o.offsets,
+                o.perm, o.slot_pos, o.prob_sum, o.balance_stat, self.ws,
+                stage_events=stage_events, stream=stream)
             return o
         N.moe_forward(self.shape, x, self.w_router, self.logit_bias, self.select_bias, self.w_gate,
                       self.w_up, self.w_down, self.s_gate, self.s_up, self.s_down, o.y, o.topk_idx,

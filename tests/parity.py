@@ -60,8 +60,25 @@ class Fp8View(F64View):
         return w
 
 
-def oracle_views(layer: mi.Layer, cache_routed=False, fp8=False):
-    V = Fp8View if fp8 else F64View
+class Int4View(F64View):
+    """Like F64View, but each expert matrix is quantised to int4 by the oracle
+    (per-row scales) and dequantised: the weights the int4 layer computes with."""
+
+    def __getitem__(self, e):
+        e = int(e)
+        if self.cache is not None and e in self.cache:
+            return self.cache[e]
+        codes, scales = O.quantize_int4_rows(mi.bf16_bits_to_f32(self.arr[e]))
+        w = O.dequantize_int4_rows(codes, scales)
+        if self.cache is not None:
+            self.cache[e] = w
+        return w
+
+
+def oracle_views(layer: mi.Layer, cache_routed=False, fp8=False, quant=None):
+    """quant: None (the stored weights), "fp8" or "int4" (fp8=True means "fp8")."""
+    quant = "fp8" if fp8 else quant
+    V = {None: F64View, "fp8": Fp8View, "int4": Int4View}[quant]
     ws = tuple(V(a, cache=cache_routed) for a in (layer.w_gate, layer.w_up, layer.w_down))
     shared = None
     if layer.s_gate is not None:
@@ -74,9 +91,10 @@ def oracle_route(cfg: mi.MoEConfig, layer: mi.Layer, x: np.ndarray) -> O.Routing
                    layer.select_bias, cfg.renormalize)
 
 
-def oracle_y(cfg, layer, x, idx, rows, form, routing: O.Routing = None, fp8=False):
-    """Forced-routing oracle output on `rows` for the given idx (fp8: FP8 expert weights)."""
-    (wg, wu, wd), shared = oracle_views(layer, cache_routed=(form == "per_token"), fp8=fp8)
+def oracle_y(cfg, layer, x, idx, rows, form, routing: O.Routing = None, fp8=False, quant=None):
+    """Forced-routing oracle output on `rows` for the given idx (quant "fp8"/"int4": quantised
+    expert weights; fp8=True means "fp8")."""
+    (wg, wu, wd), shared = oracle_views(layer, cache_routed=(form == "per_token"), fp8=fp8, quant=quant)
     x64 = mi.to_f64(x)
     if routing is None:
         routing = oracle_route(cfg, layer, x)

@@ -136,6 +136,32 @@ def test_fp8_entry_points_validate():
     assert fw(s, ctypes.byref(sc)) == N.MOE_ERR_WORKSPACE  # 16 bytes: validation reaches the workspace check
 
 
+def test_int4_entry_points_validate():
+    L = moe.lib()
+    assert L.moe_quantize_int4(-1, 64, FAKE, FAKE, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_int4(4, 0, FAKE, FAKE, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_int4(4, 64, FAKE, None, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_int4(4, 96, FAKE, FAKE, FAKE, None) == N.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_int4(1 << 31, 64, FAKE, FAKE, FAKE, None) == N.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_int4(0, 64, None, None, None, None) == N.MOE_OK
+    s = shp()
+    args = (64, 256, FAKE, FAKE, 2, FAKE, 128, FAKE, FAKE, FAKE)
+    assert L.moe_grouped_swiglu_int4(ctypes.byref(s), *args, FAKE, None, FAKE, FAKE, FAKE, 1 << 30,
+                                     None) == N.MOE_ERR_INVALID_ARG
+    s32 = shp(dtype=N.MOE_DTYPE_F32)
+    assert L.moe_grouped_swiglu_int4(ctypes.byref(s32), *args, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                     None) == N.MOE_ERR_UNSUPPORTED
+    sc = N.MoEWeightScales(FAKE, FAKE, FAKE, None, None, None)
+    fw = lambda shape, scales: L.moe_forward_int4(
+        ctypes.byref(shape), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, None, None, scales,
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, None)
+    assert fw(s, None) == N.MOE_ERR_INVALID_ARG
+    assert fw(s, ctypes.byref(N.MoEWeightScales(FAKE, FAKE, None, None, None, None))) == N.MOE_ERR_INVALID_ARG
+    assert fw(shp(n_shared=1, d_ff_shared=128), ctypes.byref(sc)) == N.MOE_ERR_INVALID_ARG
+    assert fw(s32, ctypes.byref(sc)) == N.MOE_ERR_UNSUPPORTED
+    assert fw(s, ctypes.byref(sc)) == N.MOE_ERR_WORKSPACE
+
+
 def test_router_aux_entry_points_validate():
     L = moe.lib()
     s = shp()
