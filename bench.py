@@ -54,6 +54,8 @@ WORKLOADS = {
                     "bf16", "hbm"),
     "dsv3_decode_fp8": ("dsv3_decode", "DeepSeek-V3-shaped decode with FP8 (E4M3, per-row scale) expert weights: "
                         "N=64 d=7168 d_ff=2048 E=256 k=8 +1 shared, bf16 activations", "fp8", "hbm"),
+    "dsv3_decode_int4": ("dsv3_decode", "DeepSeek-V3-shaped decode with int4 (per-row scale, W4A16) expert "
+                         "weights: N=64 d=7168 d_ff=2048 E=256 k=8 +1 shared, bf16 activations", "int4", "hbm"),
     "switch_cap": ("switch_cap", "Switch-style top-1 with capacity 160: N=16384 d=2048 d_ff=8192 E=128, bf16",
                    "bf16", "hbm"),
 }
@@ -69,7 +71,8 @@ def algorithmic_work(cfg, counts, kept, weights="bf16"):
       weights each), the shared experts, fp32 y, and idx/w (8 bytes per copy);
     * bytes_gate_up: what the gate|up kernel must move: x, the gate and up
       weights of the touched experts (and the shared ones), and bf16 h out.
-    FP8 expert weights count 1 byte per weight plus a 4-byte scale per row.
+    FP8 expert weights count 1 byte per weight plus a 4-byte scale per row,
+    int4 weights half a byte per weight plus the same scale.
     """
     import numpy as np
     d, F, E, N, k = cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.n_tokens, cfg.top_k
@@ -79,8 +82,8 @@ def algorithmic_work(cfg, counts, kept, weights="bf16"):
     touched = int(np.sum(np.asarray(kept) > 0))
     fl_gu = 2 * d * 2 * F * n_kept + S * N * 2 * d * 2 * Fs
     fl_dn = 2 * F * d * n_kept + S * N * 2 * Fs * d
-    bw = 1 if weights == "fp8" else b                         # bytes per expert weight
-    rs = 4 if weights == "fp8" else 0                         # bytes per weight row (its scale)
+    bw = {"fp8": 1, "int4": 0.5}.get(weights, b)              # bytes per expert weight
+    rs = 4 if weights in ("fp8", "int4") else 0               # bytes per weight row (its scale)
     w_bytes = (touched * (expert_params(d, F) * bw + (2 * F + d) * rs)
                + S * (expert_params(d, Fs) * bw + (2 * Fs + d) * rs))
     byts = N * d * b + E * d * b + w_bytes + N * d * 4 + N * k * 8
@@ -160,6 +163,8 @@ def cpu_baseline(cfg, layer, x, budget_s=20.0, weights="bf16"):
             def __getitem__(self, e):
                 if weights == "fp8":
                     return O.dequantize_fp8_rows(*O.quantize_fp8_rows(mi.bf16_bits_to_f32(self.a[e])))
+                if weights == "int4":
+                    return O.dequantize_int4_rows(*O.quantize_int4_rows(mi.bf16_bits_to_f32(self.a[e])))
                 return mi.to_f64(self.a[e])
 
             def __len__(self):
@@ -232,6 +237,8 @@ def main():
     L = MoELayer.from_numpy(moe.shape_for(cfg), layer, dev)
     if weights == "fp8":
         L.quantize_fp8()  # one-off conversion on the device, before any timing
+    elif weights == "int4":
+        L.quantize_int4()
     xd = to_device(x, dev)
     torch.cuda.synchronize()
 

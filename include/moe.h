@@ -279,7 +279,7 @@ int moe_forward_fp8(const moe_shape* shape, const void* x, const void* w_router,
  * matrix and symmetric codes q in [-7, 7]. The layer they compute is the
  * bf16 layer with every expert weight replaced by scale[row] * q. x, the
  * router and h stay bf16; the shape's dtype must be MOE_DTYPE_BF16 (else
- * MOE_ERR_UNSUPPORTED). These layers never split tail tiles along K.
+ * MOE_ERR_UNSUPPORTED).
  *
  * Packed format: a row of K codes is K/2 bytes, in blocks of 64 codes (32
  * bytes). In the block of codes [k0, k0 + 64), the little-endian 32-bit

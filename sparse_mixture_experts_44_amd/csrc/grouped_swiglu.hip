@@ -340,7 +340,8 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int G, long long cap_
 // (i, j). Phase 1 writes h = bf16(silu(g) * u), phase 2 writes fp32 O;
 // with quantised weights (WQ = 8: FP8, 4: int4) each column is first
 // multiplied by its weight row's scale, and with int4 weights the offset
-// sums corr[i] (136 * sum(x) of each row) are subtracted before that.
+// sums corr[i] (136 * sum(x) of each row) are subtracted before that (none
+// when corr is NULL: the K-parts of split tiles are stored already reduced).
 template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, int FM, int NB>
 __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetView& S, const TileGeom& t,
                                            int d, int lane, int wm, int wn, const f32x16_t* corr = nullptr) {
@@ -378,7 +379,7 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
         if (decltype(check)::value && r >= t.mvalid) continue;
         const size_t row = (size_t)(t.start + t.m0 + r);
         float c = 0.f;
-        if constexpr (W4) c = corr[i][v];
+        if constexpr (W4) c = corr ? corr[i][v] : 0.f;
         if constexpr (P1) {
           bf16_t* hrow = static_cast<bf16_t*>(S.h) + row * F + col0;
 #pragma unroll
@@ -656,13 +657,15 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     // ---- epilogue
     if (part >= 0) {
       // a K-part of a split tail tile: raw accumulators, thread-major, for the reduce kernel
+      // (int4: with this part's offset sum removed, so that the parts add up to sum(x * q))
       float* dst = p.split_ws + kSplitHeader + ((size_t)(T - sp.base) * sp.S + part) * (BM * BN);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) dst[((i * NB + j) * 16 + v) * NT + tid] = acc[i][j][v];
+          for (int v = 0; v < 16; ++v)
+            dst[((i * NB + j) * 16 + v) * NT + tid] = W4 ? acc[i][j][v] - corr[i][v] : acc[i][j][v];
       continue;
     }
     store_tile<BM, BN, WGM, WGN, WQ, P1>(acc, S, tg, d, lane, wm, wn, corr);
@@ -690,7 +693,6 @@ __global__ __launch_bounds__(256) void split_sum_kernel(float* __restrict__ ws) 
 // tail tile b. Workgroups past the tail exit.
 template <int BM, int BN, int WGM, int WGN, int WQ, bool P1>
 __global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedParams p, int main_grid) {
-  static_assert(WQ != 4, "int4 layers do not split");
   constexpr int TM = BM / WGM, FM = TM / 32;
   constexpr int BH = P1 ? BN / 2 : BN;
   constexpr int TN = BH / WGN, FN = TN / 32;
@@ -842,16 +844,14 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
   else
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
-  if constexpr (WQ != 4) {  // int4 launches get no split workspace
-    if (p.split_ws && p.split_cap > kSplitHeader) {
-      hipLaunchKernelGGL(split_sum_kernel<BM * BN>, dim3(1024), dim3(256), 0, st, p.split_ws);
-      if (phase == 1)
-        hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, true>), dim3(grid), dim3(WGM * WGN * 64),
-                           0, st, p, grid);
-      else
-        hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false>), dim3(grid), dim3(WGM * WGN * 64),
-                           0, st, p, grid);
-    }
+  if (p.split_ws && p.split_cap > kSplitHeader) {
+    hipLaunchKernelGGL(split_sum_kernel<BM * BN>, dim3(1024), dim3(256), 0, st, p.split_ws);
+    if (phase == 1)
+      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, true>), dim3(grid), dim3(WGM * WGN * 64),
+                         0, st, p, grid);
+    else
+      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false>), dim3(grid), dim3(WGM * WGN * 64),
+                         0, st, p, grid);
   }
 }
 
@@ -862,11 +862,8 @@ template <int WQ>
 void launch_class(const GroupedParams& p, int phase, hipStream_t stream) {
   if constexpr (WQ == 4) {
     // int4 weights (a decode format): 64 x 256 tiles, 16 KB stages, two
-    // workgroups per CU; no split tail tiles
-    GroupedParams q = p;
-    q.split_ws = nullptr;
-    q.split_cap = 0;
-    launch_mfma<64, 256, 64, 1, 4, 4, 4, false, 2>(q, phase, 2, stream);
+    // workgroups per CU (the split workspace is sized for that grid)
+    launch_mfma<64, 256, 64, 1, 4, 4, 4, false, 2>(p, phase, 2, stream);
   } else if (large_tiles(p.set[0].max_rows, p.set[0].n_groups)) {
     // persistent grid with even m-tiles: the workgroups that share a weight
     // tile run in step, so their copies of it hit in L2

@@ -109,11 +109,12 @@ def test_int4_small_layers_every_row(kw):
     check_int4(cfg, layer, x, gpu, np.arange(cfg.n_tokens))
 
 
+@pytest.mark.parametrize("extra_ws", [0, 64 << 20])   # with room past h, the tail tiles split along K
 @pytest.mark.parametrize("sizes", [
     [0, 1, 255, 256, 257, 0, 513, 2, 300],
     [0, 1, 63, 64, 65, 0, 3, 127, 0, 0],
 ])
-def test_int4_grouped_segment_edges(sizes):
+def test_int4_grouped_segment_edges(sizes, extra_ws):
     d, F, rpt = 128, 256, 3
     rng = np.random.default_rng(len(sizes) * 11 + d)
     G = len(sizes)
@@ -130,7 +131,7 @@ def test_int4_grouped_segment_edges(sizes):
         q[name] = torch.empty(tuple(w.shape[:-1]) + (w.shape[-1] // 2,), dtype=torch.uint8, device=DEV)
         q["sc_" + name] = torch.empty(w.shape[:-1], dtype=torch.float32, device=DEV)
         moe.moe_quantize_int4(w.numel() // w.shape[-1], w.shape[-1], w, q[name], q["sc_" + name])
-    ws = torch.empty(max(256, ((rows * F * 2 + 255) // 256) * 256), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(max(256, ((rows * F * 2 + 255) // 256) * 256) + extra_ws, dtype=torch.uint8, device=DEV)
     out = torch.full((rows, d), float("nan"), dtype=torch.float32, device=DEV)
     moe.moe_grouped_swiglu_int4(moe.shape_for(cfg), G, F, dv(x), dv(perm), rpt, dv(offs), rows,
                                 q["w_gate"], q["w_up"], q["w_down"], q["sc_w_gate"], q["sc_w_up"],
