@@ -176,3 +176,29 @@ def test_int4_scale_over_eight_is_caught(monkeypatch):
 def test_int4_natural_nibble_order_is_caught(monkeypatch):
     monkeypatch.setattr(O, "_INT4_NIBBLE", np.arange(8))
     _fails(pins.test_int4_packing_matches_worked_block_and_round_trips)
+
+
+# ---------------------------------------------------------------- backward oracle
+import test_oracle_backward as bpins
+from oracle import moe_backward as OB
+
+
+def test_backward_silu_grad_without_second_term_is_caught(monkeypatch):
+    monkeypatch.setattr(OB, "silu_grad", lambda z: OB.sigmoid(z))
+    _fails(lambda: bpins.test_backward_matches_finite_differences(True))
+
+
+def test_backward_renormalisation_without_projection_is_caught(monkeypatch):
+    monkeypatch.setattr(OB, "renorm_backward", lambda dw, w, ssum: dw / ssum)
+    _fails(lambda: bpins.test_backward_matches_finite_differences(True))
+
+
+def test_backward_softmax_without_centering_is_caught(monkeypatch):
+    monkeypatch.setattr(OB, "softmax_backward", lambda p, dp: p * dp)
+    _fails(lambda: bpins.test_backward_matches_finite_differences(False))
+
+
+def test_backward_dropped_copies_sending_gradient_is_caught(monkeypatch):
+    orig_group = OB._grouping
+    monkeypatch.setattr(OB, "_grouping", lambda idx, E, capacity=0: orig_group(idx, E, 0))
+    _fails(lambda: bpins.test_backward_matches_finite_differences(True))
