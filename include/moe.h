@@ -321,6 +321,47 @@ int moe_forward_int4(const moe_shape* shape, const void* x, const void* w_router
                      int32_t* perm, int32_t* slot_pos, double* prob_sum, double* balance_stat,
                      void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
 
+/* ---------------------------------------------------------------------
+ * Backward pass (training). The gradients of
+ *   L = sum_{t,c} dy[t, c] * y[t, c] + aux_coef * stat
+ * for the bf16 layer of moe_forward, with the forward's top-k selection and
+ * dropped set frozen (they are piecewise constant); stat is the balance
+ * statistic of "混合专家 MoE" (anrans ai-infra handbook), section "负载均衡",
+ * with the counts held constant. The layer differentiated is that of the
+ * same handbook, section "实现：逐 token 与按专家分组". Readings: the bf16
+ * rounding of h passes the gradient unchanged; a dropped copy (capacity, the
+ * notes "混合专家模型 (MoE)：大规模稀疏条件计算的架构与工程实践", section 三.1)
+ * sends no gradient into its expert and its combine weight gets none, but it
+ * stays in its token's renormalisation; the selection-only bias gets none.
+ * The product operands (dy, w * dy, h, and the SwiGLU input gradients) are
+ * rounded to bf16 for the matrix cores, with fp32 accumulation; every other
+ * step and every reduction is fp32 in a fixed order (deterministic).
+ * --------------------------------------------------------------------- */
+
+/* Workspace bytes of moe_backward for a shape (0 for an invalid shape). */
+size_t moe_backward_workspace_bytes(const moe_shape* shape);
+
+/* Inputs: the layer's bf16 weights as passed to moe_forward; the forward's
+ * outputs topk_idx [N, k], topk_w [N, k], counts [E], offsets [E+1], perm
+ * [N*k], slot_pos [N*k] (unchanged since that call); dy [N, d] fp32, read at
+ * bf16 precision (every use goes through its round-to-nearest-even bf16
+ * value, so bf16-valued dy loses nothing); aux_coef (finite; 0 drops the
+ * balance term).
+ * Outputs (fp32, every entry written): dx [N, d]; dw_router [E, d];
+ * d_logit_bias [E] (NULL: not computed); dw_gate, dw_up [E, F, d]; dw_down
+ * [E, d, F] (zero for an expert with no kept copy); ds_gate, ds_up [S, Fs, d]
+ * and ds_down [S, d, Fs] (may be NULL when S == 0).
+ * Errors: MOE_ERR_UNSUPPORTED unless the shape's dtype is MOE_DTYPE_BF16;
+ * MOE_ERR_INVALID_ARG for a missing pointer or a non-finite aux_coef;
+ * MOE_ERR_WORKSPACE when ws_bytes < moe_backward_workspace_bytes(shape). */
+int moe_backward(const moe_shape* shape, const void* x, const void* w_router, const float* logit_bias,
+                 const void* w_gate, const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
+                 const void* s_down, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
+                 const int32_t* offsets, const int32_t* perm, const int32_t* slot_pos, const float* dy,
+                 double aux_coef, float* dx, float* dw_router, float* d_logit_bias, float* dw_gate, float* dw_up,
+                 float* dw_down, float* ds_gate, float* ds_up, float* ds_down, void* ws, size_t ws_bytes,
+                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -77,10 +77,10 @@ def softmax_backward(p, dp):
 _grouping = O.group
 
 
-def expert_backward(X, dO, w_gate, w_up, w_down, round_h: bool):
-    """One SwiGLU expert over the rows X [M, d] with output gradient dO [M, d]:
-    h = silu(X Wg^T) * (X Wu^T) (bf16-rounded if round_h), O = h Wd^T.
-    Returns (dX [M, d], dWg [F, d], dWu [F, d], dWd [d, F])."""
+def expert_backward_terms(X, dO, w_gate, w_up, w_down, round_h: bool):
+    """The rows expert_backward's products are taken over, for one SwiGLU expert over the rows
+    X [M, d] with output gradient dO [M, d]: h = silu(X Wg^T) * (X Wu^T) (bf16-rounded if
+    round_h), O = h Wd^T. Returns (G, H, dH, dG, dU), each [M, F]."""
     X = np.asarray(X, dtype=F64)
     Wg, Wu, Wd = (np.asarray(a, dtype=F64) for a in (w_gate, w_up, w_down))
     G = X @ Wg.T
@@ -89,11 +89,18 @@ def expert_backward(X, dO, w_gate, w_up, w_down, round_h: bool):
     if round_h:
         H = O.bf16_round(H)
     dH = dO @ Wd                        # O = H Wd^T  ->  dH = dO Wd
-    dWd = dO.T @ H
     dG = dH * U * silu_grad(G)          # h = silu(G) * U
     dU = dH * O.silu(G)
-    dX = dG @ Wg + dU @ Wu
-    return dX, dG.T @ X, dU.T @ X, dWd
+    return G, H, dH, dG, dU
+
+
+def expert_backward(X, dO, w_gate, w_up, w_down, round_h: bool):
+    """Returns (dX [M, d], dWg [F, d], dWu [F, d], dWd [d, F]) for the expert of
+    expert_backward_terms."""
+    X = np.asarray(X, dtype=F64)
+    Wg, Wu = (np.asarray(a, dtype=F64) for a in (w_gate, w_up))
+    _, H, _, dG, dU = expert_backward_terms(X, dO, Wg, Wu, w_down, round_h)
+    return dG @ Wg + dU @ Wu, dG.T @ X, dU.T @ X, dO.T @ H
 
 
 def layer_backward(x, w_router, w_gate, w_up, w_down, idx, dy, *, shared=None, logit_bias=None,
@@ -174,3 +181,75 @@ def layer_loss(x, w_router, w_gate, w_up, w_down, idx, dy, *, shared=None, logit
     if aux_coef:
         L += aux_coef * O.balance_stat(O.expert_counts(idx, E), p.sum(axis=0), N, k)
     return L
+
+
+def layer_backward_sampled(x, w_router, w_gate, w_up, w_down, idx, dy, tokens, experts, *, shared=None,
+                           logit_bias=None, capacity: int = 0, renormalize: bool = True, round_h: bool = False,
+                           aux_coef: float = 0.0):
+    """Part of layer_backward's result, reading only the expert weights that part needs (for
+    layers whose weights do not fit in memory in fp64; w_gate etc. may be lazy per-expert views):
+
+    * dx[tokens] (each token's row is its own: its kept copies' expert rows, the shared
+      experts' rows and its router row);
+    * the weight gradients (dWg, dWu, dWd) of every expert in `experts` (from all its kept rows);
+    * every shared expert's weight gradients (None without shared experts).
+
+    Returns (dx_rows [len(tokens), d], {e: (dWg, dWu, dWd)}, (ds_gate, ds_up, ds_down) or None).
+    The steps are layer_backward's, applied to the rows and experts asked for."""
+    x = np.asarray(x, dtype=F64)
+    dy = np.asarray(dy, dtype=F64)
+    Wr = np.asarray(w_router, dtype=F64)
+    idx = np.asarray(idx, dtype=np.int64)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    N, k = idx.shape
+    E = Wr.shape[0]
+    p = O.softmax(O.router_logits(x, Wr, logit_bias))
+    sel = np.take_along_axis(p, idx, axis=1)
+    ssum = sel.sum(axis=1, keepdims=True)
+    w = sel / ssum if renormalize else sel
+    g = _grouping(idx, E, capacity)
+    kept = (g.slot_pos >= 0).reshape(N, k)
+
+    weights = {}
+    for e in experts:
+        copies = g.perm[g.offsets[e]:g.offsets[e + 1]]
+        if len(copies) == 0:
+            F, d = np.shape(w_gate[e])
+            weights[e] = (np.zeros((F, d)), np.zeros((F, d)), np.zeros((d, F)))
+            continue
+        t, j = copies // k, copies % k
+        weights[e] = expert_backward(x[t], w[t, j][:, None] * dy[t], w_gate[e], w_up[e], w_down[e], round_h)[1:]
+
+    # the sampled tokens' kept copies, grouped by expert
+    dx = np.zeros((len(tokens), x.shape[1]))
+    dw = np.zeros((len(tokens), k))
+    for e in np.unique(idx[tokens]):
+        ii, jj = np.nonzero((idx[tokens] == e) & kept[tokens])
+        if len(ii) == 0:
+            continue
+        t = tokens[ii]
+        Wg, Wu, Wd = (np.asarray(a[e], dtype=F64) for a in (w_gate, w_up, w_down))
+        He = O.silu(x[t] @ Wg.T) * (x[t] @ Wu.T)
+        if round_h:
+            He = O.bf16_round(He)
+        dw[ii, jj] = np.sum(dy[t] * (He @ Wd.T), axis=1)
+        dXe = expert_backward(x[t], w[t, jj][:, None] * dy[t], Wg, Wu, Wd, round_h)[0]
+        np.add.at(dx, ii, dXe)
+    ds = None
+    if shared is not None:
+        sg, su, sd = shared
+        ds = ([], [], [])
+        for s in range(len(sg)):
+            dXs, a, b, c = expert_backward(x, dy, sg[s], su[s], sd[s], round_h)
+            dx += dXs[tokens]
+            for lst, v in zip(ds, (a, b, c)):
+                lst.append(v)
+        ds = tuple(np.stack(v) for v in ds)
+    dsel = renorm_backward(dw, w[tokens], ssum[tokens]) if renormalize else dw
+    dp = np.zeros((len(tokens), E))
+    np.put_along_axis(dp, idx[tokens], dsel, axis=1)
+    if aux_coef:
+        f = O.expert_counts(idx, E) / (N * k)
+        dp += aux_coef * E * f[None, :] / N
+    dx += softmax_backward(p[tokens], dp) @ Wr
+    return dx, weights, ds

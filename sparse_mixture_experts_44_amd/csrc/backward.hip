@@ -1,0 +1,388 @@
+// Backward pass of the MoE layer: the element-wise, gather, transpose and
+// router kernels around the grouped GEMMs (which grouped_swiglu.hip runs).
+//
+// The function differentiated is the forward layer of "混合专家 MoE" (anrans
+// ai-infra handbook), section "实现：逐 token 与按专家分组", with the top-k
+// selection and the dropped set of the forward frozen, and the scalar
+//   L = sum(dy * y) + aux_coef * E * sum_e f_e P_e
+// (the balance statistic of section "负载均衡", counts held constant). For one
+// expert over its rows X (SwiGLU, h = silu(G) * U, G = X Wg^T, U = X Wu^T,
+// O = h Wd^T, output scaled by the combine weight w):
+//   dH' = dy Wd            (per row, before the weight)
+//   dw  = sum_f h * dH'    (the combine weight's gradient: dy . O)
+//   dH  = w dH';  dG = dH * U * silu'(G);  dU = dH * silu(G)
+//   dX  = dG Wg + dU Wu;   dWd = (w dy)^T h;  dWg = dG^T X;  dWu = dU^T X
+// and for the router, per token: the renormalisation w_j = p_j / sum_i p_i,
+// the balance term's dp[e] += aux_coef * E * f_e / N, and the softmax
+// dl = p * (dp - sum(dp * p)); then dW_r = dl^T x, d(logit bias) = sum_t dl,
+// dx += dl W_r. The rounding of h to bf16 passes the gradient unchanged.
+//
+// Rounding points (bf16 operands of the MFMA GEMMs, fp32 accumulation): dy,
+// w * dy, h, dG and dU are rounded to bf16 where they feed a GEMM; the
+// element-wise steps and every reduction here run in fp32, in a fixed order.
+#include <math.h>
+
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kT = 256;
+
+__device__ __forceinline__ float bf(bf16_t b) { return bf16_to_f32(b); }
+
+// Rows of the kept copies in grouped order: Xg[r] = x[t], dYg[r] = bf16(dy[t]),
+// dO[r] = bf16(w[t, j] * dYg[r]), for copy c = perm[r] = t * k + j.
+// Shared experts (perm == nullptr): row r is token r, w = 1 (dO is not written).
+// Rows at or past *n_valid (when given) are not kept copies and are skipped.
+__global__ __launch_bounds__(kT) void gather_rows_kernel(const bf16_t* __restrict__ x, const float* __restrict__ dy,
+                                                         const float* __restrict__ topk_w,
+                                                         const int32_t* __restrict__ perm,
+                                                         const int32_t* __restrict__ n_valid, int k, int d,
+                                                         bf16_t* __restrict__ Xg, bf16_t* __restrict__ dYg,
+                                                         bf16_t* __restrict__ dO) {
+  const int r = blockIdx.x;
+  if (n_valid && r >= *n_valid) return;
+  const int c = perm ? perm[r] : r;
+  const int t = perm ? c / k : r;
+  const float w = perm ? topk_w[c] : 1.f;
+  for (int i = threadIdx.x; i < d; i += kT) {
+    const bf16_t yb = f32_to_bf16(dy[(size_t)t * d + i]);
+    if (Xg) Xg[(size_t)r * d + i] = x[(size_t)t * d + i];
+    dYg[(size_t)r * d + i] = yb;
+    if (dO) dO[(size_t)r * d + i] = f32_to_bf16(w * bf(yb));
+  }
+}
+
+// out[g][b][a] = in[g][a][b] for G matrices of A x B bf16 (64 x 64 tiles through LDS).
+// dst_stride: row length of the output (>= A) and dst_off its first column, so
+// that two transposed matrices can share output rows side by side.
+__global__ __launch_bounds__(kT) void transpose_kernel(const bf16_t* __restrict__ in, int A, int B,
+                                                       bf16_t* __restrict__ out, int dst_stride, int dst_off) {
+  __shared__ bf16_t tile[64][65];
+  const int g = blockIdx.z;
+  const int a0 = blockIdx.y * 64, b0 = blockIdx.x * 64;
+  const bf16_t* src = in + (size_t)g * A * B;
+  bf16_t* dst = out + (size_t)g * B * dst_stride;
+  for (int i = threadIdx.x; i < 64 * 64; i += kT) {
+    const int a = a0 + i / 64, b = b0 + i % 64;
+    if (a < A && b < B) tile[i / 64][i % 64] = src[(size_t)a * B + b];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += kT) {
+    const int b = b0 + i / 64, a = a0 + i % 64;
+    if (a < A && b < B) dst[(size_t)b * dst_stride + dst_off + a] = tile[i % 64][i / 64];
+  }
+}
+
+// One row per workgroup: from G, U (fp32 [rows, F]), dH' = dy Wd (fp32) and the
+// row's combine weight w: h = bf16(silu(G) U) (written when h != nullptr),
+// dw = sum_f h dH' (fixed tree order; written to dw[perm[r]] when dw != nullptr),
+// dGU[r] = [bf16(w dH' U silu'(G)) | bf16(w dH' silu(G))].
+__global__ __launch_bounds__(kT) void swiglu_backward_kernel(const float* __restrict__ G, const float* __restrict__ U,
+                                                             const float* __restrict__ dHp, const float* __restrict__ topk_w,
+                                                             const int32_t* __restrict__ perm,
+                                                             const int32_t* __restrict__ n_valid, int F,
+                                                             bf16_t* __restrict__ h, bf16_t* __restrict__ dGU,
+                                                             float* __restrict__ dw) {
+  __shared__ float s_part[kT];
+  const int r = blockIdx.x;
+  if (n_valid && r >= *n_valid) return;  // whole workgroup, before any barrier
+  const float w = perm ? topk_w[perm[r]] : 1.f;
+  const size_t o = (size_t)r * F;
+  float acc = 0.f;
+  for (int f = threadIdx.x; f < F; f += kT) {
+    const float g = G[o + f], u = U[o + f], dp = dHp[o + f];
+    const float s = 1.f / (1.f + expf(-g));
+    const float silu = g * s;
+    const bf16_t hb = f32_to_bf16(silu * u);
+    if (h) h[o + f] = hb;
+    acc += bf(hb) * dp;
+    const float dh = w * dp;
+    dGU[(size_t)r * 2 * F + f] = f32_to_bf16(dh * u * s * (1.f + g * (1.f - s)));
+    dGU[(size_t)r * 2 * F + F + f] = f32_to_bf16(dh * silu);
+  }
+  s_part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = kT / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st) s_part[threadIdx.x] += s_part[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (dw && threadIdx.x == 0) dw[perm[r]] = s_part[0];
+}
+
+// kofs[g] = start of group g's K range in the padded transposed layout: the
+// groups' row counts, each rounded up to a multiple of 64, summed in order.
+// offsets == nullptr: every group has `uniform` rows.
+__global__ void k_offsets_kernel(const int32_t* __restrict__ offsets, int G, int uniform, int32_t* __restrict__ kofs) {
+  if (threadIdx.x != 0) return;
+  int run = 0;
+  for (int g = 0; g < G; ++g) {
+    kofs[g] = run;
+    const int rows = offsets ? offsets[g + 1] - offsets[g] : uniform;
+    run += (rows + 63) / 64 * 64;
+  }
+  kofs[G] = run;
+}
+
+// Transposes grouped rows into the padded layout the weight-gradient GEMMs read:
+// out[c][kofs[g] + i] = in[row_g(i)][col_off + c] for i < rows_g, and 0 on the
+// pad columns up to kofs[g + 1]; row_g(i) = offsets[g] + i (or g * uniform + i,
+// or, with replicate, i: every group reads rows [0, uniform)). Columns past
+// kofs[G] are left untouched. One 64 x 64 tile per workgroup.
+__global__ __launch_bounds__(kT) void transpose_padded_kernel(const bf16_t* __restrict__ in, int in_stride, int col_off,
+                                                              int C, const int32_t* __restrict__ offsets, int uniform,
+                                                              int replicate, const int32_t* __restrict__ kofs, int G,
+                                                              bf16_t* __restrict__ out, int kmax) {
+  __shared__ bf16_t tile[64][65];
+  __shared__ int s_g;
+  const int c0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
+  if (threadIdx.x == 0) {
+    int g = -1;
+    if (k0 < kofs[G]) {
+      int lo = 0, hi = G;  // kofs[lo] <= k0 < kofs[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (kofs[mid] <= k0) lo = mid;
+        else hi = mid;
+      }
+      g = lo;
+    }
+    s_g = g;
+  }
+  __syncthreads();
+  const int g = s_g;
+  if (g < 0) return;  // whole workgroup
+  const int rows = offsets ? offsets[g + 1] - offsets[g] : uniform;
+  const int first = replicate ? 0 : (offsets ? offsets[g] : g * uniform);
+  const int i0 = k0 - kofs[g];  // row index within the group of column k0
+  for (int q = threadIdx.x; q < 64 * 64; q += kT) {
+    const int i = i0 + q / 64, c = c0 + q % 64;
+    bf16_t v = 0;
+    if (i < rows && c < C) v = in[(size_t)(first + i) * in_stride + col_off + c];
+    tile[q / 64][q % 64] = v;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 64 * 64; q += kT) {
+    const int c = c0 + q / 64, kk = k0 + q % 64;
+    if (c < C && kk < kmax) out[(size_t)c * kmax + kk] = tile[q % 64][q / 64];
+  }
+}
+
+// Router backward, one wave per token: p = softmax(l + logit_bias) from the
+// summed logit splits; w_j = topk_w (the forward's combine weights), sum_i p_i
+// over the selected; dsel_j = (dw_j - sum_i dw_i w_i) / sum_i p_i (renormalised)
+// or dw_j; dp[e] = dsel at the selected experts + aux_coef * E * f_e / N;
+// dl = p * (dp - sum(dp * p)).
+template <int EL>
+__global__ __launch_bounds__(kT) void router_backward_kernel(const float* __restrict__ part, int splits,
+                                                             const float* __restrict__ logit_bias,
+                                                             const int32_t* __restrict__ topk_idx,
+                                                             const float* __restrict__ topk_w,
+                                                             const float* __restrict__ dw,
+                                                             const int32_t* __restrict__ counts, float aux_scale,
+                                                             int N, int E, int k, int renorm,
+                                                             float* __restrict__ dl) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kT / kWave) + (threadIdx.x >> 6);
+  if (t >= N) return;  // whole wave
+  const size_t split_stride = (size_t)N * E;
+  float l[EL], pe[EL];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < EL; ++m) {
+    const int e = lane + kWave * m;
+    float v = -INFINITY;
+    if (e < E) {
+      v = 0.f;
+      for (int q = 0; q < splits; ++q) v += part[(size_t)q * split_stride + (size_t)t * E + e];
+      if (logit_bias) v += logit_bias[e];
+    }
+    l[m] = v;
+    mx = fmaxf(mx, v);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  float sum = 0.f;
+#pragma unroll
+  for (int m = 0; m < EL; ++m) {
+    pe[m] = (lane + kWave * m < E) ? expf(l[m] - mx) : 0.f;
+    sum += pe[m];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+#pragma unroll
+  for (int m = 0; m < EL; ++m) pe[m] /= sum;
+  // the selected experts' p (each lane looks its own experts up), sum_i p_i and sum_i dw_i w_i
+  float ssum = 0.f, dww = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[(size_t)t * k + j];
+    float pj = 0.f;
+#pragma unroll
+    for (int m = 0; m < EL; ++m)
+      if (lane + kWave * m == e) pj = pe[m];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) pj += __shfl_xor(pj, o, kWave);
+    ssum += pj;
+    dww += dw[(size_t)t * k + j] * topk_w[(size_t)t * k + j];
+  }
+  float dp[EL];
+#pragma unroll
+  for (int m = 0; m < EL; ++m) {
+    const int e = lane + kWave * m;
+    dp[m] = (e < E && counts) ? aux_scale * (float)counts[e] : 0.f;
+  }
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[(size_t)t * k + j];
+    const float dwj = dw[(size_t)t * k + j];
+    const float ds = renorm ? (dwj - dww) / ssum : dwj;
+#pragma unroll
+    for (int m = 0; m < EL; ++m)
+      if (lane + kWave * m == e) dp[m] += ds;
+  }
+  float dot = 0.f;
+#pragma unroll
+  for (int m = 0; m < EL; ++m) dot += dp[m] * pe[m];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o, kWave);
+#pragma unroll
+  for (int m = 0; m < EL; ++m) {
+    const int e = lane + kWave * m;
+    if (e < E) dl[(size_t)t * E + e] = pe[m] * (dp[m] - dot);
+  }
+}
+
+// dW_r[e][c] = sum_t dl[t][e] x[t][c] (t in order), 16 experts per thread;
+// d_logit_bias[e] = sum_t dl[t][e] (when requested, by the c == 0 threads).
+constexpr int kEB = 16;
+__global__ __launch_bounds__(kT) void router_wgrad_kernel(const float* __restrict__ dl, const bf16_t* __restrict__ x,
+                                                          int N, int E, int d, float* __restrict__ dwr,
+                                                          float* __restrict__ dlb) {
+  const int c = blockIdx.x * kT + threadIdx.x;
+  const int e0 = blockIdx.y * kEB;
+  if (c >= d) return;
+  float acc[kEB], bsum[kEB];
+#pragma unroll
+  for (int q = 0; q < kEB; ++q) acc[q] = bsum[q] = 0.f;
+  for (int t = 0; t < N; ++t) {
+    const float xv = bf(x[(size_t)t * d + c]);
+#pragma unroll
+    for (int q = 0; q < kEB; ++q) {
+      const float g = (e0 + q < E) ? dl[(size_t)t * E + e0 + q] : 0.f;
+      acc[q] += g * xv;
+      bsum[q] += g;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kEB; ++q) {
+    if (e0 + q >= E) break;
+    dwr[(size_t)(e0 + q) * d + c] = acc[q];
+    if (dlb && c == 0) dlb[e0 + q] = bsum[q];
+  }
+}
+
+// dx[t][c] = sum_j dXr[slot_pos[t*k + j]][c] (kept copies, j in order)
+//          + sum_s dXs[s*N + t][c] + sum_e dl[t][e] W_r[e][c] (e in order).
+__global__ __launch_bounds__(kT) void dx_kernel(const float* __restrict__ dXr, const int32_t* __restrict__ slot_pos,
+                                                const float* __restrict__ dXs, int S, const float* __restrict__ dl,
+                                                const bf16_t* __restrict__ wr, int N, int E, int k, int d,
+                                                float* __restrict__ dx) {
+  const int t = blockIdx.y;
+  const int c = blockIdx.x * kT + threadIdx.x;
+  if (c >= d) return;
+  float acc = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int r = slot_pos[(size_t)t * k + j];
+    if (r >= 0) acc += dXr[(size_t)r * d + c];
+  }
+  for (int s = 0; s < S; ++s) acc += dXs[((size_t)s * N + t) * d + c];
+  float rr = 0.f;
+  for (int e = 0; e < E; ++e) rr += dl[(size_t)t * E + e] * bf(wr[(size_t)e * d + c]);
+  dx[(size_t)t * d + c] = acc + rr;
+}
+
+__global__ void fill_f32_kernel(float* p, size_t n, float v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+}  // namespace
+
+int launch_gather_rows(const void* x, const float* dy, const float* topk_w, const int32_t* perm,
+                       const int32_t* n_valid, int k, int d, int rows, void* Xg, void* dYg, void* dO, hipStream_t st) {
+  if (rows <= 0) return MOE_OK;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(rows), dim3(kT), 0, st, static_cast<const bf16_t*>(x), dy, topk_w,
+                     perm, n_valid, k, d, static_cast<bf16_t*>(Xg), static_cast<bf16_t*>(dYg),
+                     static_cast<bf16_t*>(dO));
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_transpose(const void* in, int G, int A, int B, void* out, int dst_stride, int dst_off, hipStream_t st) {
+  if (G <= 0 || A <= 0 || B <= 0) return MOE_OK;
+  hipLaunchKernelGGL(transpose_kernel, dim3((B + 63) / 64, (A + 63) / 64, G), dim3(kT), 0, st,
+                     static_cast<const bf16_t*>(in), A, B, static_cast<bf16_t*>(out), dst_stride, dst_off);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_swiglu_backward(const float* G, const float* U, const float* dHp, const float* topk_w,
+                           const int32_t* perm, const int32_t* n_valid, int rows, int F, void* h, void* dGU,
+                           float* dw, hipStream_t st) {
+  if (rows <= 0) return MOE_OK;
+  hipLaunchKernelGGL(swiglu_backward_kernel, dim3(rows), dim3(kT), 0, st, G, U, dHp, topk_w, perm, n_valid, F,
+                     static_cast<bf16_t*>(h), static_cast<bf16_t*>(dGU), dw);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_k_offsets(const int32_t* offsets, int G, int uniform, int32_t* kofs, hipStream_t st) {
+  hipLaunchKernelGGL(k_offsets_kernel, dim3(1), dim3(kWave), 0, st, offsets, G, uniform, kofs);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_transpose_padded(const void* in, int in_stride, int col_off, int C, const int32_t* offsets, int uniform,
+                            int replicate, const int32_t* kofs, int G, void* out, int kmax, hipStream_t st) {
+  if (C <= 0 || kmax <= 0) return MOE_OK;
+  hipLaunchKernelGGL(transpose_padded_kernel, dim3(kmax / 64, (C + 63) / 64), dim3(kT), 0, st,
+                     static_cast<const bf16_t*>(in), in_stride, col_off, C, offsets, uniform, replicate, kofs, G,
+                     static_cast<bf16_t*>(out), kmax);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_router_backward(const moe_shape& s, const float* logits, int splits, const float* logit_bias,
+                           const int32_t* topk_idx, const float* topk_w, const float* dw, const int32_t* counts,
+                           double aux_coef, float* dl, hipStream_t st) {
+  const int N = s.n_tokens, E = s.n_experts, k = s.top_k;
+  // aux_coef * E * f_e / N with f_e = counts_e / (N k)
+  const float aux_scale = (float)(aux_coef * E / ((double)N * k * N));
+  const int el = (E + kWave - 1) / kWave;
+  const dim3 grid((N + kT / kWave - 1) / (kT / kWave));
+#define MOE_RB(EL_)                                                                                          \
+  hipLaunchKernelGGL(router_backward_kernel<EL_>, grid, dim3(kT), 0, st, logits, splits, logit_bias, topk_idx, \
+                     topk_w, dw, aux_coef != 0.0 ? counts : nullptr, aux_scale, N, E, k, s.renormalize, dl)
+  if (el <= 1) MOE_RB(1);
+  else if (el <= 2) MOE_RB(2);
+  else if (el <= 4) MOE_RB(4);
+  else MOE_RB(8);
+#undef MOE_RB
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_router_wgrad(const float* dl, const void* x, int N, int E, int d, float* dwr, float* dlb, hipStream_t st) {
+  hipLaunchKernelGGL(router_wgrad_kernel, dim3((d + kT - 1) / kT, (E + kEB - 1) / kEB), dim3(kT), 0, st, dl,
+                     static_cast<const bf16_t*>(x), N, E, d, dwr, dlb);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_dx(const float* dXr, const int32_t* slot_pos, const float* dXs, int S, const float* dl, const void* wr,
+              int N, int E, int k, int d, float* dx, hipStream_t st) {
+  if (N <= 0) return MOE_OK;
+  hipLaunchKernelGGL(dx_kernel, dim3((d + kT - 1) / kT, N), dim3(kT), 0, st, dXr, slot_pos, dXs, S, dl,
+                     static_cast<const bf16_t*>(wr), N, E, k, d, dx);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_fill_f32(float* p, size_t n, float v, hipStream_t st) {
+  if (n == 0) return MOE_OK;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(1024), dim3(kT), 0, st, p, n, v);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe

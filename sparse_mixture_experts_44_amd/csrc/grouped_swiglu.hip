@@ -53,6 +53,7 @@ struct SetView {  // the fields of one SegSet, picked with selects rather than a
   const float* sd;
   void* h;
   float* out;
+  const int32_t* kofs;  // weight-gradient mode (phase 2): per-group K ranges
 };
 
 __device__ __forceinline__ SetView pick(const GroupedParams& p, int si) {
@@ -68,6 +69,7 @@ __device__ __forceinline__ SetView pick(const GroupedParams& p, int si) {
   v.sd = si ? p.set[1].sc_down : p.set[0].sc_down;
   v.h = si ? p.set[1].h : p.set[0].h;
   v.out = si ? p.set[1].out : p.set[0].out;
+  v.kofs = si ? p.set[1].k_offsets : p.set[0].k_offsets;
   return v;
 }
 
@@ -484,7 +486,16 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     const SetView S = pick(p, si);
     const int start = tg.start, m0 = tg.m0, mvalid = tg.mvalid, n0 = tg.n0;
     const int F = S.d_ff;
-    const int K = P1 ? d : F;
+    // K values per row of A (phase 2) and of the weight rows; a weight-gradient
+    // set takes its group's K range [kbase, kbase + K) of matrices shared by all groups
+    const int kstride = P1 ? d : F;
+    int K = kstride, kbase = 0;
+    if constexpr (!P1) {
+      if (S.kofs) {
+        kbase = S.kofs[g];
+        K = S.kofs[g + 1] - kbase;
+      }
+    }
     const int nk_all = K / BK;
     // this unit's K steps: all of them, or part `part` of sp.S
     const int k_lo = part < 0 ? 0 : (int)((long long)part * nk_all / sp.S);
@@ -506,7 +517,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
         src = (unsigned)tok < (unsigned)p.n_tokens ? (uint32_t)tok : 0u;
         src *= (uint32_t)d;
       } else {
-        src = (uint32_t)row * (uint32_t)F;
+        src = (uint32_t)(S.kofs ? row - start : row) * (uint32_t)F + (uint32_t)kbase;
       }
       a_off[i] = src + ((cpcA ^ swz<PPA>(r)) << 3);
     }
@@ -518,14 +529,15 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
       const bool up = wave * B_INS * RPIB >= BN / 2;
       b_base = static_cast<const BT*>(up ? S.wu : S.wg) + (size_t)g * F * d / KDIV;
     } else {
-      b_base = static_cast<const BT*>(S.wd) + (size_t)g * d * F / KDIV;
+      b_base = static_cast<const BT*>(S.wd) + (S.kofs ? 0 : (size_t)g * d * F / KDIV);
     }
     uint32_t b_off[B_INS];
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
       const int r = (wave * B_INS + i) * RPIB + crowB;    // tile row
       const int mr = P1 ? (r % (BN / 2)) : r;              // row within its weight matrix tile
-      b_off[i] = (uint32_t)(n0 + min(mr, lastq)) * (uint32_t)(K / KDIV) + (uint32_t)((cpcB ^ swz<PPB>(r)) * EPP);
+      b_off[i] = (uint32_t)(n0 + min(mr, lastq)) * (uint32_t)(kstride / KDIV) + (uint32_t)(kbase / KDIV) +
+                 (uint32_t)((cpcB ^ swz<PPB>(r)) * EPP);
     }
     const uint32_t a_lds0 = lds_addr(&s_tile[0][(wave * A_INS) * 1024]);
     const uint32_t b_lds0 = lds_addr(&s_tile[0][STAGE_A + (wave * B_INS) * 1024]);

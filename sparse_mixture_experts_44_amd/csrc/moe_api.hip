@@ -4,6 +4,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <cmath>
+#include <utility>
 
 #include "moe_common.h"
 
@@ -138,6 +140,95 @@ int grouped_impl(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const v
   int st = launch_grouped(p, 1, stream);
   if (st != MOE_OK) return st;
   return launch_grouped(p, 2, stream);
+}
+
+// ------------------------------------------------------------------ backward
+// Workspace of moe_backward (byte offsets, 256-aligned). R = N*k rows (the
+// kept copies occupy the first offsets[E]), Kmax = R rounded up to 64 plus 64
+// per expert (each expert's rows padded to 64 in the transposed layout).
+struct BwLayout {
+  size_t logits, dl, dw, kofs, kofs_s, Xg, dYg, dO, G, U, dHp, h, dGU, dXr, WdT, WguT, dOT, hT, dGT, dUT, XT, split;
+  size_t Xs, dYs, Gs, Us, dHs, hs, dGUs, dXs, SdT, SguT, dOsT, hsT, dGsT, dUsT, XsT, total;
+  long long R, Kmax, Npad, KSmax;
+};
+
+BwLayout bw_layout(const moe_shape& s) {
+  BwLayout L{};
+  const long long N = s.n_tokens, k = s.top_k, E = s.n_experts, d = s.d_model, F = s.d_ff;
+  const long long S = s.n_shared, Fs = S ? s.d_ff_shared : 0;
+  L.R = N * k;
+  L.Kmax = (L.R + 63) / 64 * 64 + 64 * E;
+  L.Npad = (N + 63) / 64 * 64;
+  L.KSmax = S * L.Npad;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+  L.logits = take(route_logits_floats(s) * 4);
+  L.dl = take(N * E * 4);
+  L.dw = take(N * k * 4);
+  L.kofs = take((E + 1) * 4);
+  L.kofs_s = take((S + 1) * 4);
+  L.Xg = take(L.R * d * 2);
+  L.dYg = take(L.R * d * 2);
+  L.dO = take(L.R * d * 2);
+  L.G = take(L.R * F * 4);
+  L.U = take(L.R * F * 4);
+  L.dHp = take(L.R * F * 4);
+  L.h = take(L.R * F * 2);
+  L.dGU = take(L.R * 2 * F * 2);
+  L.dXr = take(L.R * d * 4);
+  L.WdT = take(E * F * d * 2);
+  L.WguT = take(E * d * 2 * F * 2);
+  L.dOT = take(d * L.Kmax * 2);
+  L.hT = take(F * L.Kmax * 2);
+  L.dGT = take(F * L.Kmax * 2);
+  L.dUT = take(F * L.Kmax * 2);
+  L.XT = take(d * L.Kmax * 2);
+  L.split = take(std::max(grouped_split_bytes(L.R, (int)E), grouped_split_bytes(E * std::max(d, F), (int)E)));
+  L.Xs = take(S * N * d * 2);
+  L.dYs = take(S * N * d * 2);
+  L.Gs = take(S * N * Fs * 4);
+  L.Us = take(S * N * Fs * 4);
+  L.dHs = take(S * N * Fs * 4);
+  L.hs = take(S * N * Fs * 2);
+  L.dGUs = take(S * N * 2 * Fs * 2);
+  L.dXs = take(S * N * d * 4);
+  L.SdT = take(S * Fs * d * 2);
+  L.SguT = take(S * d * 2 * Fs * 2);
+  L.dOsT = take(d * L.KSmax * 2);
+  L.hsT = take(Fs * L.KSmax * 2);
+  L.dGsT = take(Fs * L.KSmax * 2);
+  L.dUsT = take(Fs * L.KSmax * 2);
+  L.XsT = take(d * L.KSmax * 2);
+  L.total = off;
+  return L;
+}
+
+// One plain grouped product out[r, n] = sum_k A[r, k] B_g[n, k] over groups of rows
+// (offsets, or `uniform` rows per group), or, with kofs, the weight-gradient form
+// out[g*M + m, n] = sum over group g's K range of A[m, k] B[n, k].
+int grouped_gemm(int n_groups, const int32_t* offsets, int uniform, long long max_rows, int K_or_stride, int ncols,
+                 const void* A, const void* B, float* out, const int32_t* kofs, float* split_ws, size_t split_bytes,
+                 hipStream_t st) {
+  GroupedParams p{};
+  p.n_sets = 1;
+  p.x = A;
+  p.n_tokens = 1;
+  p.d_model = ncols;
+  p.dtype = MOE_DTYPE_BF16;
+  p.split_ws = split_ws;
+  p.split_cap = split_ws ? (long long)(split_bytes / sizeof(float)) : 0;
+  SegSet& S = p.set[0];
+  S.offsets = offsets;
+  S.n_groups = n_groups;
+  S.uniform_rows = uniform;
+  S.rows_per_token = 1;
+  S.max_rows = (int32_t)max_rows;
+  S.d_ff = K_or_stride;
+  S.w_gate = S.w_up = S.w_down = B;
+  S.h = const_cast<void*>(A);
+  S.out = out;
+  S.k_offsets = kofs;
+  return launch_grouped(p, 2, st);
 }
 
 }  // namespace
@@ -423,6 +514,116 @@ int moe_update_select_bias(const moe_shape* shape, const int32_t* counts, float 
   if (st != MOE_OK) return st;
   if (!counts || !select_bias || !(gamma >= 0.0f) || gamma == INFINITY) return MOE_ERR_INVALID_ARG;
   return launch_bias_update(*shape, counts, gamma, select_bias, stream);
+}
+
+size_t moe_backward_workspace_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return std::max<size_t>(bw_layout(*shape).total, 256);
+}
+
+int moe_backward(const moe_shape* shape, const void* x, const void* w_router, const float* logit_bias,
+                 const void* w_gate, const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
+                 const void* s_down, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
+                 const int32_t* offsets, const int32_t* perm, const int32_t* slot_pos, const float* dy,
+                 double aux_coef, float* dx, float* dw_router, float* d_logit_bias, float* dw_gate, float* dw_up,
+                 float* dw_down, float* ds_gate, float* ds_up, float* ds_down, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!std::isfinite(aux_coef)) return MOE_ERR_INVALID_ARG;
+  if (!dw_router || !dw_gate || !dw_up || !dw_down || !w_gate || !w_up || !w_down || !w_router || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (s.n_shared > 0 && (!s_gate || !s_up || !s_down || !ds_gate || !ds_up || !ds_down)) return MOE_ERR_INVALID_ARG;
+  if (s.n_tokens > 0 && (!x || !topk_idx || !topk_w || !counts || !offsets || !perm || !slot_pos || !dy || !dx))
+    return MOE_ERR_INVALID_ARG;
+  const BwLayout L = bw_layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const int N = s.n_tokens, k = s.top_k, E = s.n_experts, d = s.d_model, F = s.d_ff;
+  const int S = s.n_shared, Fs = S ? s.d_ff_shared : 0;
+  if (N == 0) {  // no tokens: every gradient is 0
+    for (auto pr : {std::make_pair(dw_router, (size_t)E * d), std::make_pair(dw_gate, (size_t)E * F * d),
+                    std::make_pair(dw_up, (size_t)E * F * d), std::make_pair(dw_down, (size_t)E * d * F),
+                    std::make_pair(d_logit_bias, (size_t)E), std::make_pair(ds_gate, (size_t)S * Fs * d),
+                    std::make_pair(ds_up, (size_t)S * Fs * d), std::make_pair(ds_down, (size_t)S * d * Fs)})
+      if (pr.first && (st = launch_fill_f32(pr.first, pr.second, 0.f, stream))) return st;
+    return MOE_OK;
+  }
+  auto P = [&](size_t o) { return static_cast<void*>(at(ws, o)); };
+  auto Pf = [&](size_t o) { return reinterpret_cast<float*>(at(ws, o)); };
+  auto Pi = [&](size_t o) { return reinterpret_cast<int32_t*>(at(ws, o)); };
+  float* split = Pf(L.split);
+  const size_t split_bytes = L.Xs - L.split;
+  const int R = (int)L.R, Kmax = (int)L.Kmax;
+  const int32_t* n_kept = offsets + E;
+#define MOE_TRY(call) \
+  if ((st = (call)) != MOE_OK) return st
+  // ---- routed experts
+  MOE_TRY(launch_fill_f32(Pf(L.dw), (size_t)N * k, 0.f, stream));  // dropped copies keep 0
+  MOE_TRY(launch_gather_rows(x, dy, topk_w, perm, n_kept, k, d, R, P(L.Xg), P(L.dYg), P(L.dO), stream));
+  MOE_TRY(launch_transpose(w_down, E, d, F, P(L.WdT), d, 0, stream));          // [E, F, d]
+  MOE_TRY(launch_transpose(w_gate, E, F, d, P(L.WguT), 2 * F, 0, stream));     // [E, d, 2F]: Wg^T | Wu^T
+  MOE_TRY(launch_transpose(w_up, E, F, d, P(L.WguT), 2 * F, F, stream));
+  MOE_TRY(grouped_gemm(E, offsets, 0, R, d, F, P(L.Xg), w_gate, Pf(L.G), nullptr, split, split_bytes, stream));
+  MOE_TRY(grouped_gemm(E, offsets, 0, R, d, F, P(L.Xg), w_up, Pf(L.U), nullptr, split, split_bytes, stream));
+  MOE_TRY(grouped_gemm(E, offsets, 0, R, d, F, P(L.dYg), P(L.WdT), Pf(L.dHp), nullptr, split, split_bytes, stream));
+  MOE_TRY(launch_swiglu_backward(Pf(L.G), Pf(L.U), Pf(L.dHp), topk_w, perm, n_kept, R, F, P(L.h), P(L.dGU),
+                                 Pf(L.dw), stream));
+  MOE_TRY(grouped_gemm(E, offsets, 0, R, 2 * F, d, P(L.dGU), P(L.WguT), Pf(L.dXr), nullptr, split, split_bytes,
+                       stream));
+  MOE_TRY(launch_k_offsets(offsets, E, 0, Pi(L.kofs), stream));
+  MOE_TRY(launch_transpose_padded(P(L.dO), d, 0, d, offsets, 0, 0, Pi(L.kofs), E, P(L.dOT), Kmax, stream));
+  MOE_TRY(launch_transpose_padded(P(L.h), F, 0, F, offsets, 0, 0, Pi(L.kofs), E, P(L.hT), Kmax, stream));
+  MOE_TRY(launch_transpose_padded(P(L.dGU), 2 * F, 0, F, offsets, 0, 0, Pi(L.kofs), E, P(L.dGT), Kmax, stream));
+  MOE_TRY(launch_transpose_padded(P(L.dGU), 2 * F, F, F, offsets, 0, 0, Pi(L.kofs), E, P(L.dUT), Kmax, stream));
+  MOE_TRY(launch_transpose_padded(P(L.Xg), d, 0, d, offsets, 0, 0, Pi(L.kofs), E, P(L.XT), Kmax, stream));
+  MOE_TRY(grouped_gemm(E, nullptr, d, (long long)E * d, Kmax, F, P(L.dOT), P(L.hT), dw_down, Pi(L.kofs), split,
+                       split_bytes, stream));
+  MOE_TRY(grouped_gemm(E, nullptr, F, (long long)E * F, Kmax, d, P(L.dGT), P(L.XT), dw_gate, Pi(L.kofs), split,
+                       split_bytes, stream));
+  MOE_TRY(grouped_gemm(E, nullptr, F, (long long)E * F, Kmax, d, P(L.dUT), P(L.XT), dw_up, Pi(L.kofs), split,
+                       split_bytes, stream));
+  // ---- shared experts: every token, weight 1
+  if (S > 0) {
+    const int RS = S * N, KS = (int)L.KSmax;
+    for (int q = 0; q < S; ++q)
+      MOE_TRY(launch_gather_rows(x, dy, nullptr, nullptr, nullptr, 1, d, N,
+                                 static_cast<uint8_t*>(P(L.Xs)) + (size_t)q * N * d * 2,
+                                 static_cast<uint8_t*>(P(L.dYs)) + (size_t)q * N * d * 2, nullptr, stream));
+    MOE_TRY(launch_transpose(s_down, S, d, Fs, P(L.SdT), d, 0, stream));
+    MOE_TRY(launch_transpose(s_gate, S, Fs, d, P(L.SguT), 2 * Fs, 0, stream));
+    MOE_TRY(launch_transpose(s_up, S, Fs, d, P(L.SguT), 2 * Fs, Fs, stream));
+    MOE_TRY(grouped_gemm(S, nullptr, N, RS, d, Fs, P(L.Xs), s_gate, Pf(L.Gs), nullptr, split, split_bytes, stream));
+    MOE_TRY(grouped_gemm(S, nullptr, N, RS, d, Fs, P(L.Xs), s_up, Pf(L.Us), nullptr, split, split_bytes, stream));
+    MOE_TRY(grouped_gemm(S, nullptr, N, RS, d, Fs, P(L.dYs), P(L.SdT), Pf(L.dHs), nullptr, split, split_bytes,
+                         stream));
+    MOE_TRY(launch_swiglu_backward(Pf(L.Gs), Pf(L.Us), Pf(L.dHs), nullptr, nullptr, nullptr, RS, Fs, P(L.hs),
+                                   P(L.dGUs), nullptr, stream));
+    MOE_TRY(grouped_gemm(S, nullptr, N, RS, 2 * Fs, d, P(L.dGUs), P(L.SguT), Pf(L.dXs), nullptr, split,
+                         split_bytes, stream));
+    MOE_TRY(launch_k_offsets(nullptr, S, N, Pi(L.kofs_s), stream));
+    MOE_TRY(launch_transpose_padded(P(L.dYs), d, 0, d, nullptr, N, 0, Pi(L.kofs_s), S, P(L.dOsT), KS, stream));
+    MOE_TRY(launch_transpose_padded(P(L.hs), Fs, 0, Fs, nullptr, N, 0, Pi(L.kofs_s), S, P(L.hsT), KS, stream));
+    MOE_TRY(launch_transpose_padded(P(L.dGUs), 2 * Fs, 0, Fs, nullptr, N, 0, Pi(L.kofs_s), S, P(L.dGsT), KS, stream));
+    MOE_TRY(launch_transpose_padded(P(L.dGUs), 2 * Fs, Fs, Fs, nullptr, N, 0, Pi(L.kofs_s), S, P(L.dUsT), KS, stream));
+    MOE_TRY(launch_transpose_padded(P(L.Xs), d, 0, d, nullptr, N, 0, Pi(L.kofs_s), S, P(L.XsT), KS, stream));
+    MOE_TRY(grouped_gemm(S, nullptr, d, (long long)S * d, KS, Fs, P(L.dOsT), P(L.hsT), ds_down, Pi(L.kofs_s), split,
+                         split_bytes, stream));
+    MOE_TRY(grouped_gemm(S, nullptr, Fs, (long long)S * Fs, KS, d, P(L.dGsT), P(L.XsT), ds_gate, Pi(L.kofs_s), split,
+                         split_bytes, stream));
+    MOE_TRY(grouped_gemm(S, nullptr, Fs, (long long)S * Fs, KS, d, P(L.dUsT), P(L.XsT), ds_up, Pi(L.kofs_s), split,
+                         split_bytes, stream));
+  }
+  // ---- router and dx
+  int splits = 1;
+  MOE_TRY(launch_router_logits(s, x, w_router, Pf(L.logits), &splits, stream));
+  MOE_TRY(launch_router_backward(s, Pf(L.logits), splits, logit_bias, topk_idx, topk_w, Pf(L.dw), counts, aux_coef,
+                                 Pf(L.dl), stream));
+  MOE_TRY(launch_router_wgrad(Pf(L.dl), x, N, E, d, dw_router, d_logit_bias, stream));
+  MOE_TRY(launch_dx(Pf(L.dXr), slot_pos, S > 0 ? Pf(L.dXs) : nullptr, S, Pf(L.dl), w_router, N, E, k, d, dx, stream));
+#undef MOE_TRY
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -47,6 +47,9 @@ int launch_router_aux(const moe_shape& s, const void* x, const void* w_router, c
 int launch_bias_update(const moe_shape& s, const int32_t* counts, float gamma, float* bias,
                        hipStream_t stream);
 size_t route_logits_floats(const moe_shape& s);
+// The router logits' K-split partial sums ([splits, N, E] floats; their sum in split order is x W_r^T).
+int launch_router_logits(const moe_shape& s, const void* x, const void* w_router, float* logits, int* splits,
+                         hipStream_t stream);
 
 // ------------------------------------------------------------------ permute
 int permute_chunks(const moe_shape& s);
@@ -72,6 +75,11 @@ struct SegSet {
   const float* sc_down;    // [G, d]
   void* h;                 // [max_rows, d_ff]: gate|up output, down input
   float* out;              // [max_rows, d]
+  // Weight-gradient mode (phase 2 only, bf16): when set, group g multiplies
+  // h and w_down over the K range [k_offsets[g], k_offsets[g+1]) (multiples
+  // of 64; empty: zero output); both are single matrices shared by all
+  // groups, with rows d_ff values apart: out[g*M + m, n] = sum_k h[m, k] * w_down[n, k].
+  const int32_t* k_offsets;
 };
 
 struct GroupedParams {
@@ -104,6 +112,24 @@ int launch_quantize_fp8(long long rows, int cols, const void* w_bf16, uint8_t* c
 // the grouped GEMM reads it (quant_int4.hip states the layout).
 int launch_quantize_int4(long long rows, int cols, const void* w_bf16, uint8_t* packed, float* scales,
                          hipStream_t stream);
+
+// ------------------------------------------------------------------ backward (backward.hip)
+int launch_gather_rows(const void* x, const float* dy, const float* topk_w, const int32_t* perm,
+                       const int32_t* n_valid, int k, int d, int rows, void* Xg, void* dYg, void* dO, hipStream_t st);
+int launch_transpose(const void* in, int G, int A, int B, void* out, int dst_stride, int dst_off, hipStream_t st);
+int launch_swiglu_backward(const float* G, const float* U, const float* dHp, const float* topk_w,
+                           const int32_t* perm, const int32_t* n_valid, int rows, int F, void* h, void* dGU,
+                           float* dw, hipStream_t st);
+int launch_k_offsets(const int32_t* offsets, int G, int uniform, int32_t* kofs, hipStream_t st);
+int launch_transpose_padded(const void* in, int in_stride, int col_off, int C, const int32_t* offsets, int uniform,
+                            int replicate, const int32_t* kofs, int G, void* out, int kmax, hipStream_t st);
+int launch_router_backward(const moe_shape& s, const float* logits, int splits, const float* logit_bias,
+                           const int32_t* topk_idx, const float* topk_w, const float* dw, const int32_t* counts,
+                           double aux_coef, float* dl, hipStream_t st);
+int launch_router_wgrad(const float* dl, const void* x, int N, int E, int d, float* dwr, float* dlb, hipStream_t st);
+int launch_dx(const float* dXr, const int32_t* slot_pos, const float* dXs, int S, const float* dl, const void* wr,
+              int N, int E, int k, int d, float* dx, hipStream_t st);
+int launch_fill_f32(float* p, size_t n, float v, hipStream_t st);
 
 // ------------------------------------------------------------------ combine
 int launch_combine(const moe_shape& s, const float* expert_out, const int32_t* slot_pos,

@@ -528,6 +528,15 @@ int launch_route(const moe_shape& s, const void* x, const void* w_router, const 
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+int launch_router_logits(const moe_shape& s, const void* x, const void* w_router, float* logits, int* splits,
+                         hipStream_t stream) {
+  const LogitsPlan L = plan_logits(s);
+  if (s.dtype == MOE_DTYPE_BF16) launch_logits<true>(s, L, x, w_router, logits, stream);
+  else launch_logits<false>(s, L, x, w_router, logits, stream);
+  *splits = L.splits;
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 int launch_router_aux(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                       const int32_t* topk_idx, const float* topk_w, double* z_loss, double* imp,
                       double* imp_cv2, double* partials, float* logits, hipStream_t stream) {

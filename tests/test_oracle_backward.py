@@ -147,3 +147,24 @@ def test_capacity_one_uses_only_the_kept_row():
         np.testing.assert_allclose(g.dw_gate[e], dWg, rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(g.dw_up[e], dWu, rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(g.dw_down[e], dWd, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("renormalize,S", [(True, 1), (False, 0)])
+def test_sampled_backward_equals_full(renormalize, S):
+    """The sampled form returns the same rows and experts as the full backward."""
+    rng = np.random.default_rng(65 + S)
+    x, wr, wg, wu, wd, shared, lb, dy, idx = small_layer(rng, N=11, d=8, F=6, E=5, k=2, S=S, Fs=4)
+    kw = dict(shared=shared, logit_bias=lb, capacity=3, renormalize=renormalize, round_h=True, aux_coef=0.4)
+    full = B.layer_backward(x, wr, wg, wu, wd, idx, dy, **kw)
+    tokens = [10, 0, 4, 7]
+    experts = list(range(5))
+    dx, weights, ds = B.layer_backward_sampled(x, wr, wg, wu, wd, idx, dy, tokens, experts, **kw)
+    np.testing.assert_allclose(dx, full.dx[tokens], rtol=1e-12, atol=1e-14)
+    for e in experts:
+        for got, ref in zip(weights[e], (full.dw_gate[e], full.dw_up[e], full.dw_down[e])):
+            np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+    if S:
+        for got, ref in zip(ds, (full.ds_gate, full.ds_up, full.ds_down)):
+            np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+    else:
+        assert ds is None
