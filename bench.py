@@ -93,6 +93,50 @@ def algorithmic_work(cfg, counts, kept, weights="bf16"):
                 bytes_gate_up=by_gu, touched=touched, kept=n_kept)
 
 
+def backward_work(cfg, kept):
+    """FLOPs of the backward pass from the real routing (moe_backward).
+
+    * algorithmic: what the backward must compute given the forward's
+      activations: per kept copy dH' = dy Wd (2 d F), dX = [dG|dU] [Wg;Wu]
+      (4 d F), dWd (2 d F), dWg and dWu (4 d F): 12 d F; the same per token per
+      shared expert; the router: dW_r and dl W_r (4 N E d);
+    * executed: moe_backward also recomputes G and U (4 d F per copy) and the
+      router logits (2 N E d) instead of keeping them from the forward pass.
+    """
+    import numpy as np
+    d, F, E, N = cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.n_tokens
+    S, Fs = cfg.n_shared, cfg.d_ff_shared
+    n_kept = int(np.sum(kept))
+    alg = 12 * d * F * n_kept + S * N * 12 * d * Fs + 4 * N * E * d
+    exe = alg + 4 * d * F * n_kept + S * N * 4 * d * Fs + 2 * N * E * d
+    return dict(flops_algorithmic=alg, flops_executed=exe)
+
+
+def time_backward(L, xd, cfg, steps, warmup, kept):
+    """K moe_backward calls on the last forward's routing, bracketed by HIP events on the stream
+    they run on; dy is a seeded bf16-valued N(0, 1) tensor, aux_coef 0.01."""
+    import torch
+    g = torch.Generator(device=xd.device).manual_seed(1234)
+    dy = torch.randn(cfg.n_tokens, cfg.d_model, generator=g, device=xd.device).bfloat16().float()
+    for _ in range(warmup):
+        L.backward(xd, dy, 0.01)
+    ev = HipEvents(2)
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    ev.record(0, stream)
+    for _ in range(steps):
+        L.backward(xd, dy, 0.01)
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(0, 1) / steps
+    w = backward_work(cfg, kept)
+    tf = w["flops_algorithmic"] / (ms * 1e-3) / 1e12
+    return {"ms": ms, "steps": steps, "tflops_algorithmic": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
+            "tflops_executed": w["flops_executed"] / (ms * 1e-3) / 1e12, **w,
+            "note": "moe_backward alone (gradients of x, W_r, logit bias, every expert weight); "
+                    "algorithmic FLOPs exclude the G, U and logit recompute"}
+
+
 class HipEvents:
     """hipEvent_t handles from the HIP runtime torch has loaded."""
 
@@ -105,6 +149,11 @@ class HipEvents:
             if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
                 raise RuntimeError("hipEventCreate failed")
             self.ev.append(h.value)
+
+    def record(self, i, stream):
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        if self.hip.hipEventRecord(self.ev[i], stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -202,6 +251,9 @@ def main():
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="extra untimed-region reps, each after a 1 GiB write that evicts L2 and the "
                          "Infinity Cache; reported as layer.cold (median/min/max)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time moe_backward on the last forward's routing (bf16 workloads); reported "
+                         "as backward, outside the headline value")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -323,6 +375,8 @@ def main():
                   "touched_experts": work["touched"], "kept_copies": work["kept"],
                   "balance_stat": float(L.out.balance_stat.item()), "cold": cold},
     }
+    if args.backward and weights == "bf16":
+        out["backward"] = time_backward(L, xd, cfg, K, args.warmup, kept)
     if not args.no_cpu_baseline:
         del L, xd
         torch.cuda.empty_cache()

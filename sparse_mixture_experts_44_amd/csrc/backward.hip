@@ -22,6 +22,8 @@
 // element-wise steps and every reduction here run in fp32, in a fixed order.
 #include <math.h>
 
+#include <algorithm>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -35,6 +37,7 @@ __device__ __forceinline__ float bf(bf16_t b) { return bf16_to_f32(b); }
 // dO[r] = bf16(w[t, j] * dYg[r]), for copy c = perm[r] = t * k + j.
 // Shared experts (perm == nullptr): row r is token r, w = 1 (dO is not written).
 // Rows at or past *n_valid (when given) are not kept copies and are skipped.
+// Eight columns (16 bytes of bf16) per thread; d is a multiple of 8.
 __global__ __launch_bounds__(kT) void gather_rows_kernel(const bf16_t* __restrict__ x, const float* __restrict__ dy,
                                                          const float* __restrict__ topk_w,
                                                          const int32_t* __restrict__ perm,
@@ -46,32 +49,69 @@ __global__ __launch_bounds__(kT) void gather_rows_kernel(const bf16_t* __restric
   const int c = perm ? perm[r] : r;
   const int t = perm ? c / k : r;
   const float w = perm ? topk_w[c] : 1.f;
-  for (int i = threadIdx.x; i < d; i += kT) {
-    const bf16_t yb = f32_to_bf16(dy[(size_t)t * d + i]);
-    if (Xg) Xg[(size_t)r * d + i] = x[(size_t)t * d + i];
-    dYg[(size_t)r * d + i] = yb;
-    if (dO) dO[(size_t)r * d + i] = f32_to_bf16(w * bf(yb));
+  const int d8 = d / 8;
+  const u32x4_t* xs = reinterpret_cast<const u32x4_t*>(x + (size_t)t * d);
+  const float4* ys = reinterpret_cast<const float4*>(dy + (size_t)t * d);
+  u32x4_t* xo = reinterpret_cast<u32x4_t*>(Xg + (size_t)r * d);
+  u32x4_t* yo = reinterpret_cast<u32x4_t*>(dYg + (size_t)r * d);
+  u32x4_t* oo = reinterpret_cast<u32x4_t*>(dO + (size_t)r * d);
+  for (int i = threadIdx.x; i < d8; i += kT) {
+    if (Xg) xo[i] = xs[i];
+    const float4 a = ys[2 * i], b = ys[2 * i + 1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    u32x4_t yb, ob;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16_t y0 = f32_to_bf16(v[2 * q]), y1 = f32_to_bf16(v[2 * q + 1]);
+      yb[q] = (uint32_t)y0 | ((uint32_t)y1 << 16);
+      ob[q] = (uint32_t)f32_to_bf16(w * bf(y0)) | ((uint32_t)f32_to_bf16(w * bf(y1)) << 16);
+    }
+    yo[i] = yb;
+    if (dO) oo[i] = ob;
   }
 }
 
-// out[g][b][a] = in[g][a][b] for G matrices of A x B bf16 (64 x 64 tiles through LDS).
-// dst_stride: row length of the output (>= A) and dst_off its first column, so
-// that two transposed matrices can share output rows side by side.
+// A 64 x 64 bf16 tile in LDS: rows of 66 halves (33 words), so that the
+// column reads of the transposed store hit at most two lanes per bank.
+constexpr int kTP = 66;
+
+// Packs the 8 column entries tile[a0 .. a0+7][b] into 16 bytes.
+__device__ __forceinline__ u32x4_t tile_column8(const uint16_t (*tile)[kTP], int a0, int b) {
+  u32x4_t v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = (uint32_t)tile[a0 + 2 * q][b] | ((uint32_t)tile[a0 + 2 * q + 1][b] << 16);
+  return v;
+}
+
+// Stores 16 bytes (8 halves) into row a of the tile at column b0 (b0 a multiple of 8).
+__device__ __forceinline__ void tile_row8(uint16_t (*tile)[kTP], int a, int b0, u32x4_t v) {
+  uint32_t* p = reinterpret_cast<uint32_t*>(&tile[a][b0]);  // 4-byte aligned: 66 a + b0 is even
+#pragma unroll
+  for (int q = 0; q < 4; ++q) p[q] = v[q];
+}
+
+// out[g][b][a] = in[g][a][b] for G matrices of A x B bf16 (A, B multiples of 64), one
+// 64 x 64 tile per workgroup through LDS, 16-byte loads and stores. dst_stride: row
+// length of the output (>= A, a multiple of 8) and dst_off (a multiple of 8) its first
+// column, so that two transposed matrices can share output rows side by side.
 __global__ __launch_bounds__(kT) void transpose_kernel(const bf16_t* __restrict__ in, int A, int B,
                                                        bf16_t* __restrict__ out, int dst_stride, int dst_off) {
-  __shared__ bf16_t tile[64][65];
+  __shared__ uint16_t tile[64][kTP];
   const int g = blockIdx.z;
   const int a0 = blockIdx.y * 64, b0 = blockIdx.x * 64;
   const bf16_t* src = in + (size_t)g * A * B;
   bf16_t* dst = out + (size_t)g * B * dst_stride;
-  for (int i = threadIdx.x; i < 64 * 64; i += kT) {
-    const int a = a0 + i / 64, b = b0 + i % 64;
-    if (a < A && b < B) tile[i / 64][i % 64] = src[(size_t)a * B + b];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = threadIdx.x + it * kT, a = q >> 3, ch = q & 7;
+    tile_row8(tile, a, ch * 8, *reinterpret_cast<const u32x4_t*>(src + (size_t)(a0 + a) * B + b0 + ch * 8));
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += kT) {
-    const int b = b0 + i / 64, a = a0 + i % 64;
-    if (a < A && b < B) dst[(size_t)b * dst_stride + dst_off + a] = tile[i % 64][i / 64];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = threadIdx.x + it * kT, b = q >> 3, ch = q & 7;
+    *reinterpret_cast<u32x4_t*>(dst + (size_t)(b0 + b) * dst_stride + dst_off + a0 + ch * 8) =
+        tile_column8(tile, ch * 8, b);
   }
 }
 
@@ -129,12 +169,13 @@ __global__ void k_offsets_kernel(const int32_t* __restrict__ offsets, int G, int
 // out[c][kofs[g] + i] = in[row_g(i)][col_off + c] for i < rows_g, and 0 on the
 // pad columns up to kofs[g + 1]; row_g(i) = offsets[g] + i (or g * uniform + i,
 // or, with replicate, i: every group reads rows [0, uniform)). Columns past
-// kofs[G] are left untouched. One 64 x 64 tile per workgroup.
+// kofs[G] are left untouched. One 64 x 64 tile per workgroup, 16-byte loads and
+// stores (in_stride, col_off and C multiples of 8).
 __global__ __launch_bounds__(kT) void transpose_padded_kernel(const bf16_t* __restrict__ in, int in_stride, int col_off,
                                                               int C, const int32_t* __restrict__ offsets, int uniform,
                                                               int replicate, const int32_t* __restrict__ kofs, int G,
                                                               bf16_t* __restrict__ out, int kmax) {
-  __shared__ bf16_t tile[64][65];
+  __shared__ uint16_t tile[64][kTP];
   __shared__ int s_g;
   const int c0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
   if (threadIdx.x == 0) {
@@ -156,16 +197,20 @@ __global__ __launch_bounds__(kT) void transpose_padded_kernel(const bf16_t* __re
   const int rows = offsets ? offsets[g + 1] - offsets[g] : uniform;
   const int first = replicate ? 0 : (offsets ? offsets[g] : g * uniform);
   const int i0 = k0 - kofs[g];  // row index within the group of column k0
-  for (int q = threadIdx.x; q < 64 * 64; q += kT) {
-    const int i = i0 + q / 64, c = c0 + q % 64;
-    bf16_t v = 0;
-    if (i < rows && c < C) v = in[(size_t)(first + i) * in_stride + col_off + c];
-    tile[q / 64][q % 64] = v;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = threadIdx.x + it * kT, i = q >> 3, ch = q & 7;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (i0 + i < rows && c0 + ch * 8 < C)
+      v = *reinterpret_cast<const u32x4_t*>(in + (size_t)(first + i0 + i) * in_stride + col_off + c0 + ch * 8);
+    tile_row8(tile, i, ch * 8, v);
   }
   __syncthreads();
-  for (int q = threadIdx.x; q < 64 * 64; q += kT) {
-    const int c = c0 + q / 64, kk = k0 + q % 64;
-    if (c < C && kk < kmax) out[(size_t)c * kmax + kk] = tile[q % 64][q / 64];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = threadIdx.x + it * kT, c = q >> 3, ch = q & 7;
+    if (c0 + c < C)
+      *reinterpret_cast<u32x4_t*>(out + (size_t)(c0 + c) * kmax + k0 + ch * 8) = tile_column8(tile, ch * 8, c);
   }
 }
 
@@ -252,53 +297,132 @@ __global__ __launch_bounds__(kT) void router_backward_kernel(const float* __rest
   }
 }
 
-// dW_r[e][c] = sum_t dl[t][e] x[t][c] (t in order), 16 experts per thread;
-// d_logit_bias[e] = sum_t dl[t][e] (when requested, by the c == 0 threads).
-constexpr int kEB = 16;
-__global__ __launch_bounds__(kT) void router_wgrad_kernel(const float* __restrict__ dl, const bf16_t* __restrict__ x,
-                                                          int N, int E, int d, float* __restrict__ dwr,
-                                                          float* __restrict__ dlb) {
+// Router weight gradient, first pass: part[z][e][c] = sum over the tokens t of
+// chunk z (in order) of dl[t][e] x[t][c]. A workgroup takes EB experts and kT
+// columns (one per thread, EB fp32 accumulators) over one chunk, staging 64
+// tokens of dl at a time in LDS (read back as broadcasts).
+constexpr int kRT = 64;  // tokens per LDS stage
+template <int EB>
+__global__ __launch_bounds__(kT) void router_wgrad_part_kernel(const float* __restrict__ dl,
+                                                               const bf16_t* __restrict__ x, int N, int E, int d,
+                                                               int chunk, float* __restrict__ part) {
+  __shared__ __align__(16) float s_dl[kRT][EB];
   const int c = blockIdx.x * kT + threadIdx.x;
-  const int e0 = blockIdx.y * kEB;
-  if (c >= d) return;
-  float acc[kEB], bsum[kEB];
+  const int e0 = blockIdx.y * EB;
+  const int t0 = blockIdx.z * chunk, t1 = min(N, t0 + chunk);
+  float acc[EB];
 #pragma unroll
-  for (int q = 0; q < kEB; ++q) acc[q] = bsum[q] = 0.f;
-  for (int t = 0; t < N; ++t) {
-    const float xv = bf(x[(size_t)t * d + c]);
-#pragma unroll
-    for (int q = 0; q < kEB; ++q) {
-      const float g = (e0 + q < E) ? dl[(size_t)t * E + e0 + q] : 0.f;
-      acc[q] += g * xv;
-      bsum[q] += g;
+  for (int q = 0; q < EB; ++q) acc[q] = 0.f;
+  for (int tb = t0; tb < t1; tb += kRT) {
+    const int nt = min(kRT, t1 - tb);
+    for (int i = threadIdx.x; i < kRT * EB; i += kT) {
+      const int tt = i / EB, ee = i % EB;
+      s_dl[tt][ee] = (tt < nt && e0 + ee < E) ? dl[(size_t)(tb + tt) * E + e0 + ee] : 0.f;
     }
-  }
+    __syncthreads();
+    if (c < d) {
+      for (int tt = 0; tt < nt; ++tt) {
+        const float xv = bf(x[(size_t)(tb + tt) * d + c]);
 #pragma unroll
-  for (int q = 0; q < kEB; ++q) {
-    if (e0 + q >= E) break;
-    dwr[(size_t)(e0 + q) * d + c] = acc[q];
-    if (dlb && c == 0) dlb[e0 + q] = bsum[q];
+        for (int q = 0; q < EB; q += 4) {
+          const float4 g = *reinterpret_cast<const float4*>(&s_dl[tt][q]);
+          acc[q] += g.x * xv;
+          acc[q + 1] += g.y * xv;
+          acc[q + 2] += g.z * xv;
+          acc[q + 3] += g.w * xv;
+        }
+      }
+    }
+    __syncthreads();
   }
+  if (c >= d) return;
+#pragma unroll
+  for (int q = 0; q < EB; ++q)
+    if (e0 + q < E) part[((size_t)blockIdx.z * E + e0 + q) * d + c] = acc[q];
 }
 
-// dx[t][c] = sum_j dXr[slot_pos[t*k + j]][c] (kept copies, j in order)
-//          + sum_s dXs[s*N + t][c] + sum_e dl[t][e] W_r[e][c] (e in order).
+// Second pass: dW_r[e][c] = sum_z part[z][e][c], z in order.
+__global__ __launch_bounds__(kT) void router_wgrad_reduce_kernel(const float* __restrict__ part, int Z, size_t n,
+                                                                 float* __restrict__ dwr) {
+  const size_t i = (size_t)blockIdx.x * kT + threadIdx.x;
+  if (i >= n) return;
+  float acc = 0.f;
+  for (int z = 0; z < Z; ++z) acc += part[(size_t)z * n + i];
+  dwr[i] = acc;
+}
+
+// d_logit_bias[e] = sum_t dl[t][e]: one workgroup per expert, a strided sum per
+// thread and a fixed tree over the threads.
+__global__ __launch_bounds__(kT) void logit_bias_grad_kernel(const float* __restrict__ dl, int N, int E,
+                                                             float* __restrict__ dlb) {
+  __shared__ float s_part[kT];
+  const int e = blockIdx.x;
+  float acc = 0.f;
+  for (int t = threadIdx.x; t < N; t += kT) acc += dl[(size_t)t * E + e];
+  s_part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = kT / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st) s_part[threadIdx.x] += s_part[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dlb[e] = s_part[0];
+}
+
+// dx[t][c] = (sum_j dXr[slot_pos[t*k + j]][c] over the kept copies, j in order,
+//             + sum_s dXs[s*N + t][c]) + sum_e dl[t][e] W_r[e][c] (e in order).
+// A workgroup takes 64 tokens and kT columns (one per thread, 64 fp32 router
+// accumulators); dl is staged 64 experts at a time in LDS, transposed, and read
+// back as broadcasts.
+constexpr int kXT = 64;   // tokens per workgroup
+constexpr int kXE = 64;   // experts per LDS stage
+constexpr int kXP = kXT + 4;  // LDS row pitch (floats): 16-byte aligned rows
 __global__ __launch_bounds__(kT) void dx_kernel(const float* __restrict__ dXr, const int32_t* __restrict__ slot_pos,
                                                 const float* __restrict__ dXs, int S, const float* __restrict__ dl,
                                                 const bf16_t* __restrict__ wr, int N, int E, int k, int d,
                                                 float* __restrict__ dx) {
-  const int t = blockIdx.y;
+  __shared__ __align__(16) float s_dl[kXE][kXP];
   const int c = blockIdx.x * kT + threadIdx.x;
-  if (c >= d) return;
-  float acc = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int r = slot_pos[(size_t)t * k + j];
-    if (r >= 0) acc += dXr[(size_t)r * d + c];
+  const int t0 = blockIdx.y * kXT;
+  const int nt = min(kXT, N - t0);
+  float acc[kXT];
+#pragma unroll
+  for (int q = 0; q < kXT; ++q) acc[q] = 0.f;
+  for (int e0 = 0; e0 < E; e0 += kXE) {
+    const int ne = min(kXE, E - e0);
+    for (int i = threadIdx.x; i < kXT * kXE; i += kT) {
+      const int tt = i / kXE, ee = i % kXE;
+      s_dl[ee][tt] = (tt < nt && ee < ne) ? dl[(size_t)(t0 + tt) * E + e0 + ee] : 0.f;
+    }
+    __syncthreads();
+    if (c < d) {
+      for (int ee = 0; ee < ne; ++ee) {
+        const float w = bf(wr[(size_t)(e0 + ee) * d + c]);
+#pragma unroll
+        for (int q = 0; q < kXT; q += 4) {
+          const float4 g = *reinterpret_cast<const float4*>(&s_dl[ee][q]);
+          acc[q] += g.x * w;
+          acc[q + 1] += g.y * w;
+          acc[q + 2] += g.z * w;
+          acc[q + 3] += g.w * w;
+        }
+      }
+    }
+    __syncthreads();
   }
-  for (int s = 0; s < S; ++s) acc += dXs[((size_t)s * N + t) * d + c];
-  float rr = 0.f;
-  for (int e = 0; e < E; ++e) rr += dl[(size_t)t * E + e] * bf(wr[(size_t)e * d + c]);
-  dx[(size_t)t * d + c] = acc + rr;
+  if (c >= d) return;
+#pragma unroll
+  for (int q = 0; q < kXT; ++q) {
+    if (q < nt) {
+      const int t = t0 + q;
+      float sum = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int r = slot_pos[(size_t)t * k + j];
+        if (r >= 0) sum += dXr[(size_t)r * d + c];
+      }
+      for (int s2 = 0; s2 < S; ++s2) sum += dXs[((size_t)s2 * N + t) * d + c];
+      dx[(size_t)t * d + c] = sum + acc[q];
+    }
+  }
 }
 
 __global__ void fill_f32_kernel(float* p, size_t n, float v) {
@@ -310,6 +434,7 @@ __global__ void fill_f32_kernel(float* p, size_t n, float v) {
 int launch_gather_rows(const void* x, const float* dy, const float* topk_w, const int32_t* perm,
                        const int32_t* n_valid, int k, int d, int rows, void* Xg, void* dYg, void* dO, hipStream_t st) {
   if (rows <= 0) return MOE_OK;
+  if (d % 8) return MOE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(gather_rows_kernel, dim3(rows), dim3(kT), 0, st, static_cast<const bf16_t*>(x), dy, topk_w,
                      perm, n_valid, k, d, static_cast<bf16_t*>(Xg), static_cast<bf16_t*>(dYg),
                      static_cast<bf16_t*>(dO));
@@ -318,6 +443,7 @@ int launch_gather_rows(const void* x, const float* dy, const float* topk_w, cons
 
 int launch_transpose(const void* in, int G, int A, int B, void* out, int dst_stride, int dst_off, hipStream_t st) {
   if (G <= 0 || A <= 0 || B <= 0) return MOE_OK;
+  if (A % 64 || B % 64 || dst_stride % 8 || dst_off % 8 || dst_stride < dst_off + A) return MOE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(transpose_kernel, dim3((B + 63) / 64, (A + 63) / 64, G), dim3(kT), 0, st,
                      static_cast<const bf16_t*>(in), A, B, static_cast<bf16_t*>(out), dst_stride, dst_off);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -340,6 +466,7 @@ int launch_k_offsets(const int32_t* offsets, int G, int uniform, int32_t* kofs, 
 int launch_transpose_padded(const void* in, int in_stride, int col_off, int C, const int32_t* offsets, int uniform,
                             int replicate, const int32_t* kofs, int G, void* out, int kmax, hipStream_t st) {
   if (C <= 0 || kmax <= 0) return MOE_OK;
+  if (in_stride % 8 || col_off % 8 || C % 8 || kmax % 64) return MOE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(transpose_padded_kernel, dim3(kmax / 64, (C + 63) / 64), dim3(kT), 0, st,
                      static_cast<const bf16_t*>(in), in_stride, col_off, C, offsets, uniform, replicate, kofs, G,
                      static_cast<bf16_t*>(out), kmax);
@@ -365,17 +492,36 @@ int launch_router_backward(const moe_shape& s, const float* logits, int splits, 
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-int launch_router_wgrad(const float* dl, const void* x, int N, int E, int d, float* dwr, float* dlb, hipStream_t st) {
-  hipLaunchKernelGGL(router_wgrad_kernel, dim3((d + kT - 1) / kT, (E + kEB - 1) / kEB), dim3(kT), 0, st, dl,
-                     static_cast<const bf16_t*>(x), N, E, d, dwr, dlb);
+int router_wgrad_splits(int N) { return std::max(1, std::min(64, N / 256)); }
+
+size_t router_wgrad_part_floats(int N, int E, int d) { return (size_t)router_wgrad_splits(N) * E * d; }
+
+int launch_router_wgrad(const float* dl, const void* x, int N, int E, int d, float* part, float* dwr, float* dlb,
+                        hipStream_t st) {
+  const int Z = router_wgrad_splits(N);
+  const int chunk = (N + Z - 1) / Z;
+  const int eb = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64;
+  const dim3 grid((d + kT - 1) / kT, (E + eb - 1) / eb, Z);
+#define MOE_RW(EB_)                                                                                              \
+  hipLaunchKernelGGL(router_wgrad_part_kernel<EB_>, grid, dim3(kT), 0, st, dl, static_cast<const bf16_t*>(x), N, E, \
+                     d, chunk, part)
+  if (eb == 8) MOE_RW(8);
+  else if (eb == 16) MOE_RW(16);
+  else if (eb == 32) MOE_RW(32);
+  else MOE_RW(64);
+#undef MOE_RW
+  const size_t n = (size_t)E * d;
+  hipLaunchKernelGGL(router_wgrad_reduce_kernel, dim3((unsigned)((n + kT - 1) / kT)), dim3(kT), 0, st, part, Z, n,
+                     dwr);
+  if (dlb) hipLaunchKernelGGL(logit_bias_grad_kernel, dim3(E), dim3(kT), 0, st, dl, N, E, dlb);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int launch_dx(const float* dXr, const int32_t* slot_pos, const float* dXs, int S, const float* dl, const void* wr,
               int N, int E, int k, int d, float* dx, hipStream_t st) {
   if (N <= 0) return MOE_OK;
-  hipLaunchKernelGGL(dx_kernel, dim3((d + kT - 1) / kT, N), dim3(kT), 0, st, dXr, slot_pos, dXs, S, dl,
-                     static_cast<const bf16_t*>(wr), N, E, k, d, dx);
+  hipLaunchKernelGGL(dx_kernel, dim3((d + kT - 1) / kT, (N + kXT - 1) / kXT), dim3(kT), 0, st, dXr, slot_pos, dXs, S,
+                     dl, static_cast<const bf16_t*>(wr), N, E, k, d, dx);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

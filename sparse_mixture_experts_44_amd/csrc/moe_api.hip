@@ -147,7 +147,7 @@ int grouped_impl(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const v
 // kept copies occupy the first offsets[E]), Kmax = R rounded up to 64 plus 64
 // per expert (each expert's rows padded to 64 in the transposed layout).
 struct BwLayout {
-  size_t logits, dl, dw, kofs, kofs_s, Xg, dYg, dO, G, U, dHp, h, dGU, dXr, WdT, WguT, dOT, hT, dGT, dUT, XT, split;
+  size_t logits, dl, rpart, dw, kofs, kofs_s, Xg, dYg, dO, G, U, dHp, h, dGU, dXr, WdT, WguT, dOT, hT, dGT, dUT, XT, split;
   size_t Xs, dYs, Gs, Us, dHs, hs, dGUs, dXs, SdT, SguT, dOsT, hsT, dGsT, dUsT, XsT, total;
   long long R, Kmax, Npad, KSmax;
 };
@@ -164,6 +164,7 @@ BwLayout bw_layout(const moe_shape& s) {
   auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
   L.logits = take(route_logits_floats(s) * 4);
   L.dl = take(N * E * 4);
+  L.rpart = take(router_wgrad_part_floats((int)N, (int)E, (int)d) * 4);
   L.dw = take(N * k * 4);
   L.kofs = take((E + 1) * 4);
   L.kofs_s = take((S + 1) * 4);
@@ -620,7 +621,7 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
   MOE_TRY(launch_router_logits(s, x, w_router, Pf(L.logits), &splits, stream));
   MOE_TRY(launch_router_backward(s, Pf(L.logits), splits, logit_bias, topk_idx, topk_w, Pf(L.dw), counts, aux_coef,
                                  Pf(L.dl), stream));
-  MOE_TRY(launch_router_wgrad(Pf(L.dl), x, N, E, d, dw_router, d_logit_bias, stream));
+  MOE_TRY(launch_router_wgrad(Pf(L.dl), x, N, E, d, Pf(L.rpart), dw_router, d_logit_bias, stream));
   MOE_TRY(launch_dx(Pf(L.dXr), slot_pos, S > 0 ? Pf(L.dXs) : nullptr, S, Pf(L.dl), w_router, N, E, k, d, dx, stream));
 #undef MOE_TRY
   return MOE_OK;

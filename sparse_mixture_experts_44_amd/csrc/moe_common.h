@@ -126,7 +126,12 @@ int launch_transpose_padded(const void* in, int in_stride, int col_off, int C, c
 int launch_router_backward(const moe_shape& s, const float* logits, int splits, const float* logit_bias,
                            const int32_t* topk_idx, const float* topk_w, const float* dw, const int32_t* counts,
                            double aux_coef, float* dl, hipStream_t st);
-int launch_router_wgrad(const float* dl, const void* x, int N, int E, int d, float* dwr, float* dlb, hipStream_t st);
+// The router weight gradient sums token chunks into part (router_wgrad_part_floats
+// floats), then the chunks in order into dwr; dlb (optional) gets sum_t dl.
+int router_wgrad_splits(int N);
+size_t router_wgrad_part_floats(int N, int E, int d);
+int launch_router_wgrad(const float* dl, const void* x, int N, int E, int d, float* part, float* dwr, float* dlb,
+                        hipStream_t st);
 int launch_dx(const float* dXr, const int32_t* slot_pos, const float* dXs, int S, const float* dl, const void* wr,
               int N, int E, int k, int d, float* dx, hipStream_t st);
 int launch_fill_f32(float* p, size_t n, float v, hipStream_t st);

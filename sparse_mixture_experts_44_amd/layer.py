@@ -52,6 +52,29 @@ class Outputs:
                    torch.empty(1, dtype=f64, device=device))
 
 
+@dataclass
+class Grads:
+    """fp32 gradients of one moe_backward call (ds_*: None without shared experts)."""
+    dx: torch.Tensor            # [N, d]
+    dw_router: torch.Tensor     # [E, d]
+    d_logit_bias: torch.Tensor  # [E]
+    dw_gate: torch.Tensor       # [E, F, d]
+    dw_up: torch.Tensor         # [E, F, d]
+    dw_down: torch.Tensor       # [E, d, F]
+    ds_gate: Optional[torch.Tensor] = None   # [S, Fs, d]
+    ds_up: Optional[torch.Tensor] = None     # [S, Fs, d]
+    ds_down: Optional[torch.Tensor] = None   # [S, d, Fs]
+
+    @classmethod
+    def empty(cls, s: N.MoEShape, device):
+        f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=device)
+        E, d, F, S, Fs = s.n_experts, s.d_model, s.d_ff, s.n_shared, s.d_ff_shared
+        g = cls(f(s.n_tokens, d), f(E, d), f(E), f(E, F, d), f(E, F, d), f(E, d, F))
+        if S:
+            g.ds_gate, g.ds_up, g.ds_down = f(S, Fs, d), f(S, Fs, d), f(S, d, Fs)
+        return g
+
+
 class MoELayer:
     """Weights on the device plus a workspace and outputs sized for n_tokens."""
 
@@ -79,6 +102,7 @@ class MoELayer:
             raise N.MoEError("moe_workspace_bytes", N.MOE_ERR_INVALID_ARG, "invalid shape")
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.out = Outputs.empty(s.n_tokens, s.d_model, s.n_experts, s.top_k, self.device)
+        self.grads = self.bws = None
 
     fp8 = None   # after quantize_fp8(): codes and row scales of every expert weight
     int4 = None  # after quantize_int4(): packed codes and row scales of every expert weight
@@ -142,3 +166,22 @@ class MoELayer:
                       o.topk_w, o.counts, o.offsets, o.perm, o.slot_pos, o.prob_sum,
                       o.balance_stat, self.ws, stage_events=stage_events, stream=stream)
         return o
+
+    def backward(self, x: torch.Tensor, dy: torch.Tensor, aux_coef: float = 0.0, stream=None) -> Grads:
+        """Gradients (moe_backward) of sum(dy * y) + aux_coef * balance statistic for the last
+        forward(x) of this bf16 layer, whose routing in self.out it reuses. The gradient buffers
+        and the backward workspace are allocated on first use and reused."""
+        if self.fp8 is not None or self.int4 is not None:
+            raise ValueError("the backward pass needs the bf16 expert weights")
+        if x.shape[0] != self.shape.n_tokens or tuple(dy.shape) != (self.shape.n_tokens, self.shape.d_model):
+            raise ValueError("x and dy must match the last forward's tokens")
+        if self.grads is None:
+            self.grads = Grads.empty(self.shape, self.device)
+            self.bws = torch.empty(max(1, N.backward_workspace_bytes(self.shape)), dtype=torch.uint8,
+                                   device=self.device)
+        g, o = self.grads, self.out
+        N.moe_backward(self.shape, x, self.w_router, self.logit_bias, self.w_gate, self.w_up, self.w_down,
+                       self.s_gate, self.s_up, self.s_down, o.topk_idx, o.topk_w, o.counts, o.offsets, o.perm,
+                       o.slot_pos, dy, aux_coef, g.dx, g.dw_router, g.d_logit_bias, g.dw_gate, g.dw_up,
+                       g.dw_down, g.ds_gate, g.ds_up, g.ds_down, self.bws, stream=stream)
+        return g

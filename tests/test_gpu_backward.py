@@ -214,38 +214,48 @@ def test_backward_empty_input():
 
 
 @pytest.mark.timeout(600)
-def test_backward_dsv3_decode_sampled():
-    """The DeepSeek-V3-shaped decode layer at full size (64 tokens, 256 experts of d 7168,
-    F 2048, top-8, one shared expert, selection bias), in the launch the benchmark uses: dx on
-    sampled tokens, the weight gradients of sampled experts (the busiest, one with a single
-    copy) and of the shared expert against the sampled oracle; every expert with no copy must
-    get exactly zero gradients; the router gradients satisfy sum_e = 0 (each token's softmax
-    gradient sums to zero over the experts), their full check being the small cases'."""
-    cfg = mi.CONFIGS["dsv3_decode"]
+@pytest.mark.parametrize("name", ["dsv3_decode", "mixtral"])
+def test_backward_full_size_sampled(name):
+    """Full-size layers in the launch the benchmark uses: the DeepSeek-V3-shaped decode layer (64
+    tokens, 256 experts of d 7168, F 2048, top-8, one shared expert, selection bias) and the
+    Mixtral-shaped prefill layer (4096 tokens, 8 experts of d 4096, F 14336, top-2). Checked: dx on
+    sampled tokens; the weight gradients of sampled experts (decode: the two busiest and one with
+    a single copy; prefill: the least loaded) and of the shared expert, against the sampled
+    oracle; exact zeros for every expert with no copy; and, for the router gradients, sum_e = 0
+    (each token's softmax gradient sums to zero over the experts), their full check being the
+    small cases'."""
+    cfg = mi.CONFIGS[name]
     layer, x = mi.make_layer(cfg), mi.make_x(cfg)
     dy = make_dy(cfg.n_tokens, cfg.d_model, 7)
-    ref_idx = P.oracle_route(cfg, layer, x).idx
-    counts = np.bincount(ref_idx.ravel(), minlength=cfg.n_experts)
-    experts = [int(e) for e in np.argsort(-counts, kind="stable")[:2]] + [int(np.flatnonzero(counts == 1)[0])]
-    gpu = run_backward(cfg, layer, x, dy, 0.2, experts=experts)
-    assert gpu.get("n_untouched", 0) > 0 and not gpu["zero_experts"], gpu["zero_experts"]
+    counts = np.bincount(P.oracle_route(cfg, layer, x).idx.ravel(), minlength=cfg.n_experts)
+    if name == "dsv3_decode":
+        experts = [int(e) for e in np.argsort(-counts, kind="stable")[:2]] + [int(np.flatnonzero(counts == 1)[0])]
+    else:
+        experts = [int(np.argmin(counts))]
+    aux = 0.2
+    gpu = run_backward(cfg, layer, x, dy, aux, experts=experts)
+    assert not gpu["zero_experts"], gpu["zero_experts"]
+    assert name != "dsv3_decode" or gpu.get("n_untouched", 0) > 0
     t = time.time()
     tokens = P.sample_rows(cfg.n_tokens, 4, seed=71)
     (wg, wu, wd), shared = P.oracle_views(layer)
-    dx, weights, ds = B.layer_backward_sampled(mi.to_f64(x), mi.to_f64(layer.w_router), wg, wu, wd, gpu["idx"], dy,
-                                               tokens, experts, shared=shared, logit_bias=layer.logit_bias,
-                                               capacity=cfg.capacity, renormalize=cfg.renormalize, round_h=True,
-                                               aux_coef=0.2)
-    check_rows(gpu["dx"][tokens], dx, "dx")
     x64, idx = mi.to_f64(x), np.asarray(gpu["idx"], dtype=np.int64)
+    dx, weights, ds = B.layer_backward_sampled(x64, mi.to_f64(layer.w_router), wg, wu, wd, idx, dy, tokens,
+                                               experts, shared=shared, logit_bias=layer.logit_bias,
+                                               capacity=cfg.capacity, renormalize=cfg.renormalize, round_h=True,
+                                               aux_coef=aux)
+    check_rows(gpu["dx"][tokens], dx, "dx")
     M = term_magnitudes(x64, dy, routed_rows(cfg, layer, x64, idx), wg, wu, wd, experts)
     for e in experts:
-        for i, (name, ref) in enumerate(zip(("dw_gate", "dw_up", "dw_down"), weights[e])):
-            check_terms(gpu[name][e], ref, M[e][i], f"{name}[{e}]")
-    Ms = term_magnitudes(x64, dy, lambda s: (np.arange(cfg.n_tokens), np.ones(cfg.n_tokens)), *shared, [0])
-    for i, (name, ref) in enumerate(zip(("ds_gate", "ds_up", "ds_down"), ds)):
-        check_terms(gpu[name][0], ref[0], Ms[0][i], name)
+        for i, (gname, ref) in enumerate(zip(("dw_gate", "dw_up", "dw_down"), weights[e])):
+            check_terms(gpu[gname][e], ref, M[e][i], f"{gname}[{e}]")
+    if cfg.n_shared:
+        Ms = term_magnitudes(x64, dy, lambda s: (np.arange(cfg.n_tokens), np.ones(cfg.n_tokens)), *shared,
+                             range(cfg.n_shared))
+        for i, (gname, ref) in enumerate(zip(("ds_gate", "ds_up", "ds_down"), ds)):
+            for s_ in range(cfg.n_shared):
+                check_terms(gpu[gname][s_], ref[s_], Ms[s_][i], f"{gname}[{s_}]")
     lb, wr = gpu["d_logit_bias"].astype(np.float64), gpu["dw_router"].astype(np.float64)
     assert abs(lb.sum()) <= 1e-5 * np.sum(np.abs(lb))
     assert np.all(np.abs(wr.sum(axis=0)) <= 1e-5 * np.sum(np.abs(wr), axis=0) + 1e-30)
-    log(f"dsv3_decode: sampled gradients within bounds [{time.time() - t:.1f}s]")
+    log(f"{name}: sampled gradients within bounds [{time.time() - t:.1f}s]")
