@@ -90,31 +90,6 @@ __device__ __forceinline__ void tile_row8(uint16_t (*tile)[kTP], int a, int b0, 
   for (int q = 0; q < 4; ++q) p[q] = v[q];
 }
 
-// out[g][b][a] = in[g][a][b] for G matrices of A x B bf16 (A, B multiples of 64), one
-// 64 x 64 tile per workgroup through LDS, 16-byte loads and stores. dst_stride: row
-// length of the output (>= A, a multiple of 8) and dst_off (a multiple of 8) its first
-// column, so that two transposed matrices can share output rows side by side.
-__global__ __launch_bounds__(kT) void transpose_kernel(const bf16_t* __restrict__ in, int A, int B,
-                                                       bf16_t* __restrict__ out, int dst_stride, int dst_off) {
-  __shared__ uint16_t tile[64][kTP];
-  const int g = blockIdx.z;
-  const int a0 = blockIdx.y * 64, b0 = blockIdx.x * 64;
-  const bf16_t* src = in + (size_t)g * A * B;
-  bf16_t* dst = out + (size_t)g * B * dst_stride;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int q = threadIdx.x + it * kT, a = q >> 3, ch = q & 7;
-    tile_row8(tile, a, ch * 8, *reinterpret_cast<const u32x4_t*>(src + (size_t)(a0 + a) * B + b0 + ch * 8));
-  }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int q = threadIdx.x + it * kT, b = q >> 3, ch = q & 7;
-    *reinterpret_cast<u32x4_t*>(dst + (size_t)(b0 + b) * dst_stride + dst_off + a0 + ch * 8) =
-        tile_column8(tile, ch * 8, b);
-  }
-}
-
 // One row per workgroup: from G, U (fp32 [rows, F]), dH' = dy Wd (fp32) and the
 // row's combine weight w: h = bf16(silu(G) U) (written when h != nullptr),
 // dw = sum_f h dH' (fixed tree order; written to dw[perm[r]] when dw != nullptr),
@@ -438,14 +413,6 @@ int launch_gather_rows(const void* x, const float* dy, const float* topk_w, cons
   hipLaunchKernelGGL(gather_rows_kernel, dim3(rows), dim3(kT), 0, st, static_cast<const bf16_t*>(x), dy, topk_w,
                      perm, n_valid, k, d, static_cast<bf16_t*>(Xg), static_cast<bf16_t*>(dYg),
                      static_cast<bf16_t*>(dO));
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
-}
-
-int launch_transpose(const void* in, int G, int A, int B, void* out, int dst_stride, int dst_off, hipStream_t st) {
-  if (G <= 0 || A <= 0 || B <= 0) return MOE_OK;
-  if (A % 64 || B % 64 || dst_stride % 8 || dst_off % 8 || dst_stride < dst_off + A) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(transpose_kernel, dim3((B + 63) / 64, (A + 63) / 64, G), dim3(kT), 0, st,
-                     static_cast<const bf16_t*>(in), A, B, static_cast<bf16_t*>(out), dst_stride, dst_off);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -54,6 +54,7 @@ struct SetView {  // the fields of one SegSet, picked with selects rather than a
   void* h;
   float* out;
   const int32_t* kofs;  // weight-gradient mode (phase 2): per-group K ranges
+  int32_t bsplit;       // N-major weights: rows >= bsplit come from wu (0: none)
 };
 
 __device__ __forceinline__ SetView pick(const GroupedParams& p, int si) {
@@ -70,6 +71,7 @@ __device__ __forceinline__ SetView pick(const GroupedParams& p, int si) {
   v.h = si ? p.set[1].h : p.set[0].h;
   v.out = si ? p.set[1].out : p.set[0].out;
   v.kofs = si ? p.set[1].k_offsets : p.set[0].k_offsets;
+  v.bsplit = si ? p.set[1].b_split : p.set[0].b_split;
   return v;
 }
 
@@ -206,6 +208,25 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// N-major B tiles (the weight read in its stored orientation). The LDS tile
+// holds BK k-rows of BN bf16 (n contiguous); 64-byte unit u of row k is stored
+// at unit u ^ (k & 3). ds_read_b64_tr_b16 works on groups of 16 lanes: lane i
+// of a group receives, as element j, element (i % 4) of the 8 bytes addressed
+// by lane 4 j + i / 4 of the group. Each lane here addresses 4 consecutive n
+// of one k-row: lane s reads row 8 (s / 32) + (s / 4) % 4 (+ 4 for the second
+// read) at column 16 ((s / 16) % 2) + 4 (s % 4) of its 32-column block, so that
+// lane L ends up with B[8 (L / 32) + t][L % 32], t = 0..7: the MFMA B fragment,
+// in the same k order as the A fragment.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i16x4_t lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+}
+
+template <int ROW>
+__device__ __forceinline__ int nmajor_offset(int k, int n) {
+  return k * ROW + ((((n >> 5) ^ (k & 3)) << 6) | ((n & 31) << 1));
 }
 
 // Wait until at most N of this wave's vector-memory operations are
@@ -419,7 +440,8 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
 // each k16 step of the first half of the step, instead of all at its start,
 // so that fewer copies queue at once behind the barrier (3-5% faster on
 // 256 x 256 tiles; the second half of the step still covers their latency).
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB, int WQ, bool P1, bool SPREAD>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB, int WQ, bool P1, bool SPREAD,
+          bool NMAJ = false>
 __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(GroupedParams p) {
   constexpr bool W8 = WQ == 8, W4 = WQ == 4, WS = WQ != 0;
   using BT = typename std::conditional<WS, uint8_t, bf16_t>::type;  // weight storage unit
@@ -446,6 +468,10 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
   static_assert(A_INS >= 1 && B_INS >= 1 && FM >= 1 && FN >= 1 && NS >= 2 && NS <= 6, "tile shape");
   static_assert(A_INS * RPIA * WAVES == BM && B_INS * RPIB * WAVES == BN, "copy slots cover the tile");
   static_assert(!P1 || (BN / 2) % (RPIB * B_INS) == 0, "a wave's B rows come from one matrix");
+  // N-major B: a 1 KB copy fills 1024 / (2 BN) k-rows
+  constexpr int ROWBN = BN * 2;
+  static_assert(!NMAJ || (!P1 && !WS && BK == 64 && ROWBN == 512 && B_INS * 2 * WAVES == BK),
+                "N-major weights: phase 2, bf16, 64 x 256 B tiles");
 
   __shared__ __attribute__((aligned(1024))) uint8_t s_tile[NS][STAGE];
   __shared__ TableLds tab;
@@ -523,22 +549,42 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     }
     // ---- B sources: weight rows n0 + (tile row within its matrix); rows past
     // the last output column (partial n-tile) re-read an in-range row.
+    // N-major weights: k-rows (wave*B_INS + i)*2 + lane/32, lane%32 the 16-byte
+    // piece, fetched from the swizzled column; columns past the last output
+    // column re-read an in-range piece.
     const int lastq = min(BH, ncols - n0) - 1;
     const BT* b_base;
+    const BT* b_hi = nullptr;
+    const int bsplit = NMAJ ? (S.bsplit ? S.bsplit : K) : 0;
     if constexpr (P1) {
       const bool up = wave * B_INS * RPIB >= BN / 2;
       b_base = static_cast<const BT*>(up ? S.wu : S.wg) + (size_t)g * F * d / KDIV;
+    } else if constexpr (NMAJ) {
+      b_base = static_cast<const BT*>(S.wd) + (size_t)g * bsplit * d;
+      b_hi = static_cast<const BT*>(S.wu) + (size_t)g * bsplit * d;
     } else {
       b_base = static_cast<const BT*>(S.wd) + (S.kofs ? 0 : (size_t)g * d * F / KDIV);
     }
     uint32_t b_off[B_INS];
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
-      const int r = (wave * B_INS + i) * RPIB + crowB;    // tile row
-      const int mr = P1 ? (r % (BN / 2)) : r;              // row within its weight matrix tile
-      b_off[i] = (uint32_t)(n0 + min(mr, lastq)) * (uint32_t)(kstride / KDIV) + (uint32_t)(kbase / KDIV) +
-                 (uint32_t)((cpcB ^ swz<PPB>(r)) * EPP);
+      if constexpr (NMAJ) {
+        const int kr = (wave * B_INS + i) * 2 + (lane >> 5);
+        const int pl = lane & 31;
+        const int pg = (((pl >> 2) ^ (kr & 3)) << 2) | (pl & 3);
+        b_off[i] = (uint32_t)kr * (uint32_t)d + (uint32_t)min(n0 + pg * 8, ncols - 8);
+      } else {
+        const int r = (wave * B_INS + i) * RPIB + crowB;    // tile row
+        const int mr = P1 ? (r % (BN / 2)) : r;              // row within its weight matrix tile
+        b_off[i] = (uint32_t)(n0 + min(mr, lastq)) * (uint32_t)(kstride / KDIV) + (uint32_t)(kbase / KDIV) +
+                   (uint32_t)((cpcB ^ swz<PPB>(r)) * EPP);
+      }
     }
+    // the source of this wave's B copies for the stage at K offset ko
+    auto b_src = [&](int ko) -> const BT* {
+      if constexpr (NMAJ) return ko < bsplit ? b_base + (size_t)ko * d : b_hi + (size_t)(ko - bsplit) * d;
+      else return b_base + ko / KDIV;
+    };
     const uint32_t a_lds0 = lds_addr(&s_tile[0][(wave * A_INS) * 1024]);
     const uint32_t b_lds0 = lds_addr(&s_tile[0][STAGE_A + (wave * B_INS) * 1024]);
 
@@ -556,8 +602,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
 #pragma unroll
       for (int i = 0; i < A_INS; ++i)
         if (i < a_act) dma16(a_base + a_off[i] + ko, a_lds0 + st * STAGE + i * 1024);
+      const BT* bsrc = b_src(ko);
 #pragma unroll
-      for (int i = 0; i < B_INS; ++i) dma16(b_base + b_off[i] + ko / KDIV, b_lds0 + st * STAGE + i * 1024);
+      for (int i = 0; i < B_INS; ++i) dma16(bsrc + b_off[i], b_lds0 + st * STAGE + i * 1024);
     };
     // copies [c0, c1) of stage kt, in the order A (active ones) then B
     auto issue_part = [&](int kt, int c0, int c1) {
@@ -569,7 +616,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
         if (c < A_INS) {
           if (c < a_act) dma16(a_base + a_off[c] + ko, a_lds0 + st * STAGE + c * 1024);
         } else {
-          dma16(b_base + b_off[c - A_INS] + ko / KDIV, b_lds0 + st * STAGE + (c - A_INS) * 1024);
+          dma16(b_src(ko) + b_off[c - A_INS], b_lds0 + st * STAGE + (c - A_INS) * 1024);
         }
       }
     };
@@ -629,7 +676,13 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
           const int jj = P1 ? (j % FN) : j;                                                      \
           const int half = P1 ? (j / FN) * (BN / 2) : 0;                                         \
           const int r = half + wn * TN + jj * 32 + (lane & 31);                                  \
-          if constexpr (W4) {                                                                    \
+          if constexpr (NMAJ) {                                                                  \
+            const int kr = ks * 16 + 8 * (lane >> 5) + ((lane >> 2) & 3);                        \
+            const int nc = wn * TN + jj * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);          \
+            const uint8_t* pt = sb + nmajor_offset<ROWBN>(kr, nc);                               \
+            const i16x4_t lo = lds_read_tr16(pt), hi = lds_read_tr16(pt + 4 * ROWBN);            \
+            bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)); \
+          } else if constexpr (W4) {                                                             \
             bfr[j] = int4x8_to_bf16_biased(wq[j][ks]);                                           \
           } else if constexpr (W8) {                                                             \
             /* piece ks holds the 16 codes of this k16 step; lanes 32-63 take its upper 8 */     \
@@ -846,11 +899,15 @@ int grid_for(long long ub, int per_cu) {
 // per_cu: workgroups launched per CU at most. 1 is a persistent grid (each
 // workgroup walks the tile list with stride gridDim.x); a large value
 // launches about one workgroup per tile.
-template <int BM, int BN, int BK, int WGM, int WGN, int NS, int WQ, bool SPREAD = false, int MINB = 1>
+template <int BM, int BN, int BK, int WGM, int WGN, int NS, int WQ, bool SPREAD = false, int MINB = 1,
+          bool NMAJ = false>
 void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) {
   const int BH = phase == 1 ? BN / 2 : BN;
   const int grid = grid_for(tiles_upper_bound(p, phase, BM, BH), per_cu);
-  if (phase == 1)
+  if constexpr (NMAJ)
+    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, true>), dim3(grid),
+                       dim3(WGM * WGN * 64), 0, st, p);
+  else if (phase == 1)
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
   else
@@ -881,7 +938,10 @@ void launch_class(const GroupedParams& p, int phase, hipStream_t stream) {
     // tile run in step, so their copies of it hit in L2
     GroupedParams q = p;
     q.balance_m = 1;
-    launch_mfma<256, 256, 64, 2, 4, 2, WQ, true>(q, phase, 1, stream);
+    if (WQ == 0 && phase == 2 && p.set[0].b_nmajor) launch_mfma<256, 256, 64, 2, 4, 2, 0, true, 1, true>(q, 2, 1, stream);
+    else launch_mfma<256, 256, 64, 2, 4, 2, WQ, true>(q, phase, 1, stream);
+  } else if (WQ == 0 && phase == 2 && p.set[0].b_nmajor) {
+    launch_mfma<64, 256, 64, 1, 4, 3, 0, false, 1, true>(p, 2, 1, stream);
   } else {
     // FP8 weights halve the B stages (80 KB of LDS in all), so two workgroups share a CU
     launch_mfma<64, 256, 64, 1, 4, 3, WQ>(p, phase, WQ == 8 ? 2 : 1, stream);

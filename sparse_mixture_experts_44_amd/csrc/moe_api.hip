@@ -147,8 +147,8 @@ int grouped_impl(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const v
 // kept copies occupy the first offsets[E]), Kmax = R rounded up to 64 plus 64
 // per expert (each expert's rows padded to 64 in the transposed layout).
 struct BwLayout {
-  size_t logits, dl, rpart, dw, kofs, kofs_s, Xg, dYg, dO, G, U, dHp, h, dGU, dXr, WdT, WguT, dOT, hT, dGT, dUT, XT, split;
-  size_t Xs, dYs, Gs, Us, dHs, hs, dGUs, dXs, SdT, SguT, dOsT, hsT, dGsT, dUsT, XsT, total;
+  size_t logits, dl, rpart, dw, kofs, kofs_s, Xg, dYg, dO, G, U, dHp, h, dGU, dXr, dOT, hT, dGT, dUT, XT, split;
+  size_t Xs, dYs, Gs, Us, dHs, hs, dGUs, dXs, dOsT, hsT, dGsT, dUsT, XsT, total;
   long long R, Kmax, Npad, KSmax;
 };
 
@@ -177,8 +177,6 @@ BwLayout bw_layout(const moe_shape& s) {
   L.h = take(L.R * F * 2);
   L.dGU = take(L.R * 2 * F * 2);
   L.dXr = take(L.R * d * 4);
-  L.WdT = take(E * F * d * 2);
-  L.WguT = take(E * d * 2 * F * 2);
   L.dOT = take(d * L.Kmax * 2);
   L.hT = take(F * L.Kmax * 2);
   L.dGT = take(F * L.Kmax * 2);
@@ -193,8 +191,6 @@ BwLayout bw_layout(const moe_shape& s) {
   L.hs = take(S * N * Fs * 2);
   L.dGUs = take(S * N * 2 * Fs * 2);
   L.dXs = take(S * N * d * 4);
-  L.SdT = take(S * Fs * d * 2);
-  L.SguT = take(S * d * 2 * Fs * 2);
   L.dOsT = take(d * L.KSmax * 2);
   L.hsT = take(Fs * L.KSmax * 2);
   L.dGsT = take(Fs * L.KSmax * 2);
@@ -229,6 +225,37 @@ int grouped_gemm(int n_groups, const int32_t* offsets, int uniform, long long ma
   S.h = const_cast<void*>(A);
   S.out = out;
   S.k_offsets = kofs;
+  return launch_grouped(p, 2, st);
+}
+
+// out[r, n] = sum_k A[r, k] B_g[k, n] with the weights in their stored, N-major
+// orientation: B_g's rows k < b_split (all K rows when b_split == 0) are rows of
+// B_lo + g * b_split * ncols (g * K * ncols), the others rows k - b_split of
+// B_hi + g * b_split * ncols.
+int grouped_gemm_nmajor(int n_groups, const int32_t* offsets, int uniform, long long max_rows, int K, int ncols,
+                        const void* A, const void* B_lo, const void* B_hi, int b_split, float* out, float* split_ws,
+                        size_t split_bytes, hipStream_t st) {
+  GroupedParams p{};
+  p.n_sets = 1;
+  p.x = A;
+  p.n_tokens = 1;
+  p.d_model = ncols;
+  p.dtype = MOE_DTYPE_BF16;
+  p.split_ws = split_ws;
+  p.split_cap = split_ws ? (long long)(split_bytes / sizeof(float)) : 0;
+  SegSet& S = p.set[0];
+  S.offsets = offsets;
+  S.n_groups = n_groups;
+  S.uniform_rows = uniform;
+  S.rows_per_token = 1;
+  S.max_rows = (int32_t)max_rows;
+  S.d_ff = K;
+  S.w_gate = S.w_down = B_lo;
+  S.w_up = B_hi;
+  S.h = const_cast<void*>(A);
+  S.out = out;
+  S.b_nmajor = 1;
+  S.b_split = b_split;
   return launch_grouped(p, 2, st);
 }
 
@@ -563,16 +590,16 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
   // ---- routed experts
   MOE_TRY(launch_fill_f32(Pf(L.dw), (size_t)N * k, 0.f, stream));  // dropped copies keep 0
   MOE_TRY(launch_gather_rows(x, dy, topk_w, perm, n_kept, k, d, R, P(L.Xg), P(L.dYg), P(L.dO), stream));
-  MOE_TRY(launch_transpose(w_down, E, d, F, P(L.WdT), d, 0, stream));          // [E, F, d]
-  MOE_TRY(launch_transpose(w_gate, E, F, d, P(L.WguT), 2 * F, 0, stream));     // [E, d, 2F]: Wg^T | Wu^T
-  MOE_TRY(launch_transpose(w_up, E, F, d, P(L.WguT), 2 * F, F, stream));
   MOE_TRY(grouped_gemm(E, offsets, 0, R, d, F, P(L.Xg), w_gate, Pf(L.G), nullptr, split, split_bytes, stream));
   MOE_TRY(grouped_gemm(E, offsets, 0, R, d, F, P(L.Xg), w_up, Pf(L.U), nullptr, split, split_bytes, stream));
-  MOE_TRY(grouped_gemm(E, offsets, 0, R, d, F, P(L.dYg), P(L.WdT), Pf(L.dHp), nullptr, split, split_bytes, stream));
+  // dH' = dy Wd: w_down [E, d, F] is read as d rows of F values
+  MOE_TRY(grouped_gemm_nmajor(E, offsets, 0, R, d, F, P(L.dYg), w_down, nullptr, 0, Pf(L.dHp), split, split_bytes,
+                              stream));
   MOE_TRY(launch_swiglu_backward(Pf(L.G), Pf(L.U), Pf(L.dHp), topk_w, perm, n_kept, R, F, P(L.h), P(L.dGU),
                                  Pf(L.dw), stream));
-  MOE_TRY(grouped_gemm(E, offsets, 0, R, 2 * F, d, P(L.dGU), P(L.WguT), Pf(L.dXr), nullptr, split, split_bytes,
-                       stream));
+  // dX = [dG | dU] [Wg ; Wu]: rows k < F of the operand are w_gate's, the rest w_up's
+  MOE_TRY(grouped_gemm_nmajor(E, offsets, 0, R, 2 * F, d, P(L.dGU), w_gate, w_up, F, Pf(L.dXr), split, split_bytes,
+                              stream));
   MOE_TRY(launch_k_offsets(offsets, E, 0, Pi(L.kofs), stream));
   MOE_TRY(launch_transpose_padded(P(L.dO), d, 0, d, offsets, 0, 0, Pi(L.kofs), E, P(L.dOT), Kmax, stream));
   MOE_TRY(launch_transpose_padded(P(L.h), F, 0, F, offsets, 0, 0, Pi(L.kofs), E, P(L.hT), Kmax, stream));
@@ -592,17 +619,14 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
       MOE_TRY(launch_gather_rows(x, dy, nullptr, nullptr, nullptr, 1, d, N,
                                  static_cast<uint8_t*>(P(L.Xs)) + (size_t)q * N * d * 2,
                                  static_cast<uint8_t*>(P(L.dYs)) + (size_t)q * N * d * 2, nullptr, stream));
-    MOE_TRY(launch_transpose(s_down, S, d, Fs, P(L.SdT), d, 0, stream));
-    MOE_TRY(launch_transpose(s_gate, S, Fs, d, P(L.SguT), 2 * Fs, 0, stream));
-    MOE_TRY(launch_transpose(s_up, S, Fs, d, P(L.SguT), 2 * Fs, Fs, stream));
     MOE_TRY(grouped_gemm(S, nullptr, N, RS, d, Fs, P(L.Xs), s_gate, Pf(L.Gs), nullptr, split, split_bytes, stream));
     MOE_TRY(grouped_gemm(S, nullptr, N, RS, d, Fs, P(L.Xs), s_up, Pf(L.Us), nullptr, split, split_bytes, stream));
-    MOE_TRY(grouped_gemm(S, nullptr, N, RS, d, Fs, P(L.dYs), P(L.SdT), Pf(L.dHs), nullptr, split, split_bytes,
-                         stream));
+    MOE_TRY(grouped_gemm_nmajor(S, nullptr, N, RS, d, Fs, P(L.dYs), s_down, nullptr, 0, Pf(L.dHs), split,
+                                split_bytes, stream));
     MOE_TRY(launch_swiglu_backward(Pf(L.Gs), Pf(L.Us), Pf(L.dHs), nullptr, nullptr, nullptr, RS, Fs, P(L.hs),
                                    P(L.dGUs), nullptr, stream));
-    MOE_TRY(grouped_gemm(S, nullptr, N, RS, 2 * Fs, d, P(L.dGUs), P(L.SguT), Pf(L.dXs), nullptr, split,
-                         split_bytes, stream));
+    MOE_TRY(grouped_gemm_nmajor(S, nullptr, N, RS, 2 * Fs, d, P(L.dGUs), s_gate, s_up, Fs, Pf(L.dXs), split,
+                                split_bytes, stream));
     MOE_TRY(launch_k_offsets(nullptr, S, N, Pi(L.kofs_s), stream));
     MOE_TRY(launch_transpose_padded(P(L.dYs), d, 0, d, nullptr, N, 0, Pi(L.kofs_s), S, P(L.dOsT), KS, stream));
     MOE_TRY(launch_transpose_padded(P(L.hs), Fs, 0, Fs, nullptr, N, 0, Pi(L.kofs_s), S, P(L.hsT), KS, stream));

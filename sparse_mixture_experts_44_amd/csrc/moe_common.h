@@ -80,6 +80,14 @@ struct SegSet {
   // of 64; empty: zero output); both are single matrices shared by all
   // groups, with rows d_ff values apart: out[g*M + m, n] = sum_k h[m, k] * w_down[n, k].
   const int32_t* k_offsets;
+  // N-major weights (phase 2 only, bf16, not with k_offsets): when b_nmajor is
+  // set, group g's operand is read as K rows of d_model values each (the
+  // weight in its stored orientation: out[r, n] = sum_k h[r, k] * B_g[k, n]).
+  // Rows k < b_split (all rows when b_split == 0) come from w_down + g*b_split*d
+  // (g*K*d without a split), rows k >= b_split from w_up + g*b_split*d at row
+  // k - b_split. b_split is a multiple of 64.
+  int32_t b_nmajor;
+  int32_t b_split;
 };
 
 struct GroupedParams {
@@ -116,7 +124,6 @@ int launch_quantize_int4(long long rows, int cols, const void* w_bf16, uint8_t* 
 // ------------------------------------------------------------------ backward (backward.hip)
 int launch_gather_rows(const void* x, const float* dy, const float* topk_w, const int32_t* perm,
                        const int32_t* n_valid, int k, int d, int rows, void* Xg, void* dYg, void* dO, hipStream_t st);
-int launch_transpose(const void* in, int G, int A, int B, void* out, int dst_stride, int dst_off, hipStream_t st);
 int launch_swiglu_backward(const float* G, const float* U, const float* dHp, const float* topk_w,
                            const int32_t* perm, const int32_t* n_valid, int rows, int F, void* h, void* dGU,
                            float* dw, hipStream_t st);
