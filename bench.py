@@ -118,23 +118,29 @@ def time_backward(L, xd, cfg, steps, warmup, kept):
     import torch
     g = torch.Generator(device=xd.device).manual_seed(1234)
     dy = torch.randn(cfg.n_tokens, cfg.d_model, generator=g, device=xd.device).bfloat16().float()
-    for _ in range(warmup):
-        L.backward(xd, dy, 0.01)
-    ev = HipEvents(2)
     stream = torch.cuda.current_stream().cuda_stream
-    torch.cuda.synchronize()
-    ev.record(0, stream)
-    for _ in range(steps):
-        L.backward(xd, dy, 0.01)
-    ev.record(1, stream)
-    torch.cuda.synchronize()
-    ms = ev.elapsed_ms(0, 1) / steps
+
+    def timed(accumulate):
+        for _ in range(warmup):
+            L.backward(xd, dy, 0.01, accumulate=accumulate)
+        ev = HipEvents(2)
+        torch.cuda.synchronize()
+        ev.record(0, stream)
+        for _ in range(steps):
+            L.backward(xd, dy, 0.01, accumulate=accumulate)
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        return ev.elapsed_ms(0, 1) / steps
+
+    ms, ms_acc = timed(False), timed(True)
     w = backward_work(cfg, kept)
     tf = w["flops_algorithmic"] / (ms * 1e-3) / 1e12
     return {"ms": ms, "steps": steps, "tflops_algorithmic": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
             "tflops_executed": w["flops_executed"] / (ms * 1e-3) / 1e12, **w,
-            "note": "moe_backward alone (gradients of x, W_r, logit bias, every expert weight); "
-                    "algorithmic FLOPs exclude the G, U and logit recompute"}
+            "ms_accumulate": ms_acc,
+            "note": "moe_backward alone (gradients of x, W_r, logit bias, every expert weight), writing the "
+                    "gradients (ms) or adding them to fp32 buffers (ms_accumulate); algorithmic FLOPs exclude "
+                    "the G, U and logit recompute"}
 
 
 class HipEvents:

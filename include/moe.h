@@ -346,21 +346,26 @@ size_t moe_backward_workspace_bytes(const moe_shape* shape);
  * [N*k], slot_pos [N*k] (unchanged since that call); dy [N, d] fp32, read at
  * bf16 precision (every use goes through its round-to-nearest-even bf16
  * value, so bf16-valued dy loses nothing); aux_coef (finite; 0 drops the
- * balance term).
- * Outputs (fp32, every entry written): dx [N, d]; dw_router [E, d];
- * d_logit_bias [E] (NULL: not computed); dw_gate, dw_up [E, F, d]; dw_down
- * [E, d, F] (zero for an expert with no kept copy); ds_gate, ds_up [S, Fs, d]
- * and ds_down [S, d, Fs] (may be NULL when S == 0).
+ * balance term); accumulate (0 or 1, below).
+ * Outputs (fp32): dx [N, d]; dw_router [E, d]; d_logit_bias [E] (NULL: not
+ * computed); dw_gate, dw_up [E, F, d]; dw_down [E, d, F]; ds_gate, ds_up
+ * [S, Fs, d] and ds_down [S, d, Fs] (may be NULL when S == 0).
+ * accumulate == 0: every entry is written (an expert with no kept copy gets
+ * zeros). accumulate == 1: dx is written, every other output gets the
+ * gradient added to its contents (an expert with no kept copy is not
+ * touched): the form for summing gradients over micro-batches into fp32
+ * buffers, which also skips writing the zero gradients of idle experts.
  * Errors: MOE_ERR_UNSUPPORTED unless the shape's dtype is MOE_DTYPE_BF16;
- * MOE_ERR_INVALID_ARG for a missing pointer or a non-finite aux_coef;
+ * MOE_ERR_INVALID_ARG for a missing pointer, a non-finite aux_coef or
+ * accumulate not 0 or 1;
  * MOE_ERR_WORKSPACE when ws_bytes < moe_backward_workspace_bytes(shape). */
 int moe_backward(const moe_shape* shape, const void* x, const void* w_router, const float* logit_bias,
                  const void* w_gate, const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
                  const void* s_down, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
                  const int32_t* offsets, const int32_t* perm, const int32_t* slot_pos, const float* dy,
-                 double aux_coef, float* dx, float* dw_router, float* d_logit_bias, float* dw_gate, float* dw_up,
-                 float* dw_down, float* ds_gate, float* ds_up, float* ds_down, void* ws, size_t ws_bytes,
-                 hipStream_t stream);
+                 double aux_coef, int32_t accumulate, float* dx, float* dw_router, float* d_logit_bias,
+                 float* dw_gate, float* dw_up, float* dw_down, float* ds_gate, float* ds_up, float* ds_down, void* ws,
+                 size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

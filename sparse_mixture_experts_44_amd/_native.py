@@ -73,7 +73,7 @@ _SIGS = {
                                        _P, _P, _P, _SZ, _P, _P]),
     "moe_quantize_int4": (ctypes.c_int, [ctypes.c_int64, _I, _P, _P, _P, _P]),
     "moe_backward_workspace_bytes": (_SZ, [_SHP]),
-    "moe_backward": (ctypes.c_int, [_SHP] + [_P] * 16 + [ctypes.c_double] + [_P] * 10 + [_SZ, _P]),
+    "moe_backward": (ctypes.c_int, [_SHP] + [_P] * 16 + [ctypes.c_double, _I] + [_P] * 10 + [_SZ, _P]),
     "moe_grouped_swiglu_int4": (ctypes.c_int, [_SHP, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P,
                                                _P, _P, _P, _SZ, _P]),
     "moe_forward_int4": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -263,11 +263,12 @@ def backward_workspace_bytes(shape: MoEShape) -> int:
 
 
 def moe_backward(shape, x, w_router, logit_bias, w_gate, w_up, w_down, s_gate, s_up, s_down, topk_idx, topk_w,
-                 counts, offsets, perm, slot_pos, dy, aux_coef, dx, dw_router, d_logit_bias, dw_gate, dw_up,
-                 dw_down, ds_gate, ds_up, ds_down, ws, stream=None):
+                 counts, offsets, perm, slot_pos, dy, aux_coef, accumulate, dx, dw_router, d_logit_bias, dw_gate,
+                 dw_up, dw_down, ds_gate, ds_up, ds_down, ws, stream=None):
     _check("moe_backward", lib().moe_backward(
         ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
         _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
-        _ptr(perm), _ptr(slot_pos), _ptr(dy), float(aux_coef), _ptr(dx), _ptr(dw_router), _ptr(d_logit_bias),
+        _ptr(perm), _ptr(slot_pos), _ptr(dy), float(aux_coef), int(accumulate), _ptr(dx), _ptr(dw_router),
+        _ptr(d_logit_bias),
         _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ds_gate), _ptr(ds_up), _ptr(ds_down), _ptr(ws),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))

@@ -316,20 +316,20 @@ __global__ __launch_bounds__(kT) void router_wgrad_part_kernel(const float* __re
     if (e0 + q < E) part[((size_t)blockIdx.z * E + e0 + q) * d + c] = acc[q];
 }
 
-// Second pass: dW_r[e][c] = sum_z part[z][e][c], z in order.
+// Second pass: dW_r[e][c] = sum_z part[z][e][c], z in order (added to dW_r when accumulating).
 __global__ __launch_bounds__(kT) void router_wgrad_reduce_kernel(const float* __restrict__ part, int Z, size_t n,
-                                                                 float* __restrict__ dwr) {
+                                                                 int accumulate, float* __restrict__ dwr) {
   const size_t i = (size_t)blockIdx.x * kT + threadIdx.x;
   if (i >= n) return;
   float acc = 0.f;
   for (int z = 0; z < Z; ++z) acc += part[(size_t)z * n + i];
-  dwr[i] = acc;
+  dwr[i] = accumulate ? dwr[i] + acc : acc;
 }
 
 // d_logit_bias[e] = sum_t dl[t][e]: one workgroup per expert, a strided sum per
 // thread and a fixed tree over the threads.
 __global__ __launch_bounds__(kT) void logit_bias_grad_kernel(const float* __restrict__ dl, int N, int E,
-                                                             float* __restrict__ dlb) {
+                                                             int accumulate, float* __restrict__ dlb) {
   __shared__ float s_part[kT];
   const int e = blockIdx.x;
   float acc = 0.f;
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kT) void logit_bias_grad_kernel(const float* __rest
     if (threadIdx.x < st) s_part[threadIdx.x] += s_part[threadIdx.x + st];
     __syncthreads();
   }
-  if (threadIdx.x == 0) dlb[e] = s_part[0];
+  if (threadIdx.x == 0) dlb[e] = accumulate ? dlb[e] + s_part[0] : s_part[0];
 }
 
 // dx[t][c] = (sum_j dXr[slot_pos[t*k + j]][c] over the kept copies, j in order,
@@ -464,7 +464,7 @@ int router_wgrad_splits(int N) { return std::max(1, std::min(64, N / 256)); }
 size_t router_wgrad_part_floats(int N, int E, int d) { return (size_t)router_wgrad_splits(N) * E * d; }
 
 int launch_router_wgrad(const float* dl, const void* x, int N, int E, int d, float* part, float* dwr, float* dlb,
-                        hipStream_t st) {
+                        int accumulate, hipStream_t st) {
   const int Z = router_wgrad_splits(N);
   const int chunk = (N + Z - 1) / Z;
   const int eb = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64;
@@ -479,8 +479,8 @@ int launch_router_wgrad(const float* dl, const void* x, int N, int E, int d, flo
 #undef MOE_RW
   const size_t n = (size_t)E * d;
   hipLaunchKernelGGL(router_wgrad_reduce_kernel, dim3((unsigned)((n + kT - 1) / kT)), dim3(kT), 0, st, part, Z, n,
-                     dwr);
-  if (dlb) hipLaunchKernelGGL(logit_bias_grad_kernel, dim3(E), dim3(kT), 0, st, dl, N, E, dlb);
+                     accumulate, dwr);
+  if (dlb) hipLaunchKernelGGL(logit_bias_grad_kernel, dim3(E), dim3(kT), 0, st, dl, N, E, accumulate, dlb);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -55,6 +55,7 @@ struct SetView {  // the fields of one SegSet, picked with selects rather than a
   float* out;
   const int32_t* kofs;  // weight-gradient mode (phase 2): per-group K ranges
   int32_t bsplit;       // N-major weights: rows >= bsplit come from wu (0: none)
+  int32_t accum;        // phase 2: out += product
 };
 
 __device__ __forceinline__ SetView pick(const GroupedParams& p, int si) {
@@ -72,6 +73,7 @@ __device__ __forceinline__ SetView pick(const GroupedParams& p, int si) {
   v.out = si ? p.set[1].out : p.set[0].out;
   v.kofs = si ? p.set[1].k_offsets : p.set[0].k_offsets;
   v.bsplit = si ? p.set[1].b_split : p.set[0].b_split;
+  v.accum = si ? p.set[1].accumulate : p.set[0].accumulate;
   return v;
 }
 
@@ -396,6 +398,31 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
   auto rows = [&](auto check) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if constexpr (!P1 && !WS) {
+        if (S.accum) {
+          // out += product: the block's old values are all loaded before the first
+          // store (a load after a store to another row would wait for that store)
+          float old[16][FN];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
+            const bool ok = !decltype(check)::value || r < t.mvalid;
+            const float* orow = S.out + (size_t)(t.start + t.m0 + r) * d + col0;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) old[v][j] = (ok && col0 + j * 32 < ncols) ? orow[j * 32] : 0.f;
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
+            if (decltype(check)::value && r >= t.mvalid) continue;
+            float* orow = S.out + (size_t)(t.start + t.m0 + r) * d + col0;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              if (col0 + j * 32 < ncols) orow[j * 32] = old[v][j] + acc[i][j][v];
+          }
+          continue;
+        }
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
@@ -523,6 +550,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
       }
     }
     const int nk_all = K / BK;
+    // accumulating weight gradients: a group with no rows adds nothing (a K-part
+    // of a split tile still writes its zero sum for the part-sum kernel)
+    if (!P1 && S.accum && nk_all == 0 && part < 0) continue;
     // this unit's K steps: all of them, or part `part` of sp.S
     const int k_lo = part < 0 ? 0 : (int)((long long)part * nk_all / sp.S);
     const int nk = part < 0 ? nk_all : (int)((long long)(part + 1) * nk_all / sp.S) - k_lo;

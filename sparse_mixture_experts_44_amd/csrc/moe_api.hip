@@ -205,7 +205,7 @@ BwLayout bw_layout(const moe_shape& s) {
 // out[g*M + m, n] = sum over group g's K range of A[m, k] B[n, k].
 int grouped_gemm(int n_groups, const int32_t* offsets, int uniform, long long max_rows, int K_or_stride, int ncols,
                  const void* A, const void* B, float* out, const int32_t* kofs, float* split_ws, size_t split_bytes,
-                 hipStream_t st) {
+                 hipStream_t st, int accumulate = 0) {
   GroupedParams p{};
   p.n_sets = 1;
   p.x = A;
@@ -225,6 +225,7 @@ int grouped_gemm(int n_groups, const int32_t* offsets, int uniform, long long ma
   S.h = const_cast<void*>(A);
   S.out = out;
   S.k_offsets = kofs;
+  S.accumulate = accumulate;
   return launch_grouped(p, 2, st);
 }
 
@@ -553,14 +554,14 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
                  const void* w_gate, const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
                  const void* s_down, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
                  const int32_t* offsets, const int32_t* perm, const int32_t* slot_pos, const float* dy,
-                 double aux_coef, float* dx, float* dw_router, float* d_logit_bias, float* dw_gate, float* dw_up,
-                 float* dw_down, float* ds_gate, float* ds_up, float* ds_down, void* ws, size_t ws_bytes,
-                 hipStream_t stream) {
+                 double aux_coef, int32_t accumulate, float* dx, float* dw_router, float* d_logit_bias,
+                 float* dw_gate, float* dw_up, float* dw_down, float* ds_gate, float* ds_up, float* ds_down, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
   if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (!std::isfinite(aux_coef)) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(aux_coef) || (accumulate != 0 && accumulate != 1)) return MOE_ERR_INVALID_ARG;
   if (!dw_router || !dw_gate || !dw_up || !dw_down || !w_gate || !w_up || !w_down || !w_router || !ws)
     return MOE_ERR_INVALID_ARG;
   if (s.n_shared > 0 && (!s_gate || !s_up || !s_down || !ds_gate || !ds_up || !ds_down)) return MOE_ERR_INVALID_ARG;
@@ -570,7 +571,8 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   const int N = s.n_tokens, k = s.top_k, E = s.n_experts, d = s.d_model, F = s.d_ff;
   const int S = s.n_shared, Fs = S ? s.d_ff_shared : 0;
-  if (N == 0) {  // no tokens: every gradient is 0
+  if (N == 0) {  // no tokens: every gradient is 0 (nothing to add when accumulating)
+    if (accumulate) return MOE_OK;
     for (auto pr : {std::make_pair(dw_router, (size_t)E * d), std::make_pair(dw_gate, (size_t)E * F * d),
                     std::make_pair(dw_up, (size_t)E * F * d), std::make_pair(dw_down, (size_t)E * d * F),
                     std::make_pair(d_logit_bias, (size_t)E), std::make_pair(ds_gate, (size_t)S * Fs * d),
@@ -607,11 +609,11 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
   MOE_TRY(launch_transpose_padded(P(L.dGU), 2 * F, F, F, offsets, 0, 0, Pi(L.kofs), E, P(L.dUT), Kmax, stream));
   MOE_TRY(launch_transpose_padded(P(L.Xg), d, 0, d, offsets, 0, 0, Pi(L.kofs), E, P(L.XT), Kmax, stream));
   MOE_TRY(grouped_gemm(E, nullptr, d, (long long)E * d, Kmax, F, P(L.dOT), P(L.hT), dw_down, Pi(L.kofs), split,
-                       split_bytes, stream));
+                       split_bytes, stream, accumulate));
   MOE_TRY(grouped_gemm(E, nullptr, F, (long long)E * F, Kmax, d, P(L.dGT), P(L.XT), dw_gate, Pi(L.kofs), split,
-                       split_bytes, stream));
+                       split_bytes, stream, accumulate));
   MOE_TRY(grouped_gemm(E, nullptr, F, (long long)E * F, Kmax, d, P(L.dUT), P(L.XT), dw_up, Pi(L.kofs), split,
-                       split_bytes, stream));
+                       split_bytes, stream, accumulate));
   // ---- shared experts: every token, weight 1
   if (S > 0) {
     const int RS = S * N, KS = (int)L.KSmax;
@@ -634,18 +636,18 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
     MOE_TRY(launch_transpose_padded(P(L.dGUs), 2 * Fs, Fs, Fs, nullptr, N, 0, Pi(L.kofs_s), S, P(L.dUsT), KS, stream));
     MOE_TRY(launch_transpose_padded(P(L.Xs), d, 0, d, nullptr, N, 0, Pi(L.kofs_s), S, P(L.XsT), KS, stream));
     MOE_TRY(grouped_gemm(S, nullptr, d, (long long)S * d, KS, Fs, P(L.dOsT), P(L.hsT), ds_down, Pi(L.kofs_s), split,
-                         split_bytes, stream));
+                         split_bytes, stream, accumulate));
     MOE_TRY(grouped_gemm(S, nullptr, Fs, (long long)S * Fs, KS, d, P(L.dGsT), P(L.XsT), ds_gate, Pi(L.kofs_s), split,
-                         split_bytes, stream));
+                         split_bytes, stream, accumulate));
     MOE_TRY(grouped_gemm(S, nullptr, Fs, (long long)S * Fs, KS, d, P(L.dUsT), P(L.XsT), ds_up, Pi(L.kofs_s), split,
-                         split_bytes, stream));
+                         split_bytes, stream, accumulate));
   }
   // ---- router and dx
   int splits = 1;
   MOE_TRY(launch_router_logits(s, x, w_router, Pf(L.logits), &splits, stream));
   MOE_TRY(launch_router_backward(s, Pf(L.logits), splits, logit_bias, topk_idx, topk_w, Pf(L.dw), counts, aux_coef,
                                  Pf(L.dl), stream));
-  MOE_TRY(launch_router_wgrad(Pf(L.dl), x, N, E, d, Pf(L.rpart), dw_router, d_logit_bias, stream));
+  MOE_TRY(launch_router_wgrad(Pf(L.dl), x, N, E, d, Pf(L.rpart), dw_router, d_logit_bias, accumulate, stream));
   MOE_TRY(launch_dx(Pf(L.dXr), slot_pos, S > 0 ? Pf(L.dXs) : nullptr, S, Pf(L.dl), w_router, N, E, k, d, dx, stream));
 #undef MOE_TRY
   return MOE_OK;

@@ -88,6 +88,9 @@ struct SegSet {
   // k - b_split. b_split is a multiple of 64.
   int32_t b_nmajor;
   int32_t b_split;
+  // Phase 2: add the products to out instead of writing them; with k_offsets,
+  // a group whose K range is empty then leaves its rows untouched.
+  int32_t accumulate;
 };
 
 struct GroupedParams {
@@ -138,7 +141,7 @@ int launch_router_backward(const moe_shape& s, const float* logits, int splits, 
 int router_wgrad_splits(int N);
 size_t router_wgrad_part_floats(int N, int E, int d);
 int launch_router_wgrad(const float* dl, const void* x, int N, int E, int d, float* part, float* dwr, float* dlb,
-                        hipStream_t st);
+                        int accumulate, hipStream_t st);
 int launch_dx(const float* dXr, const int32_t* slot_pos, const float* dXs, int S, const float* dl, const void* wr,
               int N, int E, int k, int d, float* dx, hipStream_t st);
 int launch_fill_f32(float* p, size_t n, float v, hipStream_t st);

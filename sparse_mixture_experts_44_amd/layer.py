@@ -167,21 +167,27 @@ class MoELayer:
                       o.balance_stat, self.ws, stage_events=stage_events, stream=stream)
         return o
 
-    def backward(self, x: torch.Tensor, dy: torch.Tensor, aux_coef: float = 0.0, stream=None) -> Grads:
+    def backward(self, x: torch.Tensor, dy: torch.Tensor, aux_coef: float = 0.0, accumulate: bool = False,
+                 stream=None) -> Grads:
         """Gradients (moe_backward) of sum(dy * y) + aux_coef * balance statistic for the last
         forward(x) of this bf16 layer, whose routing in self.out it reuses. The gradient buffers
-        and the backward workspace are allocated on first use and reused."""
+        and the backward workspace are allocated on first use and reused. accumulate: add the
+        weight gradients to the buffers (which start as zeros) instead of overwriting them;
+        dx is always overwritten."""
         if self.fp8 is not None or self.int4 is not None:
             raise ValueError("the backward pass needs the bf16 expert weights")
         if x.shape[0] != self.shape.n_tokens or tuple(dy.shape) != (self.shape.n_tokens, self.shape.d_model):
             raise ValueError("x and dy must match the last forward's tokens")
         if self.grads is None:
             self.grads = Grads.empty(self.shape, self.device)
+            for t in vars(self.grads).values():
+                if t is not None:
+                    t.zero_()
             self.bws = torch.empty(max(1, N.backward_workspace_bytes(self.shape)), dtype=torch.uint8,
                                    device=self.device)
         g, o = self.grads, self.out
         N.moe_backward(self.shape, x, self.w_router, self.logit_bias, self.w_gate, self.w_up, self.w_down,
                        self.s_gate, self.s_up, self.s_down, o.topk_idx, o.topk_w, o.counts, o.offsets, o.perm,
-                       o.slot_pos, dy, aux_coef, g.dx, g.dw_router, g.d_logit_bias, g.dw_gate, g.dw_up,
+                       o.slot_pos, dy, aux_coef, accumulate, g.dx, g.dw_router, g.d_logit_bias, g.dw_gate, g.dw_up,
                        g.dw_down, g.ds_gate, g.ds_up, g.ds_down, self.bws, stream=stream)
         return g

@@ -167,11 +167,13 @@ def test_backward_entry_point_validates():
     s = shp()
     assert moe.backward_workspace_bytes(s) > moe.workspace_bytes(s)
     s32 = shp(dtype=N.MOE_DTYPE_F32)
-    bw = lambda shape, aux=0.0, ws_bytes=1 << 40, ptr=FAKE: L.moe_backward(
+    bw = lambda shape, aux=0.0, ws_bytes=1 << 40, ptr=FAKE, acc=0: L.moe_backward(
         ctypes.byref(shape), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE,
-        FAKE, FAKE, ctypes.c_double(aux), ptr, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE, ws_bytes, None)
+        FAKE, FAKE, ctypes.c_double(aux), acc, ptr, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE, ws_bytes,
+        None)
     assert bw(s32) == N.MOE_ERR_UNSUPPORTED
     assert bw(s, aux=float("nan")) == N.MOE_ERR_INVALID_ARG
+    assert bw(s, acc=2) == N.MOE_ERR_INVALID_ARG                       # accumulate is 0 or 1
     assert bw(s, ptr=None) == N.MOE_ERR_INVALID_ARG                    # dx missing
     assert bw(shp(n_shared=1, d_ff_shared=128)) == N.MOE_ERR_INVALID_ARG  # shared gradients missing
     assert bw(s, ws_bytes=16) == N.MOE_ERR_WORKSPACE

@@ -102,7 +102,7 @@ def routed_rows(cfg, layer, x64, idx):
     return rows_of
 
 
-def run_backward(cfg, layer, x, dy, aux, experts=None):
+def run_backward(cfg, layer, x, dy, aux, experts=None, accumulate_onto=None):
     """GPU forward then backward; host copies of the forward's top-k and of the gradients
     (with `experts` given: of those experts' weight gradients only, plus `zero_experts`, the
     experts with no kept copy whose gradients are not all exactly zero)."""
@@ -118,11 +118,15 @@ def run_backward(cfg, layer, x, dy, aux, experts=None):
              dw_down=nan(E, d, F))
     if S:
         g.update(ds_gate=nan(S, Fs, d), ds_up=nan(S, Fs, d), ds_down=nan(S, d, Fs))
+    if accumulate_onto is not None:  # accumulate mode: the weight gradients start from these values
+        for name, a in accumulate_onto.items():
+            g[name].copy_(torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)))
     ws = torch.empty(moe.backward_workspace_bytes(shape), dtype=torch.uint8, device=DEV)
     dyd = torch.from_numpy(np.ascontiguousarray(dy, dtype=np.float32)).to(DEV)
     log(f"{cfg.name}: moe_backward N={N} E={E} k={cfg.top_k} d={d} F={F} S={S} C={cfg.capacity} aux={aux}")
     moe.moe_backward(shape, xd, L.w_router, L.logit_bias, L.w_gate, L.w_up, L.w_down, L.s_gate, L.s_up, L.s_down,
-                     o.topk_idx, o.topk_w, o.counts, o.offsets, o.perm, o.slot_pos, dyd, aux, g["dx"],
+                     o.topk_idx, o.topk_w, o.counts, o.offsets, o.perm, o.slot_pos, dyd, aux,
+                     int(accumulate_onto is not None), g["dx"],
                      g["dw_router"], g["d_logit_bias"], g["dw_gate"], g["dw_up"], g["dw_down"], g.get("ds_gate"),
                      g.get("ds_up"), g.get("ds_down"), ws)
     torch.cuda.synchronize()
@@ -259,3 +263,26 @@ def test_backward_full_size_sampled(name):
     assert abs(lb.sum()) <= 1e-5 * np.sum(np.abs(lb))
     assert np.all(np.abs(wr.sum(axis=0)) <= 1e-5 * np.sum(np.abs(wr), axis=0) + 1e-30)
     log(f"{name}: sampled gradients within bounds [{time.time() - t:.1f}s]")
+
+
+def test_backward_accumulate_adds_to_the_buffers():
+    """accumulate = 1: every weight gradient buffer ends as its start value plus the gradient of
+    the write mode, entry by entry (one fp32 addition: exact up to its rounding); an expert with
+    no kept copy keeps its start value bit for bit; dx is overwritten."""
+    cfg = mi.small_config("bwd_acc", dtype="bf16", layer_id=813, x_id=813, n_tokens=300, n_experts=64, top_k=2,
+                          d_model=128, d_ff=192, n_shared=1, d_ff_shared=64, capacity=30, select_bias=0.1)
+    layer, x = mi.make_layer(cfg), mi.make_x(cfg)
+    dy = make_dy(cfg.n_tokens, cfg.d_model, 5)
+    ref = run_backward(cfg, layer, x, dy, 0.25)
+    rng = np.random.default_rng(9)
+    names = ("dw_router", "d_logit_bias", "dw_gate", "dw_up", "dw_down", "ds_gate", "ds_up", "ds_down")
+    start = {n: rng.standard_normal(np.shape(ref[n])).astype(np.float32) for n in names}
+    got = run_backward(cfg, layer, x, dy, 0.25, accumulate_onto=start)
+    np.testing.assert_array_equal(got["dx"], ref["dx"])
+    for n in names:
+        expect = start[n] + ref[n]   # fp32 + fp32, the addition the library performs
+        np.testing.assert_array_equal(got[n].view(np.uint32), expect.view(np.uint32), err_msg=n)
+    idle = np.flatnonzero(ref["counts"] == 0)
+    assert len(idle) > 0, "the case must have an expert with no copy"
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        np.testing.assert_array_equal(got[n][idle].view(np.uint32), start[n][idle].view(np.uint32), err_msg=n)
