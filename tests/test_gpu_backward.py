@@ -166,6 +166,7 @@ def oracle_grads(cfg, layer, x, dy, aux, idx):
     (dict(n_tokens=129, n_experts=8, top_k=1, d_model=64, d_ff=64, renormalize=False, capacity=12), 0.0),
     (dict(n_tokens=64, n_experts=256, top_k=8, d_model=256, d_ff=128, n_shared=1, d_ff_shared=128,
           select_bias=0.1), 0.2),                                                    # 256 experts, top-8
+    (dict(n_tokens=400, n_experts=32, top_k=1, d_model=128, d_ff=256, logit_skew=1.5, capacity=16), 0.05),
 ])
 def test_backward_small_layers_every_element(kw, aux):
     cfg = mi.small_config("bwd", dtype="bf16", layer_id=800 + kw["n_tokens"] % 11, x_id=800, **kw)
