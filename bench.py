@@ -133,14 +133,27 @@ def time_backward(L, xd, cfg, steps, warmup, kept):
         return ev.elapsed_ms(0, 1) / steps
 
     ms, ms_acc = timed(False), timed(True)
+    # training forward (keeps G and U), then the backward that reads them
+    for _ in range(max(1, warmup)):  # the first call also allocates the G, U buffer
+        L.forward(xd, save_for_backward=True)
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    ev.record(0, stream)
+    for _ in range(steps):
+        L.forward(xd, save_for_backward=True)
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    ms_fwd_train = ev.elapsed_ms(0, 1) / steps
+    ms_saved = timed(False)
     w = backward_work(cfg, kept)
     tf = w["flops_algorithmic"] / (ms * 1e-3) / 1e12
     return {"ms": ms, "steps": steps, "tflops_algorithmic": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
             "tflops_executed": w["flops_executed"] / (ms * 1e-3) / 1e12, **w,
-            "ms_accumulate": ms_acc,
+            "ms_accumulate": ms_acc, "forward_train_ms": ms_fwd_train, "ms_with_saved_gate_up": ms_saved,
             "note": "moe_backward alone (gradients of x, W_r, logit bias, every expert weight), writing the "
-                    "gradients (ms) or adding them to fp32 buffers (ms_accumulate); algorithmic FLOPs exclude "
-                    "the G, U and logit recompute"}
+                    "gradients (ms) or adding them to fp32 buffers (ms_accumulate); forward_train_ms: "
+                    "moe_forward_train, which keeps G and U; ms_with_saved_gate_up: the backward reading them; "
+                    "algorithmic FLOPs exclude the G, U and logit recompute"}
 
 
 class HipEvents:

@@ -184,6 +184,25 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router,
                 double* prob_sum, double* balance_stat,
                 void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
 
+/* Training forward: moe_forward (bf16 layers) that also keeps, in the
+ * caller's gu_save, the fp32 gate and up values G = x W_gate^T and
+ * U = x W_up^T of every computed row, for moe_backward (which then skips
+ * recomputing them). gu_save holds moe_train_save_floats(shape) floats:
+ * routed G [N*k, F] then routed U [N*k, F], rows in the grouped order of
+ * perm (rows at or past offsets[E] are not written); then each shared
+ * expert's G [S*N, Fs] then U [S*N, Fs] (shared expert s at rows s*N..).
+ * Everything else as in moe_forward. Errors: MOE_ERR_UNSUPPORTED unless the
+ * dtype is MOE_DTYPE_BF16; MOE_ERR_INVALID_ARG when gu_save is NULL and N > 0. */
+size_t moe_train_save_floats(const moe_shape* shape);
+int moe_forward_train(const moe_shape* shape, const void* x, const void* w_router,
+                      const float* logit_bias, const float* select_bias,
+                      const void* w_gate, const void* w_up, const void* w_down,
+                      const void* s_gate, const void* s_up, const void* s_down,
+                      float* y, int32_t* topk_idx, float* topk_w,
+                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
+                      double* prob_sum, double* balance_stat, float* gu_save,
+                      void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
+
 /* ---------------------------------------------------------------------
  * Training-side router statistics (side outputs; the forward needs none).
  * The pages' formulas for these were lost in extraction; each call states
@@ -343,7 +362,9 @@ size_t moe_backward_workspace_bytes(const moe_shape* shape);
 
 /* Inputs: the layer's bf16 weights as passed to moe_forward; the forward's
  * outputs topk_idx [N, k], topk_w [N, k], counts [E], offsets [E+1], perm
- * [N*k], slot_pos [N*k] (unchanged since that call); dy [N, d] fp32, read at
+ * [N*k], slot_pos [N*k] (unchanged since that call); gu_saved: the gu_save
+ * buffer of a moe_forward_train call with the same inputs (NULL: G and U are
+ * recomputed); dy [N, d] fp32, read at
  * bf16 precision (every use goes through its round-to-nearest-even bf16
  * value, so bf16-valued dy loses nothing); aux_coef (finite; 0 drops the
  * balance term); accumulate (0 or 1, below).
@@ -363,7 +384,7 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
                  const void* w_gate, const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
                  const void* s_down, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
                  const int32_t* offsets, const int32_t* perm, const int32_t* slot_pos, const float* dy,
-                 double aux_coef, int32_t accumulate, float* dx, float* dw_router, float* d_logit_bias,
+                 const float* gu_saved, double aux_coef, int32_t accumulate, float* dx, float* dw_router, float* d_logit_bias,
                  float* dw_gate, float* dw_up, float* dw_down, float* ds_gate, float* ds_up, float* ds_down, void* ws,
                  size_t ws_bytes, hipStream_t stream);
 

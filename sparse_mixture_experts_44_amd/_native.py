@@ -64,6 +64,9 @@ _SIGS = {
     "moe_forward": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "moe_quantize_fp8": (ctypes.c_int, [ctypes.c_int64, _I, _P, _P, _P, _P]),
+    "moe_train_save_floats": (_SZ, [_SHP]),
+    "moe_forward_train": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "moe_router_aux": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_update_select_bias": (ctypes.c_int, [_SHP, _P, ctypes.c_float, _P, _P]),
     "moe_grouped_swiglu_fp8": (ctypes.c_int, [_SHP, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P,
@@ -73,7 +76,7 @@ _SIGS = {
                                        _P, _P, _P, _SZ, _P, _P]),
     "moe_quantize_int4": (ctypes.c_int, [ctypes.c_int64, _I, _P, _P, _P, _P]),
     "moe_backward_workspace_bytes": (_SZ, [_SHP]),
-    "moe_backward": (ctypes.c_int, [_SHP] + [_P] * 16 + [ctypes.c_double, _I] + [_P] * 10 + [_SZ, _P]),
+    "moe_backward": (ctypes.c_int, [_SHP] + [_P] * 17 + [ctypes.c_double, _I] + [_P] * 10 + [_SZ, _P]),
     "moe_grouped_swiglu_int4": (ctypes.c_int, [_SHP, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P, _P, _P,
                                                _P, _P, _P, _SZ, _P]),
     "moe_forward_int4": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -174,6 +177,27 @@ def moe_forward(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_dow
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)))
 
 
+def train_save_floats(shape: MoEShape) -> int:
+    return int(lib().moe_train_save_floats(ctypes.byref(shape)))
+
+
+def moe_forward_train(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
+                      s_down, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
+                      balance_stat, gu_save, ws, stage_events: Optional[Sequence[int]] = None, stream=None):
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != MOE_STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {MOE_STAGE_EVENTS} hipEvent_t handles")
+        ev = (ctypes.c_void_p * MOE_STAGE_EVENTS)(*stage_events)
+    _check("moe_forward_train", lib().moe_forward_train(
+        ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias),
+        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(slot_pos),
+        _ptr(prob_sum), _ptr(balance_stat), _ptr(gu_save), _ptr(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0,
+        ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)))
+
+
 def moe_quantize_fp8(rows, cols, w_bf16, codes, scales, stream=None):
     _check("moe_quantize_fp8", lib().moe_quantize_fp8(
         int(rows), int(cols), _ptr(w_bf16), _ptr(codes), _ptr(scales), _stream(stream)))
@@ -263,12 +287,13 @@ def backward_workspace_bytes(shape: MoEShape) -> int:
 
 
 def moe_backward(shape, x, w_router, logit_bias, w_gate, w_up, w_down, s_gate, s_up, s_down, topk_idx, topk_w,
-                 counts, offsets, perm, slot_pos, dy, aux_coef, accumulate, dx, dw_router, d_logit_bias, dw_gate,
-                 dw_up, dw_down, ds_gate, ds_up, ds_down, ws, stream=None):
+                 counts, offsets, perm, slot_pos, dy, gu_saved, aux_coef, accumulate, dx, dw_router, d_logit_bias,
+                 dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, ws, stream=None):
     _check("moe_backward", lib().moe_backward(
         ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
         _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
-        _ptr(perm), _ptr(slot_pos), _ptr(dy), float(aux_coef), int(accumulate), _ptr(dx), _ptr(dw_router),
+        _ptr(perm), _ptr(slot_pos), _ptr(dy), _ptr(gu_saved), float(aux_coef), int(accumulate), _ptr(dx),
+        _ptr(dw_router),
         _ptr(d_logit_bias),
         _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ds_gate), _ptr(ds_up), _ptr(ds_down), _ptr(ws),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))

@@ -56,6 +56,8 @@ struct SetView {  // the fields of one SegSet, picked with selects rather than a
   const int32_t* kofs;  // weight-gradient mode (phase 2): per-group K ranges
   int32_t bsplit;       // N-major weights: rows >= bsplit come from wu (0: none)
   int32_t accum;        // phase 2: out += product
+  float* gsave;         // phase 1: fp32 gate and up values (optional)
+  float* usave;
 };
 
 __device__ __forceinline__ SetView pick(const GroupedParams& p, int si) {
@@ -74,6 +76,8 @@ __device__ __forceinline__ SetView pick(const GroupedParams& p, int si) {
   v.kofs = si ? p.set[1].k_offsets : p.set[0].k_offsets;
   v.bsplit = si ? p.set[1].b_split : p.set[0].b_split;
   v.accum = si ? p.set[1].accumulate : p.set[0].accumulate;
+  v.gsave = si ? p.set[1].g_save : p.set[0].g_save;
+  v.usave = si ? p.set[1].u_save : p.set[0].u_save;
   return v;
 }
 
@@ -367,7 +371,7 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int G, long long cap_
 // multiplied by its weight row's scale, and with int4 weights the offset
 // sums corr[i] (136 * sum(x) of each row) are subtracted before that (none
 // when corr is NULL: the K-parts of split tiles are stored already reduced).
-template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, int FM, int NB>
+template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE, int FM, int NB>
 __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetView& S, const TileGeom& t,
                                            int d, int lane, int wm, int wn, const f32x16_t* corr = nullptr) {
   constexpr bool WS = WQ != 0, W4 = WQ == 4;
@@ -432,6 +436,14 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
         if constexpr (W4) c = corr ? corr[i][v] : 0.f;
         if constexpr (P1) {
           bf16_t* hrow = static_cast<bf16_t*>(S.h) + row * F + col0;
+          if constexpr (SAVE) {  // training: keep the gate and up values for the backward pass
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              if (col0 + j * 32 < ncols) {
+                S.gsave[row * F + col0 + j * 32] = acc[i][j][v];
+                S.usave[row * F + col0 + j * 32] = acc[i][j + FN][v];
+              }
+          }
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             if (col0 + j * 32 < ncols)
@@ -468,7 +480,7 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
 // so that fewer copies queue at once behind the barrier (3-5% faster on
 // 256 x 256 tiles; the second half of the step still covers their latency).
 template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB, int WQ, bool P1, bool SPREAD,
-          bool NMAJ = false>
+          bool NMAJ = false, bool SAVE = false>
 __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(GroupedParams p) {
   constexpr bool W8 = WQ == 8, W4 = WQ == 4, WS = WQ != 0;
   using BT = typename std::conditional<WS, uint8_t, bf16_t>::type;  // weight storage unit
@@ -763,7 +775,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
             dst[((i * NB + j) * 16 + v) * NT + tid] = W4 ? acc[i][j][v] - corr[i][v] : acc[i][j][v];
       continue;
     }
-    store_tile<BM, BN, WGM, WGN, WQ, P1>(acc, S, tg, d, lane, wm, wn, corr);
+    store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE>(acc, S, tg, d, lane, wm, wn, corr);
   }
 }
 
@@ -786,7 +798,7 @@ __global__ __launch_bounds__(256) void split_sum_kernel(float* __restrict__ ws) 
 // The epilogue of the split tail tiles of the launch before it (same
 // parameters, `main_grid` workgroups), from part 0: workgroup b finishes
 // tail tile b. Workgroups past the tail exit.
-template <int BM, int BN, int WGM, int WGN, int WQ, bool P1>
+template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedParams p, int main_grid) {
   constexpr int TM = BM / WGM, FM = TM / 32;
   constexpr int BH = P1 ? BN / 2 : BN;
@@ -817,7 +829,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedPar
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = src[((size_t)(i * NB + j) * 16 + v) * NT];
-  store_tile<BM, BN, WGM, WGN, WQ, P1>(acc, S, tg, d, lane, wm, wn);
+  store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE>(acc, S, tg, d, lane, wm, wn);
 }
 
 // =====================================================================  fp32 SIMT
@@ -934,9 +946,15 @@ template <int BM, int BN, int BK, int WGM, int WGN, int NS, int WQ, bool SPREAD 
 void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) {
   const int BH = phase == 1 ? BN / 2 : BN;
   const int grid = grid_for(tiles_upper_bound(p, phase, BM, BH), per_cu);
+  // the training forward (bf16 phase 1 with g_save) runs its own instantiation: the
+  // inference kernels keep their code unchanged
+  const bool save = WQ == 0 && phase == 1 && p.set[0].g_save;
   if constexpr (NMAJ)
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, true>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
+  else if (phase == 1 && save)
+    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD, false, WQ == 0>),
+                       dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
   else if (phase == 1)
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
@@ -945,7 +963,10 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
                        dim3(WGM * WGN * 64), 0, st, p);
   if (p.split_ws && p.split_cap > kSplitHeader) {
     hipLaunchKernelGGL(split_sum_kernel<BM * BN>, dim3(1024), dim3(256), 0, st, p.split_ws);
-    if (phase == 1)
+    if (phase == 1 && save)
+      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, true, WQ == 0>), dim3(grid),
+                         dim3(WGM * WGN * 64), 0, st, p, grid);
+    else if (phase == 1)
       hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, true>), dim3(grid), dim3(WGM * WGN * 64),
                          0, st, p, grid);
     else

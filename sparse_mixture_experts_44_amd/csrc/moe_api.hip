@@ -374,7 +374,8 @@ static int forward_impl(const moe_shape* shape, const void* x, const void* w_rou
                         const void* s_down, int wq, const moe_weight_scales* sc, float* y, int32_t* topk_idx,
                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* slot_pos, double* prob_sum, double* balance_stat, void* ws,
-                        size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+                        size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream,
+                        float* gu_save = nullptr) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
@@ -429,6 +430,10 @@ static int forward_impl(const moe_shape* shape, const void* x, const void* w_rou
     }
     R.h = at(ws, L.h_routed);
     R.out = O;
+    if (gu_save) {  // [NK, F] gate, [NK, F] up, then the shared experts' [S N, Fs] each
+      R.g_save = gu_save;
+      R.u_save = gu_save + NK * s.d_ff;
+    }
     if (s.n_shared > 0) {
       SegSet& Sh = p.set[1];
       Sh.offsets = nullptr;
@@ -448,6 +453,11 @@ static int forward_impl(const moe_shape* shape, const void* x, const void* w_rou
       }
       Sh.h = at(ws, L.h_shared);
       Sh.out = O_shared;
+      if (gu_save) {
+        const size_t SN = (size_t)s.n_shared * s.n_tokens;
+        Sh.g_save = gu_save + 2 * NK * s.d_ff;
+        Sh.u_save = Sh.g_save + SN * s.d_ff_shared;
+      }
     }
     if ((st = launch_grouped(p, 1, stream))) return st;
   }
@@ -469,6 +479,27 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router, con
   return forward_impl(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
                       s_down, 0, nullptr, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
                       balance_stat, ws, ws_bytes, stage_events, stream);
+}
+
+size_t moe_train_save_floats(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  const moe_shape& s = *shape;
+  return 2 * ((size_t)s.n_tokens * s.top_k * s.d_ff + (size_t)s.n_shared * s.n_tokens * (s.n_shared ? s.d_ff_shared : 0));
+}
+
+int moe_forward_train(const moe_shape* shape, const void* x, const void* w_router, const float* logit_bias,
+                      const float* select_bias, const void* w_gate, const void* w_up, const void* w_down,
+                      const void* s_gate, const void* s_up, const void* s_down, float* y,
+                      int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                      int32_t* slot_pos, double* prob_sum, double* balance_stat, float* gu_save, void* ws,
+                      size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (shape->n_tokens > 0 && !gu_save) return MOE_ERR_INVALID_ARG;
+  return forward_impl(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
+                      s_down, 0, nullptr, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
+                      balance_stat, ws, ws_bytes, stage_events, stream, shape->n_tokens > 0 ? gu_save : nullptr);
 }
 
 static int forward_quantised(int wq, const moe_shape* shape, const void* x, const void* w_router,
@@ -554,7 +585,7 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
                  const void* w_gate, const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
                  const void* s_down, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
                  const int32_t* offsets, const int32_t* perm, const int32_t* slot_pos, const float* dy,
-                 double aux_coef, int32_t accumulate, float* dx, float* dw_router, float* d_logit_bias,
+                 const float* gu_saved, double aux_coef, int32_t accumulate, float* dx, float* dw_router, float* d_logit_bias,
                  float* dw_gate, float* dw_up, float* dw_down, float* ds_gate, float* ds_up, float* ds_down, void* ws,
                  size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
@@ -592,12 +623,17 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
   // ---- routed experts
   MOE_TRY(launch_fill_f32(Pf(L.dw), (size_t)N * k, 0.f, stream));  // dropped copies keep 0
   MOE_TRY(launch_gather_rows(x, dy, topk_w, perm, n_kept, k, d, R, P(L.Xg), P(L.dYg), P(L.dO), stream));
-  MOE_TRY(grouped_gemm(E, offsets, 0, R, d, F, P(L.Xg), w_gate, Pf(L.G), nullptr, split, split_bytes, stream));
-  MOE_TRY(grouped_gemm(E, offsets, 0, R, d, F, P(L.Xg), w_up, Pf(L.U), nullptr, split, split_bytes, stream));
+  // G and U: kept by the training forward, or recomputed
+  const float* G = gu_saved ? gu_saved : Pf(L.G);
+  const float* U = gu_saved ? gu_saved + (size_t)R * F : Pf(L.U);
+  if (!gu_saved) {
+    MOE_TRY(grouped_gemm(E, offsets, 0, R, d, F, P(L.Xg), w_gate, Pf(L.G), nullptr, split, split_bytes, stream));
+    MOE_TRY(grouped_gemm(E, offsets, 0, R, d, F, P(L.Xg), w_up, Pf(L.U), nullptr, split, split_bytes, stream));
+  }
   // dH' = dy Wd: w_down [E, d, F] is read as d rows of F values
   MOE_TRY(grouped_gemm_nmajor(E, offsets, 0, R, d, F, P(L.dYg), w_down, nullptr, 0, Pf(L.dHp), split, split_bytes,
                               stream));
-  MOE_TRY(launch_swiglu_backward(Pf(L.G), Pf(L.U), Pf(L.dHp), topk_w, perm, n_kept, R, F, P(L.h), P(L.dGU),
+  MOE_TRY(launch_swiglu_backward(G, U, Pf(L.dHp), topk_w, perm, n_kept, R, F, P(L.h), P(L.dGU),
                                  Pf(L.dw), stream));
   // dX = [dG | dU] [Wg ; Wu]: rows k < F of the operand are w_gate's, the rest w_up's
   MOE_TRY(grouped_gemm_nmajor(E, offsets, 0, R, 2 * F, d, P(L.dGU), w_gate, w_up, F, Pf(L.dXr), split, split_bytes,
@@ -621,11 +657,16 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
       MOE_TRY(launch_gather_rows(x, dy, nullptr, nullptr, nullptr, 1, d, N,
                                  static_cast<uint8_t*>(P(L.Xs)) + (size_t)q * N * d * 2,
                                  static_cast<uint8_t*>(P(L.dYs)) + (size_t)q * N * d * 2, nullptr, stream));
-    MOE_TRY(grouped_gemm(S, nullptr, N, RS, d, Fs, P(L.Xs), s_gate, Pf(L.Gs), nullptr, split, split_bytes, stream));
-    MOE_TRY(grouped_gemm(S, nullptr, N, RS, d, Fs, P(L.Xs), s_up, Pf(L.Us), nullptr, split, split_bytes, stream));
+    const float* Gs = gu_saved ? gu_saved + 2 * (size_t)R * F : Pf(L.Gs);
+    const float* Us = gu_saved ? Gs + (size_t)RS * Fs : Pf(L.Us);
+    if (!gu_saved) {
+      MOE_TRY(grouped_gemm(S, nullptr, N, RS, d, Fs, P(L.Xs), s_gate, Pf(L.Gs), nullptr, split, split_bytes,
+                           stream));
+      MOE_TRY(grouped_gemm(S, nullptr, N, RS, d, Fs, P(L.Xs), s_up, Pf(L.Us), nullptr, split, split_bytes, stream));
+    }
     MOE_TRY(grouped_gemm_nmajor(S, nullptr, N, RS, d, Fs, P(L.dYs), s_down, nullptr, 0, Pf(L.dHs), split,
                                 split_bytes, stream));
-    MOE_TRY(launch_swiglu_backward(Pf(L.Gs), Pf(L.Us), Pf(L.dHs), nullptr, nullptr, nullptr, RS, Fs, P(L.hs),
+    MOE_TRY(launch_swiglu_backward(Gs, Us, Pf(L.dHs), nullptr, nullptr, nullptr, RS, Fs, P(L.hs),
                                    P(L.dGUs), nullptr, stream));
     MOE_TRY(grouped_gemm_nmajor(S, nullptr, N, RS, 2 * Fs, d, P(L.dGUs), s_gate, s_up, Fs, Pf(L.dXs), split,
                                 split_bytes, stream));

@@ -74,6 +74,8 @@ struct SegSet {
   const float* sc_up;      // [G, d_ff]
   const float* sc_down;    // [G, d]
   void* h;                 // [max_rows, d_ff]: gate|up output, down input
+  float* g_save;           // phase 1, bf16 weights, optional: [max_rows, d_ff] fp32 gate values (x W_gate^T)
+  float* u_save;           //   and up values, beside h, for the backward pass
   float* out;              // [max_rows, d]
   // Weight-gradient mode (phase 2 only, bf16): when set, group g multiplies
   // h and w_down over the K range [k_offsets[g], k_offsets[g+1]) (multiples

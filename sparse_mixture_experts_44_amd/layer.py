@@ -103,6 +103,8 @@ class MoELayer:
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.out = Outputs.empty(s.n_tokens, s.d_model, s.n_experts, s.top_k, self.device)
         self.grads = self.bws = None
+        self.gu = None          # fp32 G and U kept by a training forward (moe_forward_train)
+        self.gu_valid = False   # whether self.gu belongs to the last forward
 
     fp8 = None   # after quantize_fp8(): codes and row scales of every expert weight
     int4 = None  # after quantize_int4(): packed codes and row scales of every expert weight
@@ -145,11 +147,26 @@ class MoELayer:
         self.int4 = self._quantize("int4", keep_bf16)
         return self.int4
 
-    def forward(self, x: torch.Tensor, stage_events=None, stream=None) -> Outputs:
+    def forward(self, x: torch.Tensor, stage_events=None, stream=None, save_for_backward: bool = False) -> Outputs:
+        """save_for_backward (bf16 layers): run moe_forward_train, which also keeps the fp32 gate and up
+        values for backward() (which then skips recomputing them)."""
         if x.shape[0] != self.shape.n_tokens:
             self.shape.n_tokens = x.shape[0]
             self._alloc()
         o = self.out
+        self.gu_valid = False
+        if save_for_backward:
+            if self.fp8 is not None or self.int4 is not None:
+                raise ValueError("save_for_backward needs the bf16 expert weights")
+            if self.gu is None:
+                self.gu = torch.empty(max(1, N.train_save_floats(self.shape)), dtype=torch.float32,
+                                      device=self.device)
+            N.moe_forward_train(self.shape, x, self.w_router, self.logit_bias, self.select_bias, self.w_gate,
+                                self.w_up, self.w_down, self.s_gate, self.s_up, self.s_down, o.y, o.topk_idx,
+                                o.topk_w, o.counts, o.offsets, o.perm, o.slot_pos, o.prob_sum, o.balance_stat,
+                                self.gu, self.ws, stage_events=stage_events, stream=stream)
+            self.gu_valid = True
+            return o
         if self.fp8 is not None or self.int4 is not None:
             q = self.fp8 if self.fp8 is not None else self.int4
             fwd = N.moe_forward_fp8 if self.fp8 is not None else N.moe_forward_int4
@@ -170,10 +187,10 @@ class MoELayer:
     def backward(self, x: torch.Tensor, dy: torch.Tensor, aux_coef: float = 0.0, accumulate: bool = False,
                  stream=None) -> Grads:
         """Gradients (moe_backward) of sum(dy * y) + aux_coef * balance statistic for the last
-        forward(x) of this bf16 layer, whose routing in self.out it reuses. The gradient buffers
-        and the backward workspace are allocated on first use and reused. accumulate: add the
-        weight gradients to the buffers (which start as zeros) instead of overwriting them;
-        dx is always overwritten."""
+        forward(x) of this bf16 layer, whose routing in self.out it reuses (and its saved gate and up
+        values, after forward(..., save_for_backward=True)). The gradient buffers and the backward
+        workspace are allocated on first use and reused. accumulate: add the weight gradients to the
+        buffers (which start as zeros) instead of overwriting them; dx is always overwritten."""
         if self.fp8 is not None or self.int4 is not None:
             raise ValueError("the backward pass needs the bf16 expert weights")
         if x.shape[0] != self.shape.n_tokens or tuple(dy.shape) != (self.shape.n_tokens, self.shape.d_model):
@@ -188,6 +205,7 @@ class MoELayer:
         g, o = self.grads, self.out
         N.moe_backward(self.shape, x, self.w_router, self.logit_bias, self.w_gate, self.w_up, self.w_down,
                        self.s_gate, self.s_up, self.s_down, o.topk_idx, o.topk_w, o.counts, o.offsets, o.perm,
-                       o.slot_pos, dy, aux_coef, accumulate, g.dx, g.dw_router, g.d_logit_bias, g.dw_gate, g.dw_up,
-                       g.dw_down, g.ds_gate, g.ds_up, g.ds_down, self.bws, stream=stream)
+                       o.slot_pos, dy, self.gu if self.gu_valid else None, aux_coef, accumulate, g.dx,
+                       g.dw_router, g.d_logit_bias, g.dw_gate, g.dw_up, g.dw_down, g.ds_gate, g.ds_up, g.ds_down,
+                       self.bws, stream=stream)
         return g

@@ -169,8 +169,8 @@ def test_backward_entry_point_validates():
     s32 = shp(dtype=N.MOE_DTYPE_F32)
     bw = lambda shape, aux=0.0, ws_bytes=1 << 40, ptr=FAKE, acc=0: L.moe_backward(
         ctypes.byref(shape), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE,
-        FAKE, FAKE, ctypes.c_double(aux), acc, ptr, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE, ws_bytes,
-        None)
+        FAKE, FAKE, None, ctypes.c_double(aux), acc, ptr, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE,
+        ws_bytes, None)
     assert bw(s32) == N.MOE_ERR_UNSUPPORTED
     assert bw(s, aux=float("nan")) == N.MOE_ERR_INVALID_ARG
     assert bw(s, acc=2) == N.MOE_ERR_INVALID_ARG                       # accumulate is 0 or 1
@@ -194,3 +194,16 @@ def test_router_aux_entry_points_validate():
     assert up(s, FAKE, -1.0, FAKE) == N.MOE_ERR_INVALID_ARG
     assert up(s, FAKE, float("nan"), FAKE) == N.MOE_ERR_INVALID_ARG
     assert up(s, FAKE, float("inf"), FAKE) == N.MOE_ERR_INVALID_ARG
+
+
+def test_train_forward_entry_point_validates():
+    L = moe.lib()
+    s = shp(n_shared=1, d_ff_shared=128)
+    assert moe.train_save_floats(s) == 2 * (s.n_tokens * s.top_k * s.d_ff + s.n_tokens * s.d_ff_shared)
+    assert moe.train_save_floats(shp(top_k=0)) == 0                   # invalid shape
+    ft = lambda shape, gu=FAKE, ws_bytes=1 << 40: L.moe_forward_train(
+        ctypes.byref(shape), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        FAKE, FAKE, FAKE, FAKE, FAKE, gu, FAKE, ws_bytes, None, None)
+    assert ft(shp(dtype=N.MOE_DTYPE_F32)) == N.MOE_ERR_UNSUPPORTED     # bf16 layers only
+    assert ft(s, gu=None) == N.MOE_ERR_INVALID_ARG                      # nowhere to keep G and U
+    assert ft(s, ws_bytes=16) == N.MOE_ERR_WORKSPACE

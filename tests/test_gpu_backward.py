@@ -125,7 +125,7 @@ def run_backward(cfg, layer, x, dy, aux, experts=None, accumulate_onto=None):
     dyd = torch.from_numpy(np.ascontiguousarray(dy, dtype=np.float32)).to(DEV)
     log(f"{cfg.name}: moe_backward N={N} E={E} k={cfg.top_k} d={d} F={F} S={S} C={cfg.capacity} aux={aux}")
     moe.moe_backward(shape, xd, L.w_router, L.logit_bias, L.w_gate, L.w_up, L.w_down, L.s_gate, L.s_up, L.s_down,
-                     o.topk_idx, o.topk_w, o.counts, o.offsets, o.perm, o.slot_pos, dyd, aux,
+                     o.topk_idx, o.topk_w, o.counts, o.offsets, o.perm, o.slot_pos, dyd, None, aux,
                      int(accumulate_onto is not None), g["dx"],
                      g["dw_router"], g["d_logit_bias"], g["dw_gate"], g["dw_up"], g["dw_down"], g.get("ds_gate"),
                      g.get("ds_up"), g.get("ds_down"), ws)
@@ -287,3 +287,54 @@ def test_backward_accumulate_adds_to_the_buffers():
     assert len(idle) > 0, "the case must have an expert with no copy"
     for n in ("dw_gate", "dw_up", "dw_down"):
         np.testing.assert_array_equal(got[n][idle].view(np.uint32), start[n][idle].view(np.uint32), err_msg=n)
+
+
+def test_training_forward_keeps_gate_up_and_backward_uses_them():
+    """moe_forward_train: y is bit-identical to moe_forward's; the kept G and U equal x W^T (fp64, on
+    every kept routed row and every shared row) within the fp32 summation bound d 2^-24 sum|x||w|;
+    the backward that reads them instead of recomputing meets the bounds above."""
+    cfg = mi.small_config("bwd_train", dtype="bf16", layer_id=814, x_id=814, n_tokens=300, n_experts=16, top_k=4,
+                          d_model=256, d_ff=128, n_shared=1, d_ff_shared=192, capacity=70, select_bias=0.05)
+    layer, x = mi.make_layer(cfg), mi.make_x(cfg)
+    dy = make_dy(cfg.n_tokens, cfg.d_model, 11)
+    N, k, d, F, Fs, E = cfg.n_tokens, cfg.top_k, cfg.d_model, cfg.d_ff, cfg.d_ff_shared, cfg.n_experts
+    L = MoELayer.from_numpy(moe.shape_for(cfg), layer, DEV)
+    xd = to_device(x, DEV)
+    y_inf = P.to_host(L.forward(xd).y).copy()
+    log(f"{cfg.name}: moe_forward_train N={N} E={E} k={k} d={d} F={F} Fs={Fs}")
+    o = L.forward(xd, save_for_backward=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(P.to_host(o.y).view(np.uint32), y_inf.view(np.uint32))
+    gu, offs, perm = P.to_host(L.gu), P.to_host(o.offsets), P.to_host(o.perm)
+    assert gu.size == 2 * (N * k * F + N * Fs)
+    x64 = mi.to_f64(x)
+    Gr, Ur = gu[:N * k * F].reshape(N * k, F), gu[N * k * F:2 * N * k * F].reshape(N * k, F)
+    bound = d * 2.0 ** -24
+    for e in range(E):
+        rows = np.arange(offs[e], offs[e + 1])
+        if len(rows) == 0:
+            continue
+        X = x64[perm[rows] // k]
+        for got, w in ((Gr[rows], layer.w_gate[e]), (Ur[rows], layer.w_up[e])):
+            W = mi.to_f64(w)
+            assert np.all(np.abs(got - X @ W.T) <= bound * (np.abs(X) @ np.abs(W).T)), f"expert {e}"
+    Gs = gu[2 * N * k * F:2 * N * k * F + N * Fs].reshape(N, Fs)
+    Us = gu[2 * N * k * F + N * Fs:].reshape(N, Fs)
+    for got, w in ((Gs, layer.s_gate[0]), (Us, layer.s_up[0])):
+        W = mi.to_f64(w)
+        assert np.all(np.abs(got - x64 @ W.T) <= bound * (np.abs(x64) @ np.abs(W).T)), "shared expert"
+    g = L.backward(xd, torch.from_numpy(dy.astype(np.float32)).to(DEV), 0.3)
+    torch.cuda.synchronize()
+    idx = np.asarray(P.to_host(o.topk_idx), dtype=np.int64)
+    ref = oracle_grads(cfg, layer, x, dy, 0.3, idx)
+    check_rows(P.to_host(g.dx), ref.dx, "dx")
+    check_rows(P.to_host(g.dw_router), ref.dw_router, "dw_router")
+    (wg, wu, wd), shared = P.oracle_views(layer)
+    M = term_magnitudes(x64, dy, routed_rows(cfg, layer, x64, idx), wg, wu, wd, range(E))
+    for i, name in enumerate(("dw_gate", "dw_up", "dw_down")):
+        got = P.to_host(getattr(g, name))
+        for e in range(E):
+            check_terms(got[e], getattr(ref, name)[e], M[e][i], f"{name}[{e}]")
+    Ms = term_magnitudes(x64, dy, lambda s: (np.arange(N), np.ones(N)), *shared, [0])
+    for i, name in enumerate(("ds_gate", "ds_up", "ds_down")):
+        check_terms(P.to_host(getattr(g, name))[0], getattr(ref, name)[0], Ms[0][i], name)
