@@ -140,16 +140,18 @@ __global__ void k_offsets_kernel(const int32_t* __restrict__ offsets, int G, int
   kofs[G] = run;
 }
 
-// Transposes grouped rows into the padded layout the weight-gradient GEMMs read:
-// out[c][kofs[g] + i] = in[row_g(i)][col_off + c] for i < rows_g, and 0 on the
-// pad columns up to kofs[g + 1]; row_g(i) = offsets[g] + i (or g * uniform + i,
-// or, with replicate, i: every group reads rows [0, uniform)). Columns past
-// kofs[G] are left untouched. One 64 x 64 tile per workgroup, 16-byte loads and
-// stores (in_stride, col_off and C multiples of 8).
+// Transposes grouped rows into the blocks the weight-gradient GEMMs read: group g
+// (rows_g rows, padded to K_g = kofs[g + 1] - kofs[g]) becomes the row-major
+// [C, K_g] block at out + C * kofs[g]: block[c][i] = in[row_g(i)][col_off + c] for
+// i < rows_g, and 0 on the pad columns; row_g(i) = offsets[g] + i (or
+// g * uniform + i, or, with replicate, i: every group reads rows [0, uniform)).
+// One 64 x 64 tile per workgroup (tile k0 of the concatenated K ranges; tiles
+// past kofs[G] do nothing), 16-byte loads and stores (in_stride, col_off and C
+// multiples of 8). Each group's rows stay a few KB long, however many groups.
 __global__ __launch_bounds__(kT) void transpose_padded_kernel(const bf16_t* __restrict__ in, int in_stride, int col_off,
                                                               int C, const int32_t* __restrict__ offsets, int uniform,
                                                               int replicate, const int32_t* __restrict__ kofs, int G,
-                                                              bf16_t* __restrict__ out, int kmax) {
+                                                              bf16_t* __restrict__ out) {
   __shared__ uint16_t tile[64][kTP];
   __shared__ int s_g;
   const int c0 = blockIdx.y * 64, k0 = blockIdx.x * 64;
@@ -172,6 +174,7 @@ __global__ __launch_bounds__(kT) void transpose_padded_kernel(const bf16_t* __re
   const int rows = offsets ? offsets[g + 1] - offsets[g] : uniform;
   const int first = replicate ? 0 : (offsets ? offsets[g] : g * uniform);
   const int i0 = k0 - kofs[g];  // row index within the group of column k0
+  const int Kg = kofs[g + 1] - kofs[g];
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int q = threadIdx.x + it * kT, i = q >> 3, ch = q & 7;
@@ -185,7 +188,8 @@ __global__ __launch_bounds__(kT) void transpose_padded_kernel(const bf16_t* __re
   for (int it = 0; it < 2; ++it) {
     const int q = threadIdx.x + it * kT, c = q >> 3, ch = q & 7;
     if (c0 + c < C)
-      *reinterpret_cast<u32x4_t*>(out + (size_t)(c0 + c) * kmax + k0 + ch * 8) = tile_column8(tile, ch * 8, c);
+      *reinterpret_cast<u32x4_t*>(out + (size_t)C * kofs[g] + (size_t)(c0 + c) * Kg + i0 + ch * 8) =
+          tile_column8(tile, ch * 8, c);
   }
 }
 
@@ -436,7 +440,7 @@ int launch_transpose_padded(const void* in, int in_stride, int col_off, int C, c
   if (in_stride % 8 || col_off % 8 || C % 8 || kmax % 64) return MOE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(transpose_padded_kernel, dim3(kmax / 64, (C + 63) / 64), dim3(kT), 0, st,
                      static_cast<const bf16_t*>(in), in_stride, col_off, C, offsets, uniform, replicate, kofs, G,
-                     static_cast<bf16_t*>(out), kmax);
+                     static_cast<bf16_t*>(out));
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -55,6 +55,7 @@ struct SetView {  // the fields of one SegSet, picked with selects rather than a
   float* out;
   const int32_t* kofs;  // weight-gradient mode (phase 2): per-group K ranges
   int32_t bsplit;       // N-major weights: rows >= bsplit come from wu (0: none)
+  int32_t urows;        // rows per group of a uniform set
   int32_t accum;        // phase 2: out += product
   float* gsave;         // phase 1: fp32 gate and up values (optional)
   float* usave;
@@ -75,6 +76,7 @@ __device__ __forceinline__ SetView pick(const GroupedParams& p, int si) {
   v.out = si ? p.set[1].out : p.set[0].out;
   v.kofs = si ? p.set[1].k_offsets : p.set[0].k_offsets;
   v.bsplit = si ? p.set[1].b_split : p.set[0].b_split;
+  v.urows = si ? p.set[1].uniform_rows : p.set[0].uniform_rows;
   v.accum = si ? p.set[1].accumulate : p.set[0].accumulate;
   v.gsave = si ? p.set[1].g_save : p.set[0].g_save;
   v.usave = si ? p.set[1].u_save : p.set[0].u_save;
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     const int start = tg.start, m0 = tg.m0, mvalid = tg.mvalid, n0 = tg.n0;
     const int F = S.d_ff;
     // K values per row of A (phase 2) and of the weight rows; a weight-gradient
-    // set takes its group's K range [kbase, kbase + K) of matrices shared by all groups
+    // group takes K = kofs[g + 1] - kofs[g] from its own blocks at kofs[g] (below)
     const int kstride = P1 ? d : F;
     int K = kstride, kbase = 0;
     if constexpr (!P1) {
@@ -573,6 +575,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     // ---- A sources: rows past the segment (or with a token out of range)
     // re-read the segment's first row; their outputs are never stored.
     const bf16_t* a_base = P1 ? xg : static_cast<const bf16_t*>(S.h);
+    if constexpr (!P1) {
+      if (S.kofs) a_base += (size_t)S.urows * kbase;  // this group's [M, K] block
+    }
     uint32_t a_off[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
@@ -585,7 +590,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
         src = (unsigned)tok < (unsigned)p.n_tokens ? (uint32_t)tok : 0u;
         src *= (uint32_t)d;
       } else {
-        src = (uint32_t)(S.kofs ? row - start : row) * (uint32_t)F + (uint32_t)kbase;
+        src = S.kofs ? (uint32_t)(row - start) * (uint32_t)K : (uint32_t)row * (uint32_t)F;
       }
       a_off[i] = src + ((cpcA ^ swz<PPA>(r)) << 3);
     }
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
       b_base = static_cast<const BT*>(S.wd) + (size_t)g * bsplit * d;
       b_hi = static_cast<const BT*>(S.wu) + (size_t)g * bsplit * d;
     } else {
-      b_base = static_cast<const BT*>(S.wd) + (S.kofs ? 0 : (size_t)g * d * F / KDIV);
+      b_base = static_cast<const BT*>(S.wd) + (S.kofs ? (size_t)d * kbase : (size_t)g * d * F / KDIV);
     }
     uint32_t b_off[B_INS];
 #pragma unroll
@@ -618,7 +623,9 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
       } else {
         const int r = (wave * B_INS + i) * RPIB + crowB;    // tile row
         const int mr = P1 ? (r % (BN / 2)) : r;              // row within its weight matrix tile
-        b_off[i] = (uint32_t)(n0 + min(mr, lastq)) * (uint32_t)(kstride / KDIV) + (uint32_t)(kbase / KDIV) +
+        // a weight-gradient group reads its own [d, K] block (rows K apart)
+        const int bstride = (!P1 && S.kofs) ? K : kstride;
+        b_off[i] = (uint32_t)(n0 + min(mr, lastq)) * (uint32_t)(bstride / KDIV) +
                    (uint32_t)((cpcB ^ swz<PPB>(r)) * EPP);
       }
     }

@@ -77,10 +77,11 @@ struct SegSet {
   float* g_save;           // phase 1, bf16 weights, optional: [max_rows, d_ff] fp32 gate values (x W_gate^T)
   float* u_save;           //   and up values, beside h, for the backward pass
   float* out;              // [max_rows, d]
-  // Weight-gradient mode (phase 2 only, bf16): when set, group g multiplies
-  // h and w_down over the K range [k_offsets[g], k_offsets[g+1]) (multiples
-  // of 64; empty: zero output); both are single matrices shared by all
-  // groups, with rows d_ff values apart: out[g*M + m, n] = sum_k h[m, k] * w_down[n, k].
+  // Weight-gradient mode (phase 2 only, bf16): when set, group g (uniform_rows
+  // = M rows) multiplies the K_g = k_offsets[g+1] - k_offsets[g] columns
+  // (multiples of 64; K_g = 0: zero output) of its own blocks of h and w_down:
+  // h + M * k_offsets[g] holds [M, K_g] and w_down + d_model * k_offsets[g]
+  // holds [d_model, K_g], each row-major: out[g*M + m, n] = sum_k h_g[m, k] * w_g[n, k].
   const int32_t* k_offsets;
   // N-major weights (phase 2 only, bf16, not with k_offsets): when b_nmajor is
   // set, group g's operand is read as K rows of d_model values each (the
