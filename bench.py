@@ -18,7 +18,10 @@ It prints one JSON line:
   workload, on this host's cores;
 * extras: layer TFLOP/s and algorithmic GB/s, and cold-cache reps (each
   after a 1 GiB write that evicts L2 and the Infinity Cache; median, min,
-  max), outside the timed region.
+  max), outside the timed region;
+* backward (bf16 workloads, unless --no-backward): moe_backward timed by
+  HIP events, writing or accumulating the gradients, and the training
+  forward with the backward that reads its kept gate and up values.
 """
 from __future__ import annotations
 
@@ -270,9 +273,10 @@ def main():
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="extra untimed-region reps, each after a 1 GiB write that evicts L2 and the "
                          "Infinity Cache; reported as layer.cold (median/min/max)")
-    ap.add_argument("--backward", action="store_true",
-                    help="also time moe_backward on the last forward's routing (bf16 workloads); reported "
-                         "as backward, outside the headline value")
+    ap.add_argument("--no-backward", dest="backward", action="store_false",
+                    help="skip timing moe_backward and the training forward (bf16 workloads; reported as "
+                         "backward, outside the headline value)")
+    ap.add_argument("--backward", dest="backward", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -395,7 +399,10 @@ def main():
                   "balance_stat": float(L.out.balance_stat.item()), "cold": cold},
     }
     if args.backward and weights == "bf16":
-        out["backward"] = time_backward(L, xd, cfg, K, args.warmup, kept)
+        try:
+            out["backward"] = time_backward(L, xd, cfg, K, args.warmup, kept)
+        except Exception as e:  # the training-path timing never hides the forward line
+            out["backward"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_cpu_baseline:
         del L, xd
         torch.cuda.empty_cache()

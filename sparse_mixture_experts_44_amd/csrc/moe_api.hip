@@ -79,9 +79,11 @@ int do_route(const moe_shape& s, const void* x, const void* w_router, const floa
              int32_t* idx, float* tw, double* prob_sum, void* ws, hipStream_t st) {
   if (s.n_tokens == 0) return zero_f64(prob_sum, s.n_experts, st);
   const Layout L = layout(s);
+  // the grouped GEMMs' split region is idle while routing: a large router's GEMM uses it
   return launch_route(s, x, w_router, lb, sb, idx, tw, prob_sum,
                       reinterpret_cast<double*>(at(ws, L.partials)),
-                      reinterpret_cast<float*>(at(ws, L.logits)), st);
+                      reinterpret_cast<float*>(at(ws, L.logits)), reinterpret_cast<float*>(at(ws, L.split)),
+                      L.h_routed - L.split, st);
 }
 
 int do_permute(const moe_shape& s, const int32_t* idx, const double* prob_sum, int32_t* counts,
@@ -565,7 +567,8 @@ int moe_router_aux(const moe_shape* shape, const void* x, const void* w_router, 
   double* imp = importance ? importance : (importance_cv2 ? reinterpret_cast<double*>(at(ws, L.aux)) : nullptr);
   return launch_router_aux(s, x, w_router, logit_bias, topk_idx, topk_w, z_loss, imp, importance_cv2,
                            reinterpret_cast<double*>(at(ws, L.partials)),
-                           reinterpret_cast<float*>(at(ws, L.logits)), stream);
+                           reinterpret_cast<float*>(at(ws, L.logits)), reinterpret_cast<float*>(at(ws, L.split)),
+                           L.h_routed - L.split, stream);
 }
 
 int moe_update_select_bias(const moe_shape* shape, const int32_t* counts, float gamma, float* select_bias,
@@ -685,7 +688,7 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
   }
   // ---- router and dx
   int splits = 1;
-  MOE_TRY(launch_router_logits(s, x, w_router, Pf(L.logits), &splits, stream));
+  MOE_TRY(launch_router_logits(s, x, w_router, Pf(L.logits), &splits, split, split_bytes, stream));
   MOE_TRY(launch_router_backward(s, Pf(L.logits), splits, logit_bias, topk_idx, topk_w, Pf(L.dw), counts, aux_coef,
                                  Pf(L.dl), stream));
   MOE_TRY(launch_router_wgrad(Pf(L.dl), x, N, E, d, Pf(L.rpart), dw_router, d_logit_bias, accumulate, stream));

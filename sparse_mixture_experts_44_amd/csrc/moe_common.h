@@ -38,18 +38,21 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(
 // `partials`: route_blocks(s) x E doubles; `logits`: route_logits_floats(s) floats (workspace).
 int launch_route(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                  const float* select_bias, int32_t* topk_idx, float* topk_w, double* prob_sum,
-                 double* partials, float* logits, hipStream_t stream);
+                 double* partials, float* logits, float* split_ws, size_t split_bytes, hipStream_t stream);
 int route_blocks(const moe_shape& s);
 // Training-side statistics: z-loss (recomputes the logits), importance and its CV^2; any output may be NULL.
 int launch_router_aux(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                       const int32_t* topk_idx, const float* topk_w, double* z_loss, double* imp,
-                      double* imp_cv2, double* partials, float* logits, hipStream_t stream);
+                      double* imp_cv2, double* partials, float* logits, float* split_ws, size_t split_bytes,
+                      hipStream_t stream);
 int launch_bias_update(const moe_shape& s, const int32_t* counts, float gamma, float* bias,
                        hipStream_t stream);
 size_t route_logits_floats(const moe_shape& s);
 // The router logits' K-split partial sums ([splits, N, E] floats; their sum in split order is x W_r^T).
+// Large bf16 routers (E >= 64, N >= 256) are one grouped GEMM on the matrix cores (splits = 1), whose
+// split tail tiles use split_ws (split_bytes; the grouped GEMMs' region, idle while the router runs).
 int launch_router_logits(const moe_shape& s, const void* x, const void* w_router, float* logits, int* splits,
-                         hipStream_t stream);
+                         float* split_ws, size_t split_bytes, hipStream_t stream);
 
 // ------------------------------------------------------------------ permute
 int permute_chunks(const moe_shape& s);

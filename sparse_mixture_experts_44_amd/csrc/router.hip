@@ -501,21 +501,58 @@ int route_blocks(const moe_shape& s) {
   return (s.n_tokens + tpb - 1) / tpb;
 }
 
+// Large bf16 routers go to the matrix cores: logits = x W_r^T is then one grouped
+// GEMM (one segment of N rows, K = d, W_r as the [E, d] weight), fp32 sums of exact
+// bf16 products as on the VALU path, in another order.
+bool logits_by_mfma(const moe_shape& s) {
+  return s.dtype == MOE_DTYPE_BF16 && s.n_experts >= 64 && s.n_tokens >= 256;
+}
+
+int compute_logits(const moe_shape& s, const void* x, const void* w_router, float* logits, float* split_ws,
+                   size_t split_bytes, int* splits, hipStream_t st) {
+  if (logits_by_mfma(s)) {
+    GroupedParams p{};
+    p.n_sets = 1;
+    p.x = x;
+    p.n_tokens = s.n_tokens;
+    p.d_model = s.n_experts;  // output columns
+    p.dtype = MOE_DTYPE_BF16;
+    p.split_ws = split_ws;
+    p.split_cap = split_ws ? (long long)(split_bytes / sizeof(float)) : 0;
+    SegSet& S = p.set[0];
+    S.n_groups = 1;
+    S.uniform_rows = s.n_tokens;
+    S.rows_per_token = 1;
+    S.max_rows = s.n_tokens;
+    S.d_ff = s.d_model;  // K
+    S.w_gate = S.w_up = S.w_down = w_router;
+    S.h = const_cast<void*>(x);
+    S.out = logits;
+    *splits = 1;
+    return launch_grouped(p, 2, st);
+  }
+  const LogitsPlan L = plan_logits(s);
+  if (s.dtype == MOE_DTYPE_BF16) launch_logits<true>(s, L, x, w_router, logits, st);
+  else launch_logits<false>(s, L, x, w_router, logits, st);
+  *splits = L.splits;
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 size_t route_logits_floats(const moe_shape& s) {
+  if (logits_by_mfma(s)) return (size_t)s.n_tokens * s.n_experts;
   const LogitsPlan L = plan_logits(s);
   return (size_t)L.splits * s.n_tokens * s.n_experts;
 }
 
 int launch_route(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                  const float* select_bias, int32_t* topk_idx, float* topk_w, double* prob_sum,
-                 double* partials, float* logits, hipStream_t stream) {
-  const LogitsPlan L = plan_logits(s);
-  if (s.dtype == MOE_DTYPE_BF16) launch_logits<true>(s, L, x, w_router, logits, stream);
-  else launch_logits<false>(s, L, x, w_router, logits, stream);
+                 double* partials, float* logits, float* split_ws, size_t split_bytes, hipStream_t stream) {
+  int splits = 1;
+  if (const int st = compute_logits(s, x, w_router, logits, split_ws, split_bytes, &splits, stream)) return st;
   const int nb = route_blocks(s);
   const int el = (s.n_experts + kWave - 1) / kWave;
 #define MOE_SELECT(EL_)                                                                          \
-  hipLaunchKernelGGL(select_kernel<EL_>, dim3(nb), dim3(kThreads), 0, stream, logits, L.splits, \
+  hipLaunchKernelGGL(select_kernel<EL_>, dim3(nb), dim3(kThreads), 0, stream, logits, splits, \
                      logit_bias, select_bias, s.n_tokens, s.n_experts, s.top_k, s.renormalize,   \
                      select_tpb(s), topk_idx, topk_w, partials)
   if (el <= 1) MOE_SELECT(1);
@@ -529,26 +566,22 @@ int launch_route(const moe_shape& s, const void* x, const void* w_router, const 
 }
 
 int launch_router_logits(const moe_shape& s, const void* x, const void* w_router, float* logits, int* splits,
-                         hipStream_t stream) {
-  const LogitsPlan L = plan_logits(s);
-  if (s.dtype == MOE_DTYPE_BF16) launch_logits<true>(s, L, x, w_router, logits, stream);
-  else launch_logits<false>(s, L, x, w_router, logits, stream);
-  *splits = L.splits;
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+                         float* split_ws, size_t split_bytes, hipStream_t stream) {
+  return compute_logits(s, x, w_router, logits, split_ws, split_bytes, splits, stream);
 }
 
 int launch_router_aux(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                       const int32_t* topk_idx, const float* topk_w, double* z_loss, double* imp,
-                      double* imp_cv2, double* partials, float* logits, hipStream_t stream) {
+                      double* imp_cv2, double* partials, float* logits, float* split_ws, size_t split_bytes,
+                      hipStream_t stream) {
   const int N = s.n_tokens, E = s.n_experts;
   if (z_loss) {
-    const LogitsPlan L = plan_logits(s);
-    if (s.dtype == MOE_DTYPE_BF16) launch_logits<true>(s, L, x, w_router, logits, stream);
-    else launch_logits<false>(s, L, x, w_router, logits, stream);
+    int splits = 1;
+    if (const int st = compute_logits(s, x, w_router, logits, split_ws, split_bytes, &splits, stream)) return st;
     const int nb = route_blocks(s);
     const int el = (E + kWave - 1) / kWave;
 #define MOE_LSE(EL_)                                                                                \
-  hipLaunchKernelGGL(lse_sq_kernel<EL_>, dim3(nb), dim3(kThreads), 0, stream, logits, L.splits, logit_bias, \
+  hipLaunchKernelGGL(lse_sq_kernel<EL_>, dim3(nb), dim3(kThreads), 0, stream, logits, splits, logit_bias, \
                      N, E, select_tpb(s), partials)
     if (el <= 1) MOE_LSE(1);
     else if (el <= 2) MOE_LSE(2);
