@@ -355,10 +355,11 @@ __global__ __launch_bounds__(kT) void logit_bias_grad_kernel(const float* __rest
 constexpr int kXT = 64;   // tokens per workgroup
 constexpr int kXE = 64;   // experts per LDS stage
 constexpr int kXP = kXT + 4;  // LDS row pitch (floats): 16-byte aligned rows
+// With rterm (the router term dl W_r already computed, [N, d]), the expert loop is skipped.
 __global__ __launch_bounds__(kT) void dx_kernel(const float* __restrict__ dXr, const int32_t* __restrict__ slot_pos,
                                                 const float* __restrict__ dXs, int S, const float* __restrict__ dl,
-                                                const bf16_t* __restrict__ wr, int N, int E, int k, int d,
-                                                float* __restrict__ dx) {
+                                                const bf16_t* __restrict__ wr, const float* __restrict__ rterm,
+                                                int N, int E, int k, int d, float* __restrict__ dx) {
   __shared__ __align__(16) float s_dl[kXE][kXP];
   const int c = blockIdx.x * kT + threadIdx.x;
   const int t0 = blockIdx.y * kXT;
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(kT) void dx_kernel(const float* __restrict__ dXr, c
   float acc[kXT];
 #pragma unroll
   for (int q = 0; q < kXT; ++q) acc[q] = 0.f;
-  for (int e0 = 0; e0 < E; e0 += kXE) {
+  for (int e0 = 0; e0 < (rterm ? 0 : E); e0 += kXE) {
     const int ne = min(kXE, E - e0);
     for (int i = threadIdx.x; i < kXT * kXE; i += kT) {
       const int tt = i / kXE, ee = i % kXE;
@@ -399,9 +400,67 @@ __global__ __launch_bounds__(kT) void dx_kernel(const float* __restrict__ dXr, c
         if (r >= 0) sum += dXr[(size_t)r * d + c];
       }
       for (int s2 = 0; s2 < S; ++s2) sum += dXs[((size_t)s2 * N + t) * d + c];
-      dx[(size_t)t * d + c] = sum + acc[q];
+      dx[(size_t)t * d + c] = sum + (rterm ? rterm[(size_t)t * d + c] : acc[q]);
     }
   }
+}
+
+// Splits dl [N, E] (fp32) into bf16 parts hi = bf16(dl), lo = bf16(dl - hi), so that
+// hi + lo equals dl to about 2^-16 relative: the router products then run as bf16
+// matrix-core GEMMs on exact bf16 W_r and x. Writes dlh [N, 2E] (row t: hi | lo) and
+// its transpose dlT [E, 2N] (row e: hi | lo). One 64 x 64 tile per workgroup through
+// LDS (partial edge tiles are checked element by element).
+__global__ __launch_bounds__(kT) void split_hilo_kernel(const float* __restrict__ dl, int N, int E,
+                                                        bf16_t* __restrict__ dlh, bf16_t* __restrict__ dlT) {
+  __shared__ uint16_t th[64][kTP], tl[64][kTP];
+  const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += kT) {
+    const int tt = i / 64, ee = i % 64, t = t0 + tt, e = e0 + ee;
+    if (t < N && e < E) {
+      const float v = dl[(size_t)t * E + e];
+      const bf16_t h = f32_to_bf16(v), l = f32_to_bf16(v - bf(h));
+      dlh[(size_t)t * 2 * E + e] = h;
+      dlh[(size_t)t * 2 * E + E + e] = l;
+      th[tt][ee] = h;
+      tl[tt][ee] = l;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += kT) {
+    const int ee = i / 64, tt = i % 64, t = t0 + tt, e = e0 + ee;
+    if (t < N && e < E) {
+      dlT[(size_t)e * 2 * N + t] = th[tt][ee];
+      dlT[(size_t)e * 2 * N + N + t] = tl[tt][ee];
+    }
+  }
+}
+
+// dx[t][c] = (sum_j dXr[slot_pos[t*k + j]][c] over the kept copies, j in order
+//            + sum_s dXs[s*N + t][c]) + rterm[t][c], the router term already computed:
+// the same sums as dx_kernel, four columns per thread (d is a multiple of 4).
+__global__ __launch_bounds__(kT) void dx_gather_kernel(const float* __restrict__ dXr,
+                                                       const int32_t* __restrict__ slot_pos,
+                                                       const float* __restrict__ dXs, int S,
+                                                       const float* __restrict__ rterm, int N, int k, int d,
+                                                       float* __restrict__ dx) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * kT + threadIdx.x) * 4;
+  if (c >= d) return;
+  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int r = slot_pos[(size_t)t * k + j];
+    if (r >= 0) {
+      const float4 v = *reinterpret_cast<const float4*>(dXr + (size_t)r * d + c);
+      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    }
+  }
+  for (int s2 = 0; s2 < S; ++s2) {
+    const float4 v = *reinterpret_cast<const float4*>(dXs + ((size_t)s2 * N + t) * d + c);
+    sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+  }
+  const float4 rr = *reinterpret_cast<const float4*>(rterm + (size_t)t * d + c);
+  *reinterpret_cast<float4*>(dx + (size_t)t * d + c) = make_float4(sum.x + rr.x, sum.y + rr.y, sum.z + rr.z,
+                                                                  sum.w + rr.w);
 }
 
 __global__ void fill_f32_kernel(float* p, size_t n, float v) {
@@ -489,10 +548,28 @@ int launch_router_wgrad(const float* dl, const void* x, int N, int E, int d, flo
 }
 
 int launch_dx(const float* dXr, const int32_t* slot_pos, const float* dXs, int S, const float* dl, const void* wr,
-              int N, int E, int k, int d, float* dx, hipStream_t st) {
+              const float* rterm, int N, int E, int k, int d, float* dx, hipStream_t st) {
   if (N <= 0) return MOE_OK;
+  if (rterm && d % 4 == 0) {
+    hipLaunchKernelGGL(dx_gather_kernel, dim3((d / 4 + kT - 1) / kT, N), dim3(kT), 0, st, dXr, slot_pos, dXs, S,
+                       rterm, N, k, d, dx);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
   hipLaunchKernelGGL(dx_kernel, dim3((d + kT - 1) / kT, (N + kXT - 1) / kXT), dim3(kT), 0, st, dXr, slot_pos, dXs, S,
-                     dl, static_cast<const bf16_t*>(wr), N, E, k, d, dx);
+                     dl, static_cast<const bf16_t*>(wr), rterm, N, E, k, d, dx);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_logit_bias_grad(const float* dl, int N, int E, float* dlb, int accumulate, hipStream_t st) {
+  if (!dlb || E <= 0) return MOE_OK;
+  hipLaunchKernelGGL(logit_bias_grad_kernel, dim3(E), dim3(kT), 0, st, dl, N, E, accumulate, dlb);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_split_hilo(const float* dl, int N, int E, void* dlh, void* dlT, hipStream_t st) {
+  if (N <= 0 || E <= 0) return MOE_OK;
+  hipLaunchKernelGGL(split_hilo_kernel, dim3((E + 63) / 64, (N + 63) / 64), dim3(kT), 0, st, dl, N, E,
+                     static_cast<bf16_t*>(dlh), static_cast<bf16_t*>(dlT));
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

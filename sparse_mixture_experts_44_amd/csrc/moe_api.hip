@@ -149,7 +149,7 @@ int grouped_impl(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const v
 // kept copies occupy the first offsets[E]), Kmax = R rounded up to 64 plus 64
 // per expert (each expert's rows padded to 64 in the transposed layout).
 struct BwLayout {
-  size_t logits, dl, rpart, dw, kofs, kofs_s, Xg, dYg, dO, G, U, dHp, h, dGU, dXr, dOT, hT, dGT, dUT, XT, split;
+  size_t logits, dl, rpart, dlh, dlT, rterm, dw, kofs, kofs_s, Xg, dYg, dO, G, U, dHp, h, dGU, dXr, dOT, hT, dGT, dUT, XT, split;
   size_t Xs, dYs, Gs, Us, dHs, hs, dGUs, dXs, dOsT, hsT, dGsT, dUsT, XsT, total;
   long long R, Kmax, Npad, KSmax;
 };
@@ -167,6 +167,9 @@ BwLayout bw_layout(const moe_shape& s) {
   L.logits = take(route_logits_floats(s) * 4);
   L.dl = take(N * E * 4);
   L.rpart = take(router_wgrad_part_floats((int)N, (int)E, (int)d) * 4);
+  L.dlh = take(N * 2 * E * 2);   // dl as bf16 hi | lo parts, and its transpose (router products as GEMMs)
+  L.dlT = take(E * 2 * N * 2);
+  L.rterm = take(N * d * 4);     // dl W_r
   L.dw = take(N * k * 4);
   L.kofs = take((E + 1) * 4);
   L.kofs_s = take((S + 1) * 4);
@@ -237,7 +240,9 @@ int grouped_gemm(int n_groups, const int32_t* offsets, int uniform, long long ma
 // B_hi + g * b_split * ncols.
 int grouped_gemm_nmajor(int n_groups, const int32_t* offsets, int uniform, long long max_rows, int K, int ncols,
                         const void* A, const void* B_lo, const void* B_hi, int b_split, float* out, float* split_ws,
-                        size_t split_bytes, hipStream_t st) {
+                        size_t split_bytes, hipStream_t st, int accumulate = 0) {
+  // each 64-row K stage must lie within one of the two matrices
+  if (K % 64 || b_split % 64 || b_split < 0 || (b_split > 0 && K - b_split > b_split)) return MOE_ERR_UNSUPPORTED;
   GroupedParams p{};
   p.n_sets = 1;
   p.x = A;
@@ -259,6 +264,7 @@ int grouped_gemm_nmajor(int n_groups, const int32_t* offsets, int uniform, long 
   S.out = out;
   S.b_nmajor = 1;
   S.b_split = b_split;
+  S.accumulate = accumulate;
   return launch_grouped(p, 2, st);
 }
 
@@ -691,8 +697,23 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
   MOE_TRY(launch_router_logits(s, x, w_router, Pf(L.logits), &splits, split, split_bytes, stream));
   MOE_TRY(launch_router_backward(s, Pf(L.logits), splits, logit_bias, topk_idx, topk_w, Pf(L.dw), counts, aux_coef,
                                  Pf(L.dl), stream));
-  MOE_TRY(launch_router_wgrad(Pf(L.dl), x, N, E, d, Pf(L.rpart), dw_router, d_logit_bias, accumulate, stream));
-  MOE_TRY(launch_dx(Pf(L.dXr), slot_pos, S > 0 ? Pf(L.dXs) : nullptr, S, Pf(L.dl), w_router, N, E, k, d, dx, stream));
+  // dW_r = dl^T x and the router term dl W_r of dx: with dl split into bf16 hi + lo parts
+  // (2^-16 relative), both are bf16 GEMMs reading W_r and x in their stored orientation
+  // (K = 2E and 2N, rows from the same matrix twice: each half a whole number of 64-row K stages)
+  float* rterm = nullptr;
+  if (E % 64 == 0 && N % 64 == 0) {
+    MOE_TRY(launch_split_hilo(Pf(L.dl), N, E, P(L.dlh), P(L.dlT), stream));
+    rterm = Pf(L.rterm);
+    MOE_TRY(grouped_gemm_nmajor(1, nullptr, N, N, 2 * E, d, P(L.dlh), w_router, w_router, E, rterm, split,
+                                split_bytes, stream));
+    MOE_TRY(grouped_gemm_nmajor(1, nullptr, E, E, 2 * N, d, P(L.dlT), x, x, N, dw_router, split, split_bytes,
+                                stream, accumulate));
+    MOE_TRY(launch_logit_bias_grad(Pf(L.dl), N, E, d_logit_bias, accumulate, stream));
+  } else {
+    MOE_TRY(launch_router_wgrad(Pf(L.dl), x, N, E, d, Pf(L.rpart), dw_router, d_logit_bias, accumulate, stream));
+  }
+  MOE_TRY(launch_dx(Pf(L.dXr), slot_pos, S > 0 ? Pf(L.dXs) : nullptr, S, Pf(L.dl), w_router, rterm, N, E, k, d, dx,
+                    stream));
 #undef MOE_TRY
   return MOE_OK;
 }

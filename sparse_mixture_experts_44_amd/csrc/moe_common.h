@@ -149,7 +149,11 @@ size_t router_wgrad_part_floats(int N, int E, int d);
 int launch_router_wgrad(const float* dl, const void* x, int N, int E, int d, float* part, float* dwr, float* dlb,
                         int accumulate, hipStream_t st);
 int launch_dx(const float* dXr, const int32_t* slot_pos, const float* dXs, int S, const float* dl, const void* wr,
-              int N, int E, int k, int d, float* dx, hipStream_t st);
+              const float* rterm, int N, int E, int k, int d, float* dx, hipStream_t st);
+// dl [N, E] fp32 -> bf16 parts: dlh [N, 2E] (hi | lo per row) and dlT [E, 2N] (its transpose)
+int launch_split_hilo(const float* dl, int N, int E, void* dlh, void* dlT, hipStream_t st);
+// d_logit_bias[e] = sum_t dl[t][e] (added to d_logit_bias when accumulating)
+int launch_logit_bias_grad(const float* dl, int N, int E, float* dlb, int accumulate, hipStream_t st);
 int launch_fill_f32(float* p, size_t n, float v, hipStream_t st);
 
 // ------------------------------------------------------------------ combine

@@ -166,7 +166,7 @@ def oracle_grads(cfg, layer, x, dy, aux, idx):
     (dict(n_tokens=129, n_experts=8, top_k=1, d_model=64, d_ff=64, renormalize=False, capacity=12), 0.0),
     (dict(n_tokens=64, n_experts=256, top_k=8, d_model=256, d_ff=128, n_shared=1, d_ff_shared=128,
           select_bias=0.1), 0.2),                                                    # 256 experts, top-8
-    (dict(n_tokens=400, n_experts=32, top_k=1, d_model=128, d_ff=256, logit_skew=1.5, capacity=16), 0.05),
+    (dict(n_tokens=384, n_experts=64, top_k=1, d_model=128, d_ff=256, logit_skew=1.5, capacity=16), 0.05),
 ])
 def test_backward_small_layers_every_element(kw, aux):
     cfg = mi.small_config("bwd", dtype="bf16", layer_id=800 + kw["n_tokens"] % 11, x_id=800, **kw)
@@ -270,7 +270,7 @@ def test_backward_accumulate_adds_to_the_buffers():
     """accumulate = 1: every weight gradient buffer ends as its start value plus the gradient of
     the write mode, entry by entry (one fp32 addition: exact up to its rounding); an expert with
     no kept copy keeps its start value bit for bit; dx is overwritten."""
-    cfg = mi.small_config("bwd_acc", dtype="bf16", layer_id=813, x_id=813, n_tokens=300, n_experts=64, top_k=2,
+    cfg = mi.small_config("bwd_acc", dtype="bf16", layer_id=813, x_id=813, n_tokens=320, n_experts=64, top_k=2,
                           d_model=128, d_ff=192, n_shared=1, d_ff_shared=64, capacity=30, select_bias=0.1)
     layer, x = mi.make_layer(cfg), mi.make_x(cfg)
     dy = make_dy(cfg.n_tokens, cfg.d_model, 5)
