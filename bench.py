@@ -123,19 +123,19 @@ def time_backward(L, xd, cfg, steps, warmup, kept):
     dy = torch.randn(cfg.n_tokens, cfg.d_model, generator=g, device=xd.device).bfloat16().float()
     stream = torch.cuda.current_stream().cuda_stream
 
-    def timed(accumulate):
+    def timed(accumulate, bf16=False):
         for _ in range(warmup):
-            L.backward(xd, dy, 0.01, accumulate=accumulate)
+            L.backward(xd, dy, 0.01, accumulate=accumulate, bf16_weight_grads=bf16)
         ev = HipEvents(2)
         torch.cuda.synchronize()
         ev.record(0, stream)
         for _ in range(steps):
-            L.backward(xd, dy, 0.01, accumulate=accumulate)
+            L.backward(xd, dy, 0.01, accumulate=accumulate, bf16_weight_grads=bf16)
         ev.record(1, stream)
         torch.cuda.synchronize()
         return ev.elapsed_ms(0, 1) / steps
 
-    ms, ms_acc = timed(False), timed(True)
+    ms, ms_acc, ms_bf16 = timed(False), timed(True), timed(False, bf16=True)
     # training forward (keeps G and U), then the backward that reads them
     for _ in range(max(1, warmup)):  # the first call also allocates the G, U buffer
         L.forward(xd, save_for_backward=True)
@@ -152,9 +152,11 @@ def time_backward(L, xd, cfg, steps, warmup, kept):
     tf = w["flops_algorithmic"] / (ms * 1e-3) / 1e12
     return {"ms": ms, "steps": steps, "tflops_algorithmic": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
             "tflops_executed": w["flops_executed"] / (ms * 1e-3) / 1e12, **w,
-            "ms_accumulate": ms_acc, "forward_train_ms": ms_fwd_train, "ms_with_saved_gate_up": ms_saved,
+            "ms_accumulate": ms_acc, "ms_bf16_weight_grads": ms_bf16, "forward_train_ms": ms_fwd_train,
+            "ms_with_saved_gate_up": ms_saved,
             "note": "moe_backward alone (gradients of x, W_r, logit bias, every expert weight), writing the "
-                    "gradients (ms) or adding them to fp32 buffers (ms_accumulate); forward_train_ms: "
+                    "gradients (ms), adding them to fp32 buffers (ms_accumulate) or writing the expert weight "
+                    "gradients as bf16 (ms_bf16_weight_grads); forward_train_ms: "
                     "moe_forward_train, which keeps G and U; ms_with_saved_gate_up: the backward reading them; "
                     "algorithmic FLOPs exclude the G, U and logit recompute"}
 

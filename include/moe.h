@@ -360,6 +360,15 @@ int moe_forward_int4(const moe_shape* shape, const void* x, const void* w_router
 /* Workspace bytes of moe_backward for a shape (0 for an invalid shape). */
 size_t moe_backward_workspace_bytes(const moe_shape* shape);
 
+/* How moe_backward delivers the gradients (grad_mode). */
+enum moe_grad_mode {
+  MOE_GRAD_WRITE = 0,       /* every output written, fp32 */
+  MOE_GRAD_ACCUMULATE = 1,  /* dx written; every other gradient added to the fp32 buffer's contents */
+  MOE_GRAD_WRITE_BF16 = 2   /* as MOE_GRAD_WRITE, but the expert weight gradients (dw_gate, dw_up,
+                               dw_down, ds_*) are stored as bf16: the round-to-nearest-even of the
+                               fp32 values MOE_GRAD_WRITE stores */
+};
+
 /* Inputs: the layer's bf16 weights as passed to moe_forward; the forward's
  * outputs topk_idx [N, k], topk_w [N, k], counts [E], offsets [E+1], perm
  * [N*k], slot_pos [N*k] (unchanged since that call); gu_saved: the gu_save
@@ -367,26 +376,29 @@ size_t moe_backward_workspace_bytes(const moe_shape* shape);
  * recomputed); dy [N, d] fp32, read at
  * bf16 precision (every use goes through its round-to-nearest-even bf16
  * value, so bf16-valued dy loses nothing); aux_coef (finite; 0 drops the
- * balance term); accumulate (0 or 1, below).
- * Outputs (fp32): dx [N, d]; dw_router [E, d]; d_logit_bias [E] (NULL: not
- * computed); dw_gate, dw_up [E, F, d]; dw_down [E, d, F]; ds_gate, ds_up
- * [S, Fs, d] and ds_down [S, d, Fs] (may be NULL when S == 0).
- * accumulate == 0: every entry is written (an expert with no kept copy gets
- * zeros). accumulate == 1: dx is written, every other output gets the
- * gradient added to its contents (an expert with no kept copy is not
+ * balance term); grad_mode (enum moe_grad_mode).
+ * Outputs: dx [N, d] fp32; dw_router [E, d] fp32; d_logit_bias [E] fp32
+ * (NULL: not computed); dw_gate, dw_up [E, F, d]; dw_down [E, d, F]; ds_gate,
+ * ds_up [S, Fs, d] and ds_down [S, d, Fs] (may be NULL when S == 0): fp32, or
+ * bf16 under MOE_GRAD_WRITE_BF16.
+ * MOE_GRAD_WRITE(_BF16): every entry is written (an expert with no kept copy
+ * gets zeros). MOE_GRAD_ACCUMULATE: dx is written, every other output gets
+ * the gradient added to its contents (an expert with no kept copy is not
  * touched): the form for summing gradients over micro-batches into fp32
  * buffers, which also skips writing the zero gradients of idle experts.
+ * MOE_GRAD_WRITE_BF16 halves the bytes of the weight-gradient stores, which
+ * bound those products when experts receive few rows.
  * Errors: MOE_ERR_UNSUPPORTED unless the shape's dtype is MOE_DTYPE_BF16;
- * MOE_ERR_INVALID_ARG for a missing pointer, a non-finite aux_coef or
- * accumulate not 0 or 1;
+ * MOE_ERR_INVALID_ARG for a missing pointer, a non-finite aux_coef or an
+ * unknown grad_mode;
  * MOE_ERR_WORKSPACE when ws_bytes < moe_backward_workspace_bytes(shape). */
 int moe_backward(const moe_shape* shape, const void* x, const void* w_router, const float* logit_bias,
                  const void* w_gate, const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
                  const void* s_down, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
                  const int32_t* offsets, const int32_t* perm, const int32_t* slot_pos, const float* dy,
-                 const float* gu_saved, double aux_coef, int32_t accumulate, float* dx, float* dw_router, float* d_logit_bias,
-                 float* dw_gate, float* dw_up, float* dw_down, float* ds_gate, float* ds_up, float* ds_down, void* ws,
-                 size_t ws_bytes, hipStream_t stream);
+                 const float* gu_saved, double aux_coef, int32_t grad_mode, float* dx, float* dw_router,
+                 float* d_logit_bias, void* dw_gate, void* dw_up, void* dw_down, void* ds_gate, void* ds_up,
+                 void* ds_down, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

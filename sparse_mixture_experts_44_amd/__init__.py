@@ -6,7 +6,7 @@ keeps the weights resident on the device. Importing the package does not load
 the library; the first call does, and fails loudly if it has not been built.
 """
 from ._native import (  # noqa: F401
-    LIB_PATH, MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
+    LIB_PATH, MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_ERR_HIP, MOE_GRAD_ACCUMULATE, MOE_GRAD_WRITE, MOE_GRAD_WRITE_BF16, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE, MOE_OK, MOE_STAGE_EVENTS, STAGES, MoEError, MoEFp8Scales, MoEShape,
     MoEWeightScales, backward_workspace_bytes, fp8_scales, lib, moe_backward, moe_combine, moe_forward,
     moe_forward_fp8, moe_forward_int4, moe_forward_train, moe_grouped_swiglu, moe_grouped_swiglu_fp8,

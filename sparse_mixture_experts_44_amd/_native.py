@@ -286,13 +286,16 @@ def backward_workspace_bytes(shape: MoEShape) -> int:
     return int(lib().moe_backward_workspace_bytes(ctypes.byref(shape)))
 
 
+MOE_GRAD_WRITE, MOE_GRAD_ACCUMULATE, MOE_GRAD_WRITE_BF16 = 0, 1, 2  # moe_backward's grad_mode
+
+
 def moe_backward(shape, x, w_router, logit_bias, w_gate, w_up, w_down, s_gate, s_up, s_down, topk_idx, topk_w,
-                 counts, offsets, perm, slot_pos, dy, gu_saved, aux_coef, accumulate, dx, dw_router, d_logit_bias,
+                 counts, offsets, perm, slot_pos, dy, gu_saved, aux_coef, grad_mode, dx, dw_router, d_logit_bias,
                  dw_gate, dw_up, dw_down, ds_gate, ds_up, ds_down, ws, stream=None):
     _check("moe_backward", lib().moe_backward(
         ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
         _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets),
-        _ptr(perm), _ptr(slot_pos), _ptr(dy), _ptr(gu_saved), float(aux_coef), int(accumulate), _ptr(dx),
+        _ptr(perm), _ptr(slot_pos), _ptr(dy), _ptr(gu_saved), float(aux_coef), int(grad_mode), _ptr(dx),
         _ptr(dw_router),
         _ptr(d_logit_bias),
         _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(ds_gate), _ptr(ds_up), _ptr(ds_down), _ptr(ws),

@@ -373,7 +373,7 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int G, long long cap_
 // multiplied by its weight row's scale, and with int4 weights the offset
 // sums corr[i] (136 * sum(x) of each row) are subtracted before that (none
 // when corr is NULL: the K-parts of split tiles are stored already reduced).
-template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE, int FM, int NB>
+template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE, int FM, int NB, bool OBF = false>
 __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetView& S, const TileGeom& t,
                                            int d, int lane, int wm, int wn, const f32x16_t* corr = nullptr) {
   constexpr bool WS = WQ != 0, W4 = WQ == 4;
@@ -451,6 +451,11 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
             if (col0 + j * 32 < ncols)
               hrow[j * 32] = WS ? silu_mul_bf16((acc[i][j][v] - c) * sc0[j], (acc[i][j + FN][v] - c) * sc1[j])
                                 : silu_mul_bf16(acc[i][j][v], acc[i][j + FN][v]);
+        } else if constexpr (OBF) {  // bf16 output (round to nearest even)
+          bf16_t* orow = reinterpret_cast<bf16_t*>(S.out) + row * d + col0;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            if (col0 + j * 32 < ncols) orow[j * 32] = __builtin_bit_cast(bf16_t, (__bf16)acc[i][j][v]);
         } else {
           float* orow = S.out + row * d + col0;
 #pragma unroll
@@ -482,7 +487,7 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
 // so that fewer copies queue at once behind the barrier (3-5% faster on
 // 256 x 256 tiles; the second half of the step still covers their latency).
 template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB, int WQ, bool P1, bool SPREAD,
-          bool NMAJ = false, bool SAVE = false>
+          bool NMAJ = false, bool SAVE = false, bool OBF = false>
 __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(GroupedParams p) {
   constexpr bool W8 = WQ == 8, W4 = WQ == 4, WS = WQ != 0;
   using BT = typename std::conditional<WS, uint8_t, bf16_t>::type;  // weight storage unit
@@ -782,7 +787,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
             dst[((i * NB + j) * 16 + v) * NT + tid] = W4 ? acc[i][j][v] - corr[i][v] : acc[i][j][v];
       continue;
     }
-    store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE>(acc, S, tg, d, lane, wm, wn, corr);
+    store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF>(acc, S, tg, d, lane, wm, wn, corr);
   }
 }
 
@@ -805,7 +810,7 @@ __global__ __launch_bounds__(256) void split_sum_kernel(float* __restrict__ ws) 
 // The epilogue of the split tail tiles of the launch before it (same
 // parameters, `main_grid` workgroups), from part 0: workgroup b finishes
 // tail tile b. Workgroups past the tail exit.
-template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE = false>
+template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE = false, bool OBF = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedParams p, int main_grid) {
   constexpr int TM = BM / WGM, FM = TM / 32;
   constexpr int BH = P1 ? BN / 2 : BN;
@@ -836,7 +841,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedPar
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = src[((size_t)(i * NB + j) * 16 + v) * NT];
-  store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE>(acc, S, tg, d, lane, wm, wn);
+  store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF>(acc, S, tg, d, lane, wm, wn);
 }
 
 // =====================================================================  fp32 SIMT
@@ -956,6 +961,7 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
   // the training forward (bf16 phase 1 with g_save) runs its own instantiation: the
   // inference kernels keep their code unchanged
   const bool save = WQ == 0 && phase == 1 && p.set[0].g_save;
+  const bool obf = WQ == 0 && phase == 2 && !NMAJ && p.set[0].out_bf16;  // bf16 weight gradients
   if constexpr (NMAJ)
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, true>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
@@ -965,6 +971,9 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
   else if (phase == 1)
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
+  else if (obf)
+    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, false, false, WQ == 0>),
+                       dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
   else
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
@@ -976,6 +985,9 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
     else if (phase == 1)
       hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, true>), dim3(grid), dim3(WGM * WGN * 64),
                          0, st, p, grid);
+    else if (obf)
+      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false, false, WQ == 0>), dim3(grid),
+                         dim3(WGM * WGN * 64), 0, st, p, grid);
     else
       hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false>), dim3(grid), dim3(WGM * WGN * 64),
                          0, st, p, grid);

@@ -210,7 +210,7 @@ BwLayout bw_layout(const moe_shape& s) {
 // out[g*M + m, n] = sum over group g's K range of A[m, k] B[n, k].
 int grouped_gemm(int n_groups, const int32_t* offsets, int uniform, long long max_rows, int K_or_stride, int ncols,
                  const void* A, const void* B, float* out, const int32_t* kofs, float* split_ws, size_t split_bytes,
-                 hipStream_t st, int accumulate = 0) {
+                 hipStream_t st, int accumulate = 0, int out_bf16 = 0) {
   GroupedParams p{};
   p.n_sets = 1;
   p.x = A;
@@ -231,6 +231,7 @@ int grouped_gemm(int n_groups, const int32_t* offsets, int uniform, long long ma
   S.out = out;
   S.k_offsets = kofs;
   S.accumulate = accumulate;
+  S.out_bf16 = out_bf16;
   return launch_grouped(p, 2, st);
 }
 
@@ -594,14 +595,24 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
                  const void* w_gate, const void* w_up, const void* w_down, const void* s_gate, const void* s_up,
                  const void* s_down, const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
                  const int32_t* offsets, const int32_t* perm, const int32_t* slot_pos, const float* dy,
-                 const float* gu_saved, double aux_coef, int32_t accumulate, float* dx, float* dw_router, float* d_logit_bias,
-                 float* dw_gate, float* dw_up, float* dw_down, float* ds_gate, float* ds_up, float* ds_down, void* ws,
-                 size_t ws_bytes, hipStream_t stream) {
+                 const float* gu_saved, double aux_coef, int32_t grad_mode, float* dx, float* dw_router,
+                 float* d_logit_bias, void* dw_gate_, void* dw_up_, void* dw_down_, void* ds_gate_, void* ds_up_,
+                 void* ds_down_, void* ws, size_t ws_bytes, hipStream_t stream) {
+  // expert weight gradients: fp32, or bf16 under MOE_GRAD_WRITE_BF16 (the GEMM's out pointer either way)
+  float* dw_gate = static_cast<float*>(dw_gate_);
+  float* dw_up = static_cast<float*>(dw_up_);
+  float* dw_down = static_cast<float*>(dw_down_);
+  float* ds_gate = static_cast<float*>(ds_gate_);
+  float* ds_up = static_cast<float*>(ds_up_);
+  float* ds_down = static_cast<float*>(ds_down_);
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
   if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (!std::isfinite(aux_coef) || (accumulate != 0 && accumulate != 1)) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(aux_coef) || grad_mode < MOE_GRAD_WRITE || grad_mode > MOE_GRAD_WRITE_BF16)
+    return MOE_ERR_INVALID_ARG;
+  const int accumulate = grad_mode == MOE_GRAD_ACCUMULATE;
+  const int wbf16 = grad_mode == MOE_GRAD_WRITE_BF16;  // expert weight gradients stored as bf16
   if (!dw_router || !dw_gate || !dw_up || !dw_down || !w_gate || !w_up || !w_down || !w_router || !ws)
     return MOE_ERR_INVALID_ARG;
   if (s.n_shared > 0 && (!s_gate || !s_up || !s_down || !ds_gate || !ds_up || !ds_down)) return MOE_ERR_INVALID_ARG;
@@ -613,11 +624,13 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
   const int S = s.n_shared, Fs = S ? s.d_ff_shared : 0;
   if (N == 0) {  // no tokens: every gradient is 0 (nothing to add when accumulating)
     if (accumulate) return MOE_OK;
-    for (auto pr : {std::make_pair(dw_router, (size_t)E * d), std::make_pair(dw_gate, (size_t)E * F * d),
-                    std::make_pair(dw_up, (size_t)E * F * d), std::make_pair(dw_down, (size_t)E * d * F),
-                    std::make_pair(d_logit_bias, (size_t)E), std::make_pair(ds_gate, (size_t)S * Fs * d),
-                    std::make_pair(ds_up, (size_t)S * Fs * d), std::make_pair(ds_down, (size_t)S * d * Fs)})
-      if (pr.first && (st = launch_fill_f32(pr.first, pr.second, 0.f, stream))) return st;
+    // zero bytes (+0 in fp32 and in bf16): expert weight gradients take 2 bytes each in bf16 mode
+    const size_t wb = wbf16 ? 2 : 4;
+    for (auto pr : {std::make_pair(dw_router, (size_t)E * d * 4), std::make_pair(dw_gate, (size_t)E * F * d * wb),
+                    std::make_pair(dw_up, (size_t)E * F * d * wb), std::make_pair(dw_down, (size_t)E * d * F * wb),
+                    std::make_pair(d_logit_bias, (size_t)E * 4), std::make_pair(ds_gate, (size_t)S * Fs * d * wb),
+                    std::make_pair(ds_up, (size_t)S * Fs * d * wb), std::make_pair(ds_down, (size_t)S * d * Fs * wb)})
+      if (pr.first && (st = launch_fill_f32(pr.first, pr.second / 4, 0.f, stream))) return st;
     return MOE_OK;
   }
   auto P = [&](size_t o) { return static_cast<void*>(at(ws, o)); };
@@ -654,11 +667,11 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
   MOE_TRY(launch_transpose_padded(P(L.dGU), 2 * F, F, F, offsets, 0, 0, Pi(L.kofs), E, P(L.dUT), Kmax, stream));
   MOE_TRY(launch_transpose_padded(P(L.Xg), d, 0, d, offsets, 0, 0, Pi(L.kofs), E, P(L.XT), Kmax, stream));
   MOE_TRY(grouped_gemm(E, nullptr, d, (long long)E * d, Kmax, F, P(L.dOT), P(L.hT), dw_down, Pi(L.kofs), split,
-                       split_bytes, stream, accumulate));
+                       split_bytes, stream, accumulate, wbf16));
   MOE_TRY(grouped_gemm(E, nullptr, F, (long long)E * F, Kmax, d, P(L.dGT), P(L.XT), dw_gate, Pi(L.kofs), split,
-                       split_bytes, stream, accumulate));
+                       split_bytes, stream, accumulate, wbf16));
   MOE_TRY(grouped_gemm(E, nullptr, F, (long long)E * F, Kmax, d, P(L.dUT), P(L.XT), dw_up, Pi(L.kofs), split,
-                       split_bytes, stream, accumulate));
+                       split_bytes, stream, accumulate, wbf16));
   // ---- shared experts: every token, weight 1
   if (S > 0) {
     const int RS = S * N, KS = (int)L.KSmax;
@@ -686,11 +699,11 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
     MOE_TRY(launch_transpose_padded(P(L.dGUs), 2 * Fs, Fs, Fs, nullptr, N, 0, Pi(L.kofs_s), S, P(L.dUsT), KS, stream));
     MOE_TRY(launch_transpose_padded(P(L.Xs), d, 0, d, nullptr, N, 0, Pi(L.kofs_s), S, P(L.XsT), KS, stream));
     MOE_TRY(grouped_gemm(S, nullptr, d, (long long)S * d, KS, Fs, P(L.dOsT), P(L.hsT), ds_down, Pi(L.kofs_s), split,
-                         split_bytes, stream, accumulate));
+                         split_bytes, stream, accumulate, wbf16));
     MOE_TRY(grouped_gemm(S, nullptr, Fs, (long long)S * Fs, KS, d, P(L.dGsT), P(L.XsT), ds_gate, Pi(L.kofs_s), split,
-                         split_bytes, stream, accumulate));
+                         split_bytes, stream, accumulate, wbf16));
     MOE_TRY(grouped_gemm(S, nullptr, Fs, (long long)S * Fs, KS, d, P(L.dUsT), P(L.XsT), ds_up, Pi(L.kofs_s), split,
-                         split_bytes, stream, accumulate));
+                         split_bytes, stream, accumulate, wbf16));
   }
   // ---- router and dx
   int splits = 1;

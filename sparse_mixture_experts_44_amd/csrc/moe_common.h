@@ -97,6 +97,8 @@ struct SegSet {
   // Phase 2: add the products to out instead of writing them; with k_offsets,
   // a group whose K range is empty then leaves its rows untouched.
   int32_t accumulate;
+  // Phase 2, not with accumulate: out holds bf16 (round to nearest even of the fp32 sums).
+  int32_t out_bf16;
 };
 
 struct GroupedParams {

@@ -66,12 +66,14 @@ class Grads:
     ds_down: Optional[torch.Tensor] = None   # [S, d, Fs]
 
     @classmethod
-    def empty(cls, s: N.MoEShape, device):
+    def empty(cls, s: N.MoEShape, device, weight_dtype=torch.float32):
+        """weight_dtype: of the expert weight gradients (bf16 for MOE_GRAD_WRITE_BF16); the rest is fp32."""
         f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=device)
+        w = lambda *sh: torch.empty(sh, dtype=weight_dtype, device=device)
         E, d, F, S, Fs = s.n_experts, s.d_model, s.d_ff, s.n_shared, s.d_ff_shared
-        g = cls(f(s.n_tokens, d), f(E, d), f(E), f(E, F, d), f(E, F, d), f(E, d, F))
+        g = cls(f(s.n_tokens, d), f(E, d), f(E), w(E, F, d), w(E, F, d), w(E, d, F))
         if S:
-            g.ds_gate, g.ds_up, g.ds_down = f(S, Fs, d), f(S, Fs, d), f(S, d, Fs)
+            g.ds_gate, g.ds_up, g.ds_down = w(S, Fs, d), w(S, Fs, d), w(S, d, Fs)
         return g
 
 
@@ -102,7 +104,7 @@ class MoELayer:
             raise N.MoEError("moe_workspace_bytes", N.MOE_ERR_INVALID_ARG, "invalid shape")
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.out = Outputs.empty(s.n_tokens, s.d_model, s.n_experts, s.top_k, self.device)
-        self.grads = self.bws = None
+        self.grads = self.grads_bf16 = self.bws = None
         self.gu = None          # fp32 G and U kept by a training forward (moe_forward_train)
         self.gu_valid = False   # whether self.gu belongs to the last forward
 
@@ -185,27 +187,37 @@ class MoELayer:
         return o
 
     def backward(self, x: torch.Tensor, dy: torch.Tensor, aux_coef: float = 0.0, accumulate: bool = False,
-                 stream=None) -> Grads:
+                 bf16_weight_grads: bool = False, stream=None) -> Grads:
         """Gradients (moe_backward) of sum(dy * y) + aux_coef * balance statistic for the last
         forward(x) of this bf16 layer, whose routing in self.out it reuses (and its saved gate and up
         values, after forward(..., save_for_backward=True)). The gradient buffers and the backward
         workspace are allocated on first use and reused. accumulate: add the weight gradients to the
-        buffers (which start as zeros) instead of overwriting them; dx is always overwritten."""
+        buffers (which start as zeros) instead of overwriting them; dx is always overwritten.
+        bf16_weight_grads: the expert weight gradients as bf16 (separate buffers; not with accumulate)."""
+        if accumulate and bf16_weight_grads:
+            raise ValueError("bf16 weight gradients are written, not accumulated")
         if self.fp8 is not None or self.int4 is not None:
             raise ValueError("the backward pass needs the bf16 expert weights")
         if x.shape[0] != self.shape.n_tokens or tuple(dy.shape) != (self.shape.n_tokens, self.shape.d_model):
             raise ValueError("x and dy must match the last forward's tokens")
-        if self.grads is None:
-            self.grads = Grads.empty(self.shape, self.device)
-            for t in vars(self.grads).values():
-                if t is not None:
-                    t.zero_()
+        if self.bws is None:
             self.bws = torch.empty(max(1, N.backward_workspace_bytes(self.shape)), dtype=torch.uint8,
                                    device=self.device)
-        g, o = self.grads, self.out
+        if bf16_weight_grads:
+            if self.grads_bf16 is None:
+                self.grads_bf16 = Grads.empty(self.shape, self.device, torch.bfloat16)
+            g, mode = self.grads_bf16, N.MOE_GRAD_WRITE_BF16
+        else:
+            if self.grads is None:
+                self.grads = Grads.empty(self.shape, self.device)
+                for t in vars(self.grads).values():
+                    if t is not None:
+                        t.zero_()
+            g, mode = self.grads, (N.MOE_GRAD_ACCUMULATE if accumulate else N.MOE_GRAD_WRITE)
+        o = self.out
         N.moe_backward(self.shape, x, self.w_router, self.logit_bias, self.w_gate, self.w_up, self.w_down,
                        self.s_gate, self.s_up, self.s_down, o.topk_idx, o.topk_w, o.counts, o.offsets, o.perm,
-                       o.slot_pos, dy, self.gu if self.gu_valid else None, aux_coef, accumulate, g.dx,
+                       o.slot_pos, dy, self.gu if self.gu_valid else None, aux_coef, mode, g.dx,
                        g.dw_router, g.d_logit_bias, g.dw_gate, g.dw_up, g.dw_down, g.ds_gate, g.ds_up, g.ds_down,
                        self.bws, stream=stream)
         return g

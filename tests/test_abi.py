@@ -173,7 +173,8 @@ def test_backward_entry_point_validates():
         ws_bytes, None)
     assert bw(s32) == N.MOE_ERR_UNSUPPORTED
     assert bw(s, aux=float("nan")) == N.MOE_ERR_INVALID_ARG
-    assert bw(s, acc=2) == N.MOE_ERR_INVALID_ARG                       # accumulate is 0 or 1
+    assert bw(s, acc=3) == N.MOE_ERR_INVALID_ARG                       # unknown grad_mode
+    assert bw(s, acc=-1) == N.MOE_ERR_INVALID_ARG
     assert bw(s, ptr=None) == N.MOE_ERR_INVALID_ARG                    # dx missing
     assert bw(shp(n_shared=1, d_ff_shared=128)) == N.MOE_ERR_INVALID_ARG  # shared gradients missing
     assert bw(s, ws_bytes=16) == N.MOE_ERR_WORKSPACE

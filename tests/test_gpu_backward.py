@@ -338,3 +338,27 @@ def test_training_forward_keeps_gate_up_and_backward_uses_them():
     Ms = term_magnitudes(x64, dy, lambda s: (np.arange(N), np.ones(N)), *shared, [0])
     for i, name in enumerate(("ds_gate", "ds_up", "ds_down")):
         check_terms(P.to_host(getattr(g, name))[0], getattr(ref, name)[0], Ms[0][i], name)
+
+
+def test_backward_bf16_weight_grads_are_the_rounded_fp32_ones():
+    """MOE_GRAD_WRITE_BF16: every expert weight gradient is the round-to-nearest-even bf16 of the fp32
+    value MOE_GRAD_WRITE stores (torch's fp32 -> bf16 cast), bit for bit; dx and the router gradients
+    are the write mode's, bit for bit."""
+    cfg = mi.small_config("bwd_bf16", dtype="bf16", layer_id=815, x_id=815, n_tokens=320, n_experts=64, top_k=2,
+                          d_model=128, d_ff=192, n_shared=1, d_ff_shared=64, capacity=30, select_bias=0.1)
+    layer, x = mi.make_layer(cfg), mi.make_x(cfg)
+    dy = torch.from_numpy(make_dy(cfg.n_tokens, cfg.d_model, 13).astype(np.float32)).to(DEV)
+    L = MoELayer.from_numpy(moe.shape_for(cfg), layer, DEV)
+    xd = to_device(x, DEV)
+    L.forward(xd)
+    log(f"{cfg.name}: moe_backward in fp32 then bf16 weight-gradient mode")
+    g32 = {k: v.clone() for k, v in vars(L.backward(xd, dy, 0.25)).items() if v is not None}
+    g16 = L.backward(xd, dy, 0.25, bf16_weight_grads=True)
+    torch.cuda.synchronize()
+    for name in ("dx", "dw_router", "d_logit_bias"):
+        assert torch.equal(getattr(g16, name).view(torch.int32), g32[name].view(torch.int32)), name
+    for name in ("dw_gate", "dw_up", "dw_down", "ds_gate", "ds_up", "ds_down"):
+        got = getattr(g16, name)
+        assert got.dtype == torch.bfloat16, name
+        want = g32[name].to(torch.bfloat16)
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), name
