@@ -18,8 +18,10 @@
 // dx += dl W_r. The rounding of h to bf16 passes the gradient unchanged.
 //
 // Rounding points (bf16 operands of the MFMA GEMMs, fp32 accumulation): dy,
-// w * dy, h, dG and dU are rounded to bf16 where they feed a GEMM; the
-// element-wise steps and every reduction here run in fp32, in a fixed order.
+// w * dy, h, dG and dU are rounded to bf16 where they feed a GEMM; dl feeds the
+// router products as two bf16 parts (hi + lo, about 2^-16 relative) when those
+// run as GEMMs. The element-wise steps and every reduction here run in fp32, in
+// a fixed order.
 #include <math.h>
 
 #include <algorithm>
