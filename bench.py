@@ -207,6 +207,50 @@ def measured_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_backward_baseline(cfg, layer, x, n_sample=256):
+    """The backward oracle as it stands (oracle/moe_backward.layer_backward, fp64) on the first
+    n_sample tokens of the workload: routing of the sample, then the gradients of every parameter
+    for a seeded bf16-valued dy, including the fp64 upcast of every expert. Skipped when those
+    fp64 weights would not fit comfortably in host memory (the DeepSeek-shaped layers)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import moe_inputs as mi
+    from oracle import moe_backward as B
+    from oracle import moe_oracle as O
+
+    fp64_bytes = 8 * 3 * (cfg.n_experts * cfg.d_model * cfg.d_ff + cfg.n_shared * cfg.d_model * cfg.d_ff_shared)
+    if fp64_bytes > 24e9:
+        return {"skipped": f"the oracle's fp64 expert weights ({fp64_bytes / 1e9:.0f} GB) exceed the host budget"}
+    n = min(cfg.n_tokens, n_sample)
+    dy = O.bf16_round(np.random.default_rng(1234).standard_normal((n, cfg.d_model)))
+
+    class View:
+        def __init__(self, a):
+            self.a = a
+
+        def __getitem__(self, e):
+            return mi.to_f64(self.a[e])
+
+        def __len__(self):
+            return len(self.a)
+
+    t = time.perf_counter()
+    x64 = mi.to_f64(x[:n])
+    wr = mi.to_f64(layer.w_router)
+    r = O.route(x64, wr, cfg.top_k, layer.logit_bias, layer.select_bias, cfg.renormalize)
+    shared = None
+    if layer.s_gate is not None:
+        shared = (View(layer.s_gate), View(layer.s_up), View(layer.s_down))
+    B.layer_backward(x64, wr, View(layer.w_gate), View(layer.w_up), View(layer.w_down), r.idx, dy, shared=shared,
+                     logit_bias=layer.logit_bias, capacity=cfg.capacity, renormalize=cfg.renormalize, round_h=True,
+                     aux_coef=0.01)
+    dt = time.perf_counter() - t
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("internal_api") == "openblas"] or [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {cfg.n_tokens} tokens of the same layer: route, then layer_backward in fp64 "
+                      f"(every expert upcast), {dt:.1f} s"}
+
+
 def cpu_baseline(cfg, layer, x, budget_s=20.0, weights="bf16"):
     """The oracle as it stands (grouped fp64 form) on the first rows of the workload.
 
@@ -409,6 +453,8 @@ def main():
         del L, xd
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(cfg, layer, x, args.cpu_budget, weights)
+        if isinstance(out.get("backward"), dict) and "ms" in out["backward"]:
+            out["backward"]["cpu_baseline"] = cpu_backward_baseline(cfg, layer, x)
     print(json.dumps(out), flush=True)
 
 
