@@ -167,6 +167,12 @@ def oracle_grads(cfg, layer, x, dy, aux, idx):
     (dict(n_tokens=64, n_experts=256, top_k=8, d_model=256, d_ff=128, n_shared=1, d_ff_shared=128,
           select_bias=0.1), 0.2),                                                    # 256 experts, top-8
     (dict(n_tokens=384, n_experts=64, top_k=1, d_model=128, d_ff=256, logit_skew=1.5, capacity=16), 0.05),
+    # degenerate shapes
+    (dict(n_tokens=1, n_experts=8, top_k=2, d_model=64, d_ff=64), 0.1),                    # one token
+    (dict(n_tokens=50, n_experts=1, top_k=1, d_model=128, d_ff=128), 0.2),                  # one expert: dl = 0
+    (dict(n_tokens=40, n_experts=4, top_k=4, d_model=64, d_ff=128), 0.1),                   # k = E
+    (dict(n_tokens=70, n_experts=8, top_k=2, d_model=64, d_ff=64, n_shared=2, d_ff_shared=64), 0.0),  # S = 2
+    (dict(n_tokens=100, n_experts=8, top_k=2, d_model=64, d_ff=128, capacity=1), 0.3),      # capacity 1
 ])
 def test_backward_small_layers_every_element(kw, aux):
     cfg = mi.small_config("bwd", dtype="bf16", layer_id=800 + kw["n_tokens"] % 11, x_id=800, **kw)
