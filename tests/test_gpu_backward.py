@@ -2,7 +2,14 @@
 
 The oracle runs on the GPU forward's own top-k (forced routing) with the bf16
 rounding of h, in fp64. Bounds:
-* dx and dW_r, per row: max |gpu - ref| <= 2e-2 * RMS(ref row);
+* dx and dW_r, per row: max |gpu - ref| <= 2e-2 * RMS(ref row); for dW_r
+  plus 2^-20 * M entry by entry, M the sum of the magnitudes of the entry's
+  terms along the whole router chain (router_magnitudes). Under
+  renormalisation the logit gradient of an expert that the token did not
+  select vanishes by cancellation, so a dW_r row of an expert that no token
+  with a kept copy selected is pure rounding residue (fp64 in the oracle,
+  fp32 on the GPU): 2^-20 = 16 fp32 units admits that residue and adds at
+  most a few thousandths of RMS(row) to the other rows;
 * d(logit bias): max |gpu - ref| <= 2e-2 * RMS(ref);
 * expert weight gradients, entry by entry: |gpu - ref| <= 2^-6 * M, where M
   is the sum of the magnitudes of the entry's terms (|dG|^T |X| for dWg,
@@ -49,17 +56,19 @@ def log(msg):
     print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
 
 
-def check_rows(got, ref, name, tol=TOL):
+def check_rows(got, ref, name, tol=TOL, floor=None):
+    """Entry by entry |got - ref| <= tol * RMS(ref row) (+ floor, an array of ref's shape)."""
     got = np.asarray(got, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
     ref = np.asarray(ref, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
     assert np.all(np.isfinite(got)), name
     zero = ~np.any(ref != 0, axis=1)
     assert np.all(got[zero] == 0), f"{name}: rows with a zero reference are not zero"
     rms = np.sqrt(np.mean(ref ** 2, axis=1))
-    err = np.max(np.abs(got - ref), axis=1)
-    bad = (~zero) & (err > tol * rms)
-    worst = float(np.max(np.where(zero, 0.0, err / np.where(rms > 0, rms, 1.0)))) if got.size else 0.0
-    assert not np.any(bad), f"{name}: {int(bad.sum())} rows over the bound, worst err/rms {worst:.3e}"
+    bound = tol * rms[:, None] + (0.0 if floor is None else np.reshape(floor, ref.shape))
+    ratio = np.abs(got - ref) / np.where(bound > 0, bound, 1.0)
+    bad = (~zero) & np.any(ratio > 1.0, axis=1)
+    worst = float(np.max(np.where(zero[:, None], 0.0, ratio))) if got.size else 0.0
+    assert not np.any(bad), f"{name}: {int(bad.sum())} rows over the bound, worst err/bound {worst:.3e}"
     return worst
 
 
@@ -85,6 +94,41 @@ def term_magnitudes(x64, dy, rows_of, w_gate, w_up, w_down, experts):
         _, H, _, dG, dU = B.expert_backward_terms(X, dO, w_gate[e], w_up[e], w_down[e], True)
         out[e] = (np.abs(dG).T @ np.abs(X), np.abs(dU).T @ np.abs(X), np.abs(dO).T @ np.abs(H))
     return out
+
+
+def router_magnitudes(cfg, layer, x64, dy, idx, aux):
+    """Term magnitudes of the router gradients: (|dW_r| bound scale [E, d], |d logit bias| scale [E]).
+
+    Each step of the chain is replaced by the sum of the magnitudes of its terms:
+    dw_tj = <dy_t, O_tj> by sum_f |h_f| (|dy_t| |W_down|)_f, the renormalisation
+    by (A_j + sum_i w_i A_i) / sum(sel), the softmax backward by
+    p_e (A_e + sum_j p_j A_j), and the products with x by |dl|^T |x|. An error of
+    relative size r in every dw term (an h one bf16 step off the oracle's) then
+    moves each entry by at most r times its scale, also where the entry itself
+    vanishes by cancellation (experts that no token with a kept copy selected,
+    under renormalisation)."""
+    N, k, E = idx.shape[0], cfg.top_k, cfg.n_experts
+    p = O.softmax(O.router_logits(x64, mi.to_f64(layer.w_router), layer.logit_bias))
+    sel = np.take_along_axis(p, idx, axis=1)
+    ssum = sel.sum(axis=1, keepdims=True)
+    w = sel / ssum if cfg.renormalize else sel
+    (wg, wu, wd), _ = P.oracle_views(layer)
+    g = O.group(idx, E, cfg.capacity)
+    A = np.zeros((N, k))
+    for e in range(E):
+        c = g.perm[g.offsets[e]:g.offsets[e + 1]]
+        if len(c) == 0:
+            continue
+        t = c // k
+        _, H, _, _, _ = B.expert_backward_terms(x64[t], dy[t], wg[e], wu[e], wd[e], True)
+        A[t, c % k] = np.sum(np.abs(H) * (np.abs(dy[t]) @ np.abs(np.asarray(wd[e], dtype=np.float64))), axis=1)
+    Ms = (A + np.sum(w * A, axis=1, keepdims=True)) / ssum if cfg.renormalize else A
+    Mp = np.zeros_like(p)
+    np.put_along_axis(Mp, idx, Ms, axis=1)
+    if aux:
+        Mp += abs(aux) * E * (O.expert_counts(idx, E) / (N * k))[None, :] / N
+    Mdl = p * (Mp + np.sum(p * Mp, axis=1, keepdims=True))
+    return Mdl.T @ np.abs(x64), Mdl.sum(axis=0)
 
 
 def routed_rows(cfg, layer, x64, idx):
@@ -182,9 +226,10 @@ def test_backward_small_layers_every_element(kw, aux):
     t = time.time()
     ref = oracle_grads(cfg, layer, x, dy, aux, gpu["idx"])
     worst = {}
-    for name in ("dx", "dw_router"):
-        worst[name] = check_rows(gpu[name], getattr(ref, name), name)
     x64, idx = mi.to_f64(x), np.asarray(gpu["idx"], dtype=np.int64)
+    worst["dx"] = check_rows(gpu["dx"], ref.dx, "dx")
+    Mr, _ = router_magnitudes(cfg, layer, x64, dy, idx, aux)
+    worst["dw_router"] = check_rows(gpu["dw_router"], ref.dw_router, "dw_router", floor=2.0 ** -20 * Mr)
     (wg, wu, wd), shared = P.oracle_views(layer)
     M = term_magnitudes(x64, dy, routed_rows(cfg, layer, x64, idx), wg, wu, wd, range(cfg.n_experts))
     for i, name in enumerate(("dw_gate", "dw_up", "dw_down")):
@@ -368,3 +413,51 @@ def test_backward_bf16_weight_grads_are_the_rounded_fp32_ones():
         assert got.dtype == torch.bfloat16, name
         want = g32[name].to(torch.bfloat16)
         assert torch.equal(got.view(torch.int16), want.view(torch.int16)), name
+
+
+def _random_cases(n=16, seed=2024):
+    """Seeded random small layers: every knob of the layer drawn at once."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 4, 8, 16, 64]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        N = int(rng.choice([1, 7, 64, 128, 200, 333]))
+        kw = dict(n_tokens=N, n_experts=E, top_k=k, d_model=int(rng.choice([64, 128, 192])),
+                  d_ff=int(rng.choice([64, 128, 256])), renormalize=bool(rng.integers(0, 2)) or k == 1)
+        if rng.random() < 0.4:
+            kw.update(n_shared=int(rng.integers(1, 3)), d_ff_shared=int(rng.choice([64, 128])))
+        if rng.random() < 0.4:
+            kw["capacity"] = int(rng.integers(1, max(2, 2 * N * k // E)))
+        if rng.random() < 0.3:
+            kw["select_bias"] = 0.05
+        if rng.random() < 0.3:
+            kw["logit_skew"] = 1.0
+        cases.append((i, kw, float(rng.choice([0.0, 0.1, 0.5]))))
+    return cases
+
+
+@pytest.mark.parametrize("i,kw,aux", _random_cases(), ids=lambda v: str(v) if isinstance(v, int) else None)
+def test_backward_random_small_layers(i, kw, aux):
+    cfg = mi.small_config(f"bwd_rand{i}", dtype="bf16", layer_id=900 + i, x_id=900 + i, **kw)
+    layer, x = mi.make_layer(cfg), mi.make_x(cfg)
+    dy = make_dy(cfg.n_tokens, cfg.d_model, 100 + i)
+    gpu = run_backward(cfg, layer, x, dy, aux)
+    ref = oracle_grads(cfg, layer, x, dy, aux, gpu["idx"])
+    x64, idx = mi.to_f64(x), np.asarray(gpu["idx"], dtype=np.int64)
+    check_rows(gpu["dx"], ref.dx, "dx")
+    Mr, _ = router_magnitudes(cfg, layer, x64, dy, idx, aux)
+    check_rows(gpu["dw_router"], ref.dw_router, "dw_router", floor=2.0 ** -20 * Mr)
+    lb = ref.d_logit_bias
+    assert np.max(np.abs(gpu["d_logit_bias"] - lb)) <= TOL * max(np.sqrt(np.mean(lb ** 2)), 1e-30)
+    (wg, wu, wd), shared = P.oracle_views(layer)
+    M = term_magnitudes(x64, dy, routed_rows(cfg, layer, x64, idx), wg, wu, wd, range(cfg.n_experts))
+    for j, name in enumerate(("dw_gate", "dw_up", "dw_down")):
+        for e in range(cfg.n_experts):
+            check_terms(gpu[name][e], getattr(ref, name)[e], M[e][j], f"{name}[{e}]")
+    if cfg.n_shared:
+        Ms = term_magnitudes(x64, dy, lambda s: (np.arange(cfg.n_tokens), np.ones(cfg.n_tokens)), *shared,
+                             range(cfg.n_shared))
+        for j, name in enumerate(("ds_gate", "ds_up", "ds_down")):
+            for s_ in range(cfg.n_shared):
+                check_terms(gpu[name][s_], getattr(ref, name)[s_], Ms[s_][j], f"{name}[{s_}]")
