@@ -1000,6 +1000,20 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
 // gate|up time and 30% less down time than 256-row tiles.
 bool large_tiles(long long rows, int groups) { return rows / std::max(1, groups) >= 192; }
 
+// Gate|up of few, tall segments (bf16): 320-row tiles when they need at least
+// 20% fewer m-tiles than 256-row ones. Tile time there scales with the tile
+// count more than with the rows: the Mixtral-shaped segments of 1030-1052 rows
+// take five 208-row tiles or four 260-row ones, and the four are 4-5% faster
+// in all (a 260-row tile costs ~1.2x a 208-row one). The counts are estimated
+// from the mean rows per segment plus 2% (the segments' spread under random
+// routing). Down keeps 256-row tiles: at 320 rows its K loop spills.
+bool tall_tiles(long long rows, int groups) {
+  const long long m100 = rows * 102 / std::max(1, groups);  // mean rows + 2%, in hundredths
+  if (m100 < 76800) return false;
+  const long long t256 = (m100 + 25599) / 25600, t320 = (m100 + 31999) / 32000;
+  return t320 * 5 <= t256 * 4;
+}
+
 template <int WQ>
 void launch_class(const GroupedParams& p, int phase, hipStream_t stream) {
   if constexpr (WQ == 4) {
@@ -1011,8 +1025,13 @@ void launch_class(const GroupedParams& p, int phase, hipStream_t stream) {
     // tile run in step, so their copies of it hit in L2
     GroupedParams q = p;
     q.balance_m = 1;
-    if (WQ == 0 && phase == 2 && p.set[0].b_nmajor) launch_mfma<256, 256, 64, 2, 4, 2, 0, true, 1, true>(q, 2, 1, stream);
-    else launch_mfma<256, 256, 64, 2, 4, 2, WQ, true>(q, phase, 1, stream);
+    if (WQ == 0 && phase == 2 && p.set[0].b_nmajor) {
+      launch_mfma<256, 256, 64, 2, 4, 2, 0, true, 1, true>(q, 2, 1, stream);
+    } else if (WQ == 0 && phase == 1 && tall_tiles(p.set[0].max_rows, p.set[0].n_groups)) {
+      if constexpr (WQ == 0) launch_mfma<320, 256, 64, 2, 4, 2, 0, true>(q, 1, 1, stream);
+    } else {
+      launch_mfma<256, 256, 64, 2, 4, 2, WQ, true>(q, phase, 1, stream);
+    }
   } else if (WQ == 0 && phase == 2 && p.set[0].b_nmajor) {
     launch_mfma<64, 256, 64, 1, 4, 3, 0, false, 1, true>(p, 2, 1, stream);
   } else {

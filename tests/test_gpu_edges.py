@@ -119,18 +119,23 @@ def _run_grouped(cfg, lay, x, offs, perm, rpt, max_rows, extra_ws=0):
     return P.to_host(out)
 
 
-@pytest.mark.parametrize("dtype,sizes,extra_ws", [
-    ("bf16", [0, 1, 255, 256, 257, 0, 513, 2, 300], 0),          # mean >= 128 rows: 256-row tiles
-    ("bf16", [0, 1, 63, 64, 65, 0, 3, 127, 0, 0], 0),            # small mean: 64-row tiles
-    ("bf16", [0, 1, 255, 256, 257, 0, 513, 2, 300], 64 << 20),   # the same, tail tiles split along K
-    ("bf16", [0, 1, 63, 64, 65, 0, 3, 127, 0, 0], 1 << 20),      # split, workspace for a few parts only
-    ("f32", [0, 1, 31, 32, 33, 0, 65], 1 << 20),                 # fp32: never split
+@pytest.mark.parametrize("dtype,sizes,extra_ws,slack", [
+    ("bf16", [0, 1, 255, 256, 257, 0, 513, 2, 300], 0, 0),          # mean >= 128 rows: 256-row tiles
+    ("bf16", [0, 1, 63, 64, 65, 0, 3, 127, 0, 0], 0, 0),            # small mean: 64-row tiles
+    ("bf16", [0, 1, 255, 256, 257, 0, 513, 2, 300], 64 << 20, 0),   # the same, with split workspace
+    ("bf16", [0, 1, 63, 64, 65, 0, 3, 127, 0, 0], 1 << 20, 0),      # tail tiles split along K (grid 2x the
+                                                                    # tiles), workspace for a few parts only
+    ("f32", [0, 1, 31, 32, 33, 0, 65], 1 << 20, 0),                 # fp32: never split
+    ("bf16", [1030, 1052, 1041, 1049], 0, 0),                       # tall segments: 320-row gate|up tiles
+    ("bf16", [1279, 0, 1100, 33, 1250, 1270], 0, 0),                # the same class, ragged, empty, tiny
+    ("bf16", [1279, 0, 1100, 33, 1250, 1270], 64 << 20, 3 * 4932),  # max_rows 4x the rows: a grid 4x the
+                                                                    # tiles, so both phases split along K
 ])
-def test_grouped_segment_edges(dtype, sizes, extra_ws):
+def test_grouped_segment_edges(dtype, sizes, extra_ws, slack):
     d, F = 128, 256
     cfg, lay, x, offs, perm = _grouped_case(sizes, d, F, dtype)
     rpt = 3
-    out = _run_grouped(cfg, lay, x, offs, perm, rpt, int(offs[-1]), extra_ws)
+    out = _run_grouped(cfg, lay, x, offs, perm, rpt, int(offs[-1]) + slack, extra_ws)
     x64 = mi.to_f64(x)
     ref = np.zeros((int(offs[-1]), d))
     for g in range(len(sizes)):
