@@ -373,7 +373,8 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int G, long long cap_
 // multiplied by its weight row's scale, and with int4 weights the offset
 // sums corr[i] (136 * sum(x) of each row) are subtracted before that (none
 // when corr is NULL: the K-parts of split tiles are stored already reduced).
-template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE, int FM, int NB, bool OBF = false>
+template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE, int FM, int NB, bool OBF = false,
+          int ACCM = 0>
 __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetView& S, const TileGeom& t,
                                            int d, int lane, int wm, int wn, const f32x16_t* corr = nullptr) {
   constexpr bool WS = WQ != 0, W4 = WQ == 4;
@@ -404,8 +405,8 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
   auto rows = [&](auto check) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      if constexpr (!P1 && !WS) {
-        if (S.accum) {
+      if constexpr (!P1 && !WS && ACCM != 0) {
+        if (ACCM == 1 || S.accum) {
           // out += product: the block's old values are all loaded before the first
           // store (a load after a store to another row would wait for that store)
           float old[16][FN];
@@ -487,7 +488,7 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
 // so that fewer copies queue at once behind the barrier (3-5% faster on
 // 256 x 256 tiles; the second half of the step still covers their latency).
 template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB, int WQ, bool P1, bool SPREAD,
-          bool NMAJ = false, bool SAVE = false, bool OBF = false>
+          bool NMAJ = false, bool SAVE = false, bool OBF = false, int ACCM = 0>
 __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(GroupedParams p) {
   constexpr bool W8 = WQ == 8, W4 = WQ == 4, WS = WQ != 0;
   using BT = typename std::conditional<WS, uint8_t, bf16_t>::type;  // weight storage unit
@@ -571,7 +572,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     const int nk_all = K / BK;
     // accumulating weight gradients: a group with no rows adds nothing (a K-part
     // of a split tile still writes its zero sum for the part-sum kernel)
-    if (!P1 && S.accum && nk_all == 0 && part < 0) continue;
+    if (!P1 && (ACCM == 1 || (ACCM == 2 && S.accum)) && nk_all == 0 && part < 0) continue;
     // this unit's K steps: all of them, or part `part` of sp.S
     const int k_lo = part < 0 ? 0 : (int)((long long)part * nk_all / sp.S);
     const int nk = part < 0 ? nk_all : (int)((long long)(part + 1) * nk_all / sp.S) - k_lo;
@@ -787,7 +788,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
             dst[((i * NB + j) * 16 + v) * NT + tid] = W4 ? acc[i][j][v] - corr[i][v] : acc[i][j][v];
       continue;
     }
-    store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF>(acc, S, tg, d, lane, wm, wn, corr);
+    store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF, ACCM>(acc, S, tg, d, lane, wm, wn, corr);
   }
 }
 
@@ -810,7 +811,7 @@ __global__ __launch_bounds__(256) void split_sum_kernel(float* __restrict__ ws) 
 // The epilogue of the split tail tiles of the launch before it (same
 // parameters, `main_grid` workgroups), from part 0: workgroup b finishes
 // tail tile b. Workgroups past the tail exit.
-template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE = false, bool OBF = false>
+template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE = false, bool OBF = false, int ACCM = 0>
 __global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedParams p, int main_grid) {
   constexpr int TM = BM / WGM, FM = TM / 32;
   constexpr int BH = P1 ? BN / 2 : BN;
@@ -841,7 +842,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedPar
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = src[((size_t)(i * NB + j) * 16 + v) * NT];
-  store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF>(acc, S, tg, d, lane, wm, wn);
+  store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF, ACCM>(acc, S, tg, d, lane, wm, wn);
 }
 
 // =====================================================================  fp32 SIMT
@@ -961,10 +962,14 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
   // the training forward (bf16 phase 1 with g_save) runs its own instantiation: the
   // inference kernels keep their code unchanged
   const bool save = WQ == 0 && phase == 1 && p.set[0].g_save;
-  const bool obf = WQ == 0 && phase == 2 && !NMAJ && p.set[0].out_bf16;  // bf16 weight gradients
+  const bool obf = WQ == 0 && phase == 2 && !NMAJ && p.set[0].out_bf16;
+  // accumulating weight gradients (bf16, phase 2): an instantiation of its own, so
+  // that the inference down kernels carry no accumulate epilogue; the N-major
+  // kernels (backward only) test the flag at run time
+  const bool accum = WQ == 0 && phase == 2 && !NMAJ && p.set[0].accumulate;
   if constexpr (NMAJ)
-    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, true>), dim3(grid),
-                       dim3(WGM * WGN * 64), 0, st, p);
+    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, true, false, false, 2>),
+                       dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
   else if (phase == 1 && save)
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD, false, WQ == 0>),
                        dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
@@ -973,6 +978,10 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
                        dim3(WGM * WGN * 64), 0, st, p);
   else if (obf)
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, false, false, WQ == 0>),
+                       dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
+  else if (accum)
+    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, false, false, false,
+                                            WQ == 0 ? 1 : 0>),
                        dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
   else
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD>), dim3(grid),
@@ -988,6 +997,12 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
     else if (obf)
       hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false, false, WQ == 0>), dim3(grid),
                          dim3(WGM * WGN * 64), 0, st, p, grid);
+    else if (NMAJ)
+      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false, false, false, 2>), dim3(grid),
+                         dim3(WGM * WGN * 64), 0, st, p, grid);
+    else if (accum)
+      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false, false, false, WQ == 0 ? 1 : 0>),
+                         dim3(grid), dim3(WGM * WGN * 64), 0, st, p, grid);
     else
       hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false>), dim3(grid), dim3(WGM * WGN * 64),
                          0, st, p, grid);
@@ -1000,13 +1015,13 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
 // gate|up time and 30% less down time than 256-row tiles.
 bool large_tiles(long long rows, int groups) { return rows / std::max(1, groups) >= 192; }
 
-// Gate|up of few, tall segments (bf16): 320-row tiles when they need at least
-// 20% fewer m-tiles than 256-row ones. Tile time there scales with the tile
-// count more than with the rows: the Mixtral-shaped segments of 1030-1052 rows
-// take five 208-row tiles or four 260-row ones, and the four are 4-5% faster
-// in all (a 260-row tile costs ~1.2x a 208-row one). The counts are estimated
-// from the mean rows per segment plus 2% (the segments' spread under random
-// routing). Down keeps 256-row tiles: at 320 rows its K loop spills.
+// Few, tall segments (bf16 layers): 320-row tiles when they need at least 20%
+// fewer m-tiles than 256-row ones. Tile time there scales with the tile count
+// more than with the rows: the Mixtral-shaped segments of 1030-1052 rows take
+// five 208-row tiles or four 260-row ones, and the four are faster in all (gate|up
+// 1-5%, down 2-3%; a 260-row tile costs ~1.2x a 208-row one). The counts are
+// estimated from the mean rows per segment plus 2% (the segments' spread under
+// random routing). The weight-gradient GEMMs keep 256-row tiles.
 bool tall_tiles(long long rows, int groups) {
   const long long m100 = rows * 102 / std::max(1, groups);  // mean rows + 2%, in hundredths
   if (m100 < 76800) return false;
@@ -1027,8 +1042,8 @@ void launch_class(const GroupedParams& p, int phase, hipStream_t stream) {
     q.balance_m = 1;
     if (WQ == 0 && phase == 2 && p.set[0].b_nmajor) {
       launch_mfma<256, 256, 64, 2, 4, 2, 0, true, 1, true>(q, 2, 1, stream);
-    } else if (WQ == 0 && phase == 1 && tall_tiles(p.set[0].max_rows, p.set[0].n_groups)) {
-      if constexpr (WQ == 0) launch_mfma<320, 256, 64, 2, 4, 2, 0, true>(q, 1, 1, stream);
+    } else if (WQ == 0 && !p.set[0].k_offsets && tall_tiles(p.set[0].max_rows, p.set[0].n_groups)) {
+      if constexpr (WQ == 0) launch_mfma<320, 256, 64, 2, 4, 2, 0, true>(q, phase, 1, stream);
     } else {
       launch_mfma<256, 256, 64, 2, 4, 2, WQ, true>(q, phase, 1, stream);
     }
