@@ -56,7 +56,6 @@ struct SetView {  // the fields of one SegSet, picked with selects rather than a
   const int32_t* kofs;  // weight-gradient mode (phase 2): per-group K ranges
   int32_t bsplit;       // N-major weights: rows >= bsplit come from wu (0: none)
   int32_t urows;        // rows per group of a uniform set
-  int32_t accum;        // phase 2: out += product
   float* gsave;         // phase 1: fp32 gate and up values (optional)
   float* usave;
 };
@@ -77,7 +76,6 @@ __device__ __forceinline__ SetView pick(const GroupedParams& p, int si) {
   v.kofs = si ? p.set[1].k_offsets : p.set[0].k_offsets;
   v.bsplit = si ? p.set[1].b_split : p.set[0].b_split;
   v.urows = si ? p.set[1].uniform_rows : p.set[0].uniform_rows;
-  v.accum = si ? p.set[1].accumulate : p.set[0].accumulate;
   v.gsave = si ? p.set[1].g_save : p.set[0].g_save;
   v.usave = si ? p.set[1].u_save : p.set[0].u_save;
   return v;
@@ -374,7 +372,7 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int G, long long cap_
 // sums corr[i] (136 * sum(x) of each row) are subtracted before that (none
 // when corr is NULL: the K-parts of split tiles are stored already reduced).
 template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE, int FM, int NB, bool OBF = false,
-          int ACCM = 0>
+          bool ACC = false>
 __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetView& S, const TileGeom& t,
                                            int d, int lane, int wm, int wn, const f32x16_t* corr = nullptr) {
   constexpr bool WS = WQ != 0, W4 = WQ == 4;
@@ -405,30 +403,28 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
   auto rows = [&](auto check) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      if constexpr (!P1 && !WS && ACCM != 0) {
-        if (ACCM == 1 || S.accum) {
-          // out += product: the block's old values are all loaded before the first
-          // store (a load after a store to another row would wait for that store)
-          float old[16][FN];
+      if constexpr (!P1 && !WS && ACC) {
+        // out += product: the block's old values are all loaded before the first
+        // store (a load after a store to another row would wait for that store)
+        float old[16][FN];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
-            const bool ok = !decltype(check)::value || r < t.mvalid;
-            const float* orow = S.out + (size_t)(t.start + t.m0 + r) * d + col0;
+        for (int v = 0; v < 16; ++v) {
+          const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
+          const bool ok = !decltype(check)::value || r < t.mvalid;
+          const float* orow = S.out + (size_t)(t.start + t.m0 + r) * d + col0;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) old[v][j] = (ok && col0 + j * 32 < ncols) ? orow[j * 32] : 0.f;
-          }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
-            if (decltype(check)::value && r >= t.mvalid) continue;
-            float* orow = S.out + (size_t)(t.start + t.m0 + r) * d + col0;
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-              if (col0 + j * 32 < ncols) orow[j * 32] = old[v][j] + acc[i][j][v];
-          }
-          continue;
+          for (int j = 0; j < FN; ++j) old[v][j] = (ok && col0 + j * 32 < ncols) ? orow[j * 32] : 0.f;
         }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
+          if (decltype(check)::value && r >= t.mvalid) continue;
+          float* orow = S.out + (size_t)(t.start + t.m0 + r) * d + col0;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            if (col0 + j * 32 < ncols) orow[j * 32] = old[v][j] + acc[i][j][v];
+        }
+        continue;
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -488,7 +484,7 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
 // so that fewer copies queue at once behind the barrier (3-5% faster on
 // 256 x 256 tiles; the second half of the step still covers their latency).
 template <int BM, int BN, int BK, int WGM, int WGN, int NS, int MINB, int WQ, bool P1, bool SPREAD,
-          bool NMAJ = false, bool SAVE = false, bool OBF = false, int ACCM = 0>
+          bool NMAJ = false, bool SAVE = false, bool OBF = false, bool ACC = false>
 __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(GroupedParams p) {
   constexpr bool W8 = WQ == 8, W4 = WQ == 4, WS = WQ != 0;
   using BT = typename std::conditional<WS, uint8_t, bf16_t>::type;  // weight storage unit
@@ -572,7 +568,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     const int nk_all = K / BK;
     // accumulating weight gradients: a group with no rows adds nothing (a K-part
     // of a split tile still writes its zero sum for the part-sum kernel)
-    if (!P1 && (ACCM == 1 || (ACCM == 2 && S.accum)) && nk_all == 0 && part < 0) continue;
+    if (ACC && nk_all == 0 && part < 0) continue;
     // this unit's K steps: all of them, or part `part` of sp.S
     const int k_lo = part < 0 ? 0 : (int)((long long)part * nk_all / sp.S);
     const int nk = part < 0 ? nk_all : (int)((long long)(part + 1) * nk_all / sp.S) - k_lo;
@@ -788,7 +784,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
             dst[((i * NB + j) * 16 + v) * NT + tid] = W4 ? acc[i][j][v] - corr[i][v] : acc[i][j][v];
       continue;
     }
-    store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF, ACCM>(acc, S, tg, d, lane, wm, wn, corr);
+    store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF, ACC>(acc, S, tg, d, lane, wm, wn, corr);
   }
 }
 
@@ -811,7 +807,7 @@ __global__ __launch_bounds__(256) void split_sum_kernel(float* __restrict__ ws) 
 // The epilogue of the split tail tiles of the launch before it (same
 // parameters, `main_grid` workgroups), from part 0: workgroup b finishes
 // tail tile b. Workgroups past the tail exit.
-template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE = false, bool OBF = false, int ACCM = 0>
+template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE = false, bool OBF = false, bool ACC = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedParams p, int main_grid) {
   constexpr int TM = BM / WGM, FM = TM / 32;
   constexpr int BH = P1 ? BN / 2 : BN;
@@ -842,7 +838,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedPar
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = src[((size_t)(i * NB + j) * 16 + v) * NT];
-  store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF, ACCM>(acc, S, tg, d, lane, wm, wn);
+  store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF, ACC>(acc, S, tg, d, lane, wm, wn);
 }
 
 // =====================================================================  fp32 SIMT
@@ -963,29 +959,34 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
   // inference kernels keep their code unchanged
   const bool save = WQ == 0 && phase == 1 && p.set[0].g_save;
   const bool obf = WQ == 0 && phase == 2 && !NMAJ && p.set[0].out_bf16;
-  // accumulating weight gradients (bf16, phase 2): an instantiation of its own, so
-  // that the inference down kernels carry no accumulate epilogue; the N-major
-  // kernels (backward only) test the flag at run time
-  const bool accum = WQ == 0 && phase == 2 && !NMAJ && p.set[0].accumulate;
-  if constexpr (NMAJ)
-    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, true, false, false, 2>),
-                       dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
-  else if (phase == 1 && save)
+  // accumulating gradients (bf16, phase 2): instantiations of their own, so that
+  // the other kernels carry no accumulate epilogue
+  const bool accum = WQ == 0 && phase == 2 && p.set[0].accumulate;
+  if constexpr (NMAJ) {
+    if (accum)
+      hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, true, false, false,
+                                              WQ == 0>),
+                         dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
+    else
+      hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, true>), dim3(grid),
+                         dim3(WGM * WGN * 64), 0, st, p);
+  } else if (phase == 1 && save) {
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD, false, WQ == 0>),
                        dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
-  else if (phase == 1)
+  } else if (phase == 1) {
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
-  else if (obf)
+  } else if (obf) {
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, false, false, WQ == 0>),
                        dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
-  else if (accum)
+  } else if (accum) {
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, false, false, false,
-                                            WQ == 0 ? 1 : 0>),
+                                            WQ == 0>),
                        dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
-  else
+  } else {
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD>), dim3(grid),
                        dim3(WGM * WGN * 64), 0, st, p);
+  }
   if (p.split_ws && p.split_cap > kSplitHeader) {
     hipLaunchKernelGGL(split_sum_kernel<BM * BN>, dim3(1024), dim3(256), 0, st, p.split_ws);
     if (phase == 1 && save)
@@ -997,12 +998,9 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
     else if (obf)
       hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false, false, WQ == 0>), dim3(grid),
                          dim3(WGM * WGN * 64), 0, st, p, grid);
-    else if (NMAJ)
-      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false, false, false, 2>), dim3(grid),
-                         dim3(WGM * WGN * 64), 0, st, p, grid);
     else if (accum)
-      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false, false, false, WQ == 0 ? 1 : 0>),
-                         dim3(grid), dim3(WGM * WGN * 64), 0, st, p, grid);
+      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false, false, false, WQ == 0>), dim3(grid),
+                         dim3(WGM * WGN * 64), 0, st, p, grid);
     else
       hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false>), dim3(grid), dim3(WGM * WGN * 64),
                          0, st, p, grid);
@@ -1042,7 +1040,8 @@ void launch_class(const GroupedParams& p, int phase, hipStream_t stream) {
     q.balance_m = 1;
     if (WQ == 0 && phase == 2 && p.set[0].b_nmajor) {
       launch_mfma<256, 256, 64, 2, 4, 2, 0, true, 1, true>(q, 2, 1, stream);
-    } else if (WQ == 0 && !p.set[0].k_offsets && tall_tiles(p.set[0].max_rows, p.set[0].n_groups)) {
+    } else if (WQ == 0 && !p.set[0].k_offsets && !p.set[0].accumulate &&
+               tall_tiles(p.set[0].max_rows, p.set[0].n_groups)) {
       if constexpr (WQ == 0) launch_mfma<320, 256, 64, 2, 4, 2, 0, true>(q, phase, 1, stream);
     } else {
       launch_mfma<256, 256, 64, 2, 4, 2, WQ, true>(q, phase, 1, stream);

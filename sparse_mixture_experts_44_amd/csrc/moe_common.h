@@ -94,7 +94,7 @@ struct SegSet {
   // k - b_split. b_split is a multiple of 64.
   int32_t b_nmajor;
   int32_t b_split;
-  // Phase 2: add the products to out instead of writing them; with k_offsets,
+  // Phase 2, set 0 (one set per launch): add the products to out instead of writing them; with k_offsets,
   // a group whose K range is empty then leaves its rows untouched.
   int32_t accumulate;
   // Phase 2, not with accumulate: out holds bf16 (round to nearest even of the fp32 sums).
