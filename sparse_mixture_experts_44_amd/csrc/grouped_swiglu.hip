@@ -954,7 +954,14 @@ template <int BM, int BN, int BK, int WGM, int WGN, int NS, int WQ, bool SPREAD 
           bool NMAJ = false>
 void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) {
   const int BH = phase == 1 ? BN / 2 : BN;
-  const int grid = grid_for(tiles_upper_bound(p, phase, BM, BH), per_cu);
+  long long ub = tiles_upper_bound(p, phase, BM, BH);
+  // Fewer tiles than CUs, each with a long K loop (a router product: one
+  // segment of N rows times E or d columns): launch up to kMaxSplit workgroups
+  // per tile so that the tail split spreads the K loops over the idle CUs.
+  const int K = phase == 1 ? p.d_model : p.set[0].d_ff;
+  if (p.split_ws && p.split_cap > kSplitHeader && ub < num_cus() && K >= 16 * BK)
+    ub = std::min<long long>(ub * kMaxSplit, num_cus());
+  const int grid = grid_for(ub, per_cu);
   // the training forward (bf16 phase 1 with g_save) runs its own instantiation: the
   // inference kernels keep their code unchanged
   const bool save = WQ == 0 && phase == 1 && p.set[0].g_save;

@@ -217,6 +217,7 @@ def oracle_grads(cfg, layer, x, dy, aux, idx):
     (dict(n_tokens=40, n_experts=4, top_k=4, d_model=64, d_ff=128), 0.1),                   # k = E
     (dict(n_tokens=70, n_experts=8, top_k=2, d_model=64, d_ff=64, n_shared=2, d_ff_shared=64), 0.0),  # S = 2
     (dict(n_tokens=100, n_experts=8, top_k=2, d_model=64, d_ff=128, capacity=1), 0.3),      # capacity 1
+    (dict(n_tokens=1024, n_experts=64, top_k=2, d_model=128, d_ff=128), 0.1),   # dW_r: K = 2N split over CUs
 ])
 def test_backward_small_layers_every_element(kw, aux):
     cfg = mi.small_config("bwd", dtype="bf16", layer_id=800 + kw["n_tokens"] % 11, x_id=800, **kw)

@@ -10,6 +10,7 @@ Small seeded layers, compared with the CPU oracle. Covered:
 * grouped GEMM segments of length 0, 1 and tile +- 1, for both tile shapes
   and fp32;
 * bitwise determinism across two runs;
+* a large router (N = 2048, E = 256, d = 1024) whose logits GEMM splits its K loops;
 * the staged entry points against moe_forward.
 """
 import numpy as np
@@ -48,6 +49,8 @@ CASES = {
     "wide_e": small("wide_e", n_tokens=70, n_experts=512, top_k=32, d_model=64, d_ff=64),
     "bf16_big_tiles": small("bf16_big_tiles", n_tokens=700, n_experts=4, top_k=2, d_model=256,
                             d_ff=256, n_shared=1, d_ff_shared=128),
+    # router logits on the matrix cores with 8 tiles of K = 1024: the K loops split over extra workgroups
+    "wide_router": small("wide_router", n_tokens=2048, n_experts=256, top_k=8, d_model=1024, d_ff=64),
 }
 
 
