@@ -11,6 +11,7 @@ Small seeded layers, compared with the CPU oracle. Covered:
   and fp32;
 * bitwise determinism across two runs;
 * a large router (N = 2048, E = 256, d = 1024) whose logits GEMM splits its K loops;
+* a seeded random sweep of 16 small layers, every knob drawn at once (bf16 and fp32).
 * the staged entry points against moe_forward.
 """
 import numpy as np
@@ -201,3 +202,34 @@ def test_staged_entry_points_match_forward():
     for key, t in staged.items():
         np.testing.assert_array_equal(P.to_host(t), fused[key], err_msg=key)
     P.check_y(P.to_host(y), fused["y"].astype(np.float64), tol=1e-6)
+
+
+def _random_layers(n=16, seed=77):
+    """Seeded random small layers: every knob of the forward drawn at once (both dtypes)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([1, 3, 8, 16, 64, 128]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        N = int(rng.choice([1, 5, 64, 200, 333, 1000]))
+        kw = dict(n_tokens=N, n_experts=E, top_k=k, d_model=int(rng.choice([64, 128, 192, 320])),
+                  d_ff=int(rng.choice([64, 128, 192, 384])), renormalize=bool(rng.integers(0, 2)) or k == 1,
+                  dtype="f32" if rng.random() < 0.25 else "bf16", layer_id=1000 + i, x_id=1000 + i)
+        if rng.random() < 0.4:
+            kw.update(n_shared=int(rng.integers(1, 3)), d_ff_shared=int(rng.choice([64, 128])))
+        if rng.random() < 0.4:
+            kw["capacity"] = int(rng.integers(1, max(2, 2 * N * k // E)))
+        if rng.random() < 0.3:
+            kw["select_bias"] = 0.05
+        if rng.random() < 0.3:
+            kw["logit_skew"] = 1.0
+        cases.append((i, kw))
+    return cases
+
+
+@pytest.mark.parametrize("i,kw", _random_layers(), ids=lambda v: str(v) if isinstance(v, int) else None)
+def test_random_small_layers(i, kw):
+    cfg = small(f"rand{i}", **kw)
+    layer, x = mi.make_layer(cfg), mi.make_x(cfg)
+    gpu = run_gpu(cfg, layer, x)
+    check_all(cfg, layer, x, gpu, per_token_rows=np.arange(min(cfg.n_tokens, 8)))
