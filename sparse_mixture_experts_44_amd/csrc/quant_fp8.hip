@@ -3,7 +3,7 @@
 // The handbook "混合专家 MoE" (anrans ai-infra handbook), section "推理视角",
 // notes that DeepSeek-V3 ships its weights in FP8 and that decode time is
 // the time to read the touched experts' weights. It names no format and no
-// scale granularity. This build reads them as: OCP E4M3 (e4m3fn, exponent
+// scale granularity. This library reads them as: OCP E4M3 (e4m3fn, exponent
 // bias 7, largest value 448, no infinities), with one fp32 scale per output
 // row of each weight matrix:
 //   scale_r   = (max_c |w[r, c]|) / 448            (fp32 division)
