@@ -268,6 +268,18 @@ typedef moe_weight_scales moe_fp8_scales;
 int moe_quantize_fp8(int64_t rows, int32_t cols, const void* w_bf16, uint8_t* codes, float* scales,
                      hipStream_t stream);
 
+/* The weights that FP8 codes stand for, as the FP8 grouped GEMM reads them
+ * (the same section of the handbook; E4M3 as in moe_quantize_fp8):
+ *   out[r, c] = scales[r] * value(codes[r, c])     (one fp32 product)
+ * value() widens each code to bf16 exactly, with the routine the FP8 grouped
+ * GEMM applies to its weight fragments; the codes 0x7F and 0xFF give NaN.
+ *   codes [rows, cols] uint8 in;  scales [rows] fp32 in;  out [rows, cols] fp32 out
+ * All device pointers, caller-owned. rows < 0, cols <= 0 or a NULL pointer
+ * with rows > 0: MOE_ERR_INVALID_ARG; cols not a multiple of 8:
+ * MOE_ERR_UNSUPPORTED. rows == 0 does nothing. */
+int moe_dequantize_fp8(int64_t rows, int32_t cols, const uint8_t* codes, const float* scales, float* out,
+                       hipStream_t stream);
+
 /* moe_grouped_swiglu with FP8 weights: w_gate/w_up [G, F, d] and w_down
  * [G, d, F] are E4M3 codes; sc_gate/sc_up [G, F] and sc_down [G, d] their
  * row scales. Everything else as in moe_grouped_swiglu (bf16 x and h). */

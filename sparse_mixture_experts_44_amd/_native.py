@@ -64,6 +64,7 @@ _SIGS = {
     "moe_forward": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "moe_quantize_fp8": (ctypes.c_int, [ctypes.c_int64, _I, _P, _P, _P, _P]),
+    "moe_dequantize_fp8": (ctypes.c_int, [ctypes.c_int64, _I, _P, _P, _P, _P]),
     "moe_train_save_floats": (_SZ, [_SHP]),
     "moe_forward_train": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
@@ -201,6 +202,11 @@ def moe_forward_train(shape, x, w_router, logit_bias, select_bias, w_gate, w_up,
 def moe_quantize_fp8(rows, cols, w_bf16, codes, scales, stream=None):
     _check("moe_quantize_fp8", lib().moe_quantize_fp8(
         int(rows), int(cols), _ptr(w_bf16), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def moe_dequantize_fp8(rows, cols, codes, scales, out, stream=None):
+    _check("moe_dequantize_fp8", lib().moe_dequantize_fp8(
+        int(rows), int(cols), _ptr(codes), _ptr(scales), _ptr(out), _stream(stream)))
 
 
 def moe_grouped_swiglu_fp8(shape, n_groups, d_ff, x, perm, rows_per_token, offsets, max_rows,

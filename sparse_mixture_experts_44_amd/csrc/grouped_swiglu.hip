@@ -256,19 +256,6 @@ __device__ __forceinline__ void wait_vm_barrier_rt(int n) {
   }
 }
 
-// FP8 E4M3 -> bf16 for 8 codes (bytes of lo, then hi), two per instruction
-// (v_cvt_scalef32_pk_bf16_fp8 with scale 1): exact, since every e4m3 value
-// (4 significant bits, exponents 2^-9 .. 2^8) is a bf16 value.
-__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
-  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false);
-  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true);
-  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false);
-  const bf16x2_t e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true);
-  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-  const bf16x4_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3), ce = __builtin_shufflevector(c, e, 0, 1, 2, 3);
-  return __builtin_shufflevector(ab, ce, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 constexpr int kBandM = 8;  // m-tiles per band of the tile order
 
 // Int4 weights: 8 offset-binary codes u = q + 8 (nibbles of w) -> the bf16

@@ -366,6 +366,14 @@ int moe_quantize_fp8(int64_t rows, int32_t cols, const void* w_bf16, uint8_t* co
   return launch_quantize_fp8(rows, cols, w_bf16, codes, scales, stream);
 }
 
+int moe_dequantize_fp8(int64_t rows, int32_t cols, const uint8_t* codes, const float* scales, float* out,
+                       hipStream_t stream) {
+  if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!codes || !scales || !out)) return MOE_ERR_INVALID_ARG;
+  if (cols % 8) return MOE_ERR_UNSUPPORTED;
+  return launch_dequantize_fp8(rows, cols, codes, scales, out, stream);
+}
+
 int moe_combine(const moe_shape* shape, const float* expert_out, const int32_t* slot_pos,
                 const float* topk_w, const float* shared_out, float* y, hipStream_t stream) {
   int st = check_shape(shape);

@@ -34,6 +34,19 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// FP8 E4M3 -> bf16 for 8 codes (bytes of lo, then hi), two per instruction
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1): exact, since every e4m3 value
+// (4 significant bits, exponents 2^-9 .. 2^8) is a bf16 value.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false);
+  const bf16x2_t e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true);
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const bf16x4_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3), ce = __builtin_shufflevector(c, e, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, ce, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // ------------------------------------------------------------------ router
 // `partials`: route_blocks(s) x E doubles; `logits`: route_logits_floats(s) floats (workspace).
 int launch_route(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
@@ -126,6 +139,9 @@ int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream);
 // codes[r, c] = e4m3(w[r, c] / scales[r]), scales[r] = max_c |w[r, c]| / 448 (fp32).
 int launch_quantize_fp8(long long rows, int cols, const void* w_bf16, uint8_t* codes, float* scales,
                         hipStream_t stream);
+// out[r, c] = scales[r] * decode(codes[r, c]) in fp32, decoding with fp8x8_to_bf16 (cols a multiple of 8).
+int launch_dequantize_fp8(long long rows, int cols, const uint8_t* codes, const float* scales, float* out,
+                          hipStream_t stream);
 // ------------------------------------------------------------------ int4 weights
 // q[r, c] = clamp(rint(w[r, c] / scales[r]), -7, 7), scales[r] = max_c |w[r, c]| / 7 (fp32), packed as
 // the grouped GEMM reads it (quant_int4.hip states the layout).

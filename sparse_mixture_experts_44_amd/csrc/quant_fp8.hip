@@ -13,6 +13,8 @@
 // scale_r * decode(code).
 #include <math.h>
 
+#include <algorithm>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -84,7 +86,32 @@ __global__ __launch_bounds__(kThreads) void quantize_fp8_kernel(const u32x4_t* _
   }
 }
 
+// out[r, c] = scales[r] * value(codes[r, c]): 8 codes per thread, widened with
+// the grouped GEMM's own fp8x8_to_bf16, then one fp32 product each.
+__global__ __launch_bounds__(kThreads) void dequantize_fp8_kernel(const u32x2_t* __restrict__ codes, long long n8,
+                                                                  int c8, const float* __restrict__ scales,
+                                                                  float* __restrict__ out) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n8; i += (long long)gridDim.x * kThreads) {
+    const u32x2_t q = codes[i];
+    const float sc = scales[i / c8];
+    const bf16x8_t v = fp8x8_to_bf16(q.x, q.y);
+    float* o = out + i * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (float)v[e] * sc;
+  }
+}
+
 }  // namespace
+
+int launch_dequantize_fp8(long long rows, int cols, const uint8_t* codes, const float* scales, float* out,
+                          hipStream_t stream) {
+  const long long n8 = rows * (cols / 8);
+  if (n8 == 0) return MOE_OK;
+  const long long blocks = std::min<long long>((n8 + kThreads - 1) / kThreads, 4096);
+  hipLaunchKernelGGL(dequantize_fp8_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const u32x2_t*>(codes), n8, cols / 8, scales, out);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
 
 int launch_quantize_fp8(long long rows, int cols, const void* w_bf16, uint8_t* codes, float* scales,
                         hipStream_t stream) {

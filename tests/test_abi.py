@@ -116,6 +116,11 @@ def test_fp8_entry_points_validate():
     assert L.moe_quantize_fp8(4, 64, None, FAKE, FAKE, None) == N.MOE_ERR_INVALID_ARG
     assert L.moe_quantize_fp8(4, 96, FAKE, FAKE, FAKE, None) == N.MOE_ERR_UNSUPPORTED
     assert L.moe_quantize_fp8(0, 64, None, None, None, None) == N.MOE_OK  # nothing to do
+    assert L.moe_dequantize_fp8(-1, 64, FAKE, FAKE, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_dequantize_fp8(4, 0, FAKE, FAKE, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_dequantize_fp8(4, 64, FAKE, None, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_dequantize_fp8(4, 12, FAKE, FAKE, FAKE, None) == N.MOE_ERR_UNSUPPORTED
+    assert L.moe_dequantize_fp8(0, 64, None, None, None, None) == N.MOE_OK  # nothing to do
     # grouped: scales required, bf16 layers only
     s = shp()
     args = (64, 256, FAKE, FAKE, 2, FAKE, 128, FAKE, FAKE, FAKE)

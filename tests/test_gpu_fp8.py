@@ -153,3 +153,20 @@ def test_fp8_dsv3_decode_full():
     log(f"generated {cfg.name} in {time.time() - t:.1f}s")
     gpu = run_fp8(cfg, layer, x)
     check_fp8(cfg, layer, x, gpu, np.arange(cfg.n_tokens))
+
+
+def test_dequantize_every_code_bit_exact():
+    """moe_dequantize_fp8 widens with the FP8 grouped GEMM's own routine. Every one of the 256 E4M3 codes, times
+    scales over many binades, must equal the oracle's exact value rounded once to fp32 (NaN for 0x7F and 0xFF,
+    -0 for 0x80). The products stay normal fp32 numbers."""
+    codes = np.tile(np.arange(256, dtype=np.uint8), (6, 1))
+    scales = np.array([1.0, 0.3712, 1.7 * 2.0 ** -40, 3.0e3, 448.0 / 7.0, 2.0 ** 20 + 1.0], dtype=np.float32)
+    out = torch.full(codes.shape, float("nan"), dtype=torch.float32, device=DEV)
+    moe.moe_dequantize_fp8(codes.shape[0], codes.shape[1], to_device(codes, DEV), to_device(scales, DEV), out)
+    torch.cuda.synchronize()
+    got = P.to_host(out)
+    ref = O.dequantize_fp8_rows(codes, scales.astype(np.float64)).astype(np.float32)
+    nan = np.isnan(ref)
+    assert int(nan.sum()) == 12
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
