@@ -338,7 +338,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this MoE layer build has no multi-GPU path "
+        print("bench.py measures one GPU only: this MoE layer library has no multi-GPU path "
               "(expert-parallel sharding is a design note, not code). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
