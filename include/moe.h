@@ -32,7 +32,11 @@
  *       d_model and every d_ff a multiple of 64;
  *       1 <= top_k <= min(n_experts, 32);
  *       n_experts <= 512; n_shared <= 16; grouped_swiglu n_groups <= 528;
- *       n_tokens * top_k < 2^31.
+ *       n_tokens * top_k < 2^31;
+ *       n_tokens * d_model < 2^31 and n_tokens * (top_k + n_shared) *
+ *       max(d_model, d_ff, d_ff_shared) < 2^31 (grouped_swiglu: max_rows *
+ *       max(d_model, d_ff) < 2^31), because the kernels address rows of x,
+ *       h and the expert outputs with 32-bit element offsets.
  *     Other sizes return MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H
@@ -147,7 +151,11 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_idx, const double* p
  *               max_rows * F * sizeof(dtype) (rounded up to 256) is used, when
  *               there is some, to split the last partial round of tiles
  *               along K (bf16 layers); results stay deterministic for a
- *               given device and workspace size */
+ *               given device and workspace size. On return, the first
+ *               max_rows * F elements of ws hold h, row r of the grouped
+ *               order at element r * F (bf16 in bf16 layers, the value the
+ *               down projection read; fp32 in fp32 layers), for the rows
+ *               below offsets[G]; the rest of ws is unspecified */
 int moe_grouped_swiglu(const moe_shape* shape, int32_t n_groups, int32_t d_ff,
                        const void* x, const int32_t* perm, int32_t rows_per_token,
                        const int32_t* offsets, int32_t max_rows,

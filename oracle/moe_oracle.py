@@ -72,6 +72,21 @@ update) are readings of passages whose formulas were lost; each function
 states its reading. Pins: closed forms (equal logits, one-hot and uniform
 routing), scipy's logsumexp, numpy's bincount, an element-wise brute force.
 
+Two correct roundings of h: the layer rounds h = silu(g) * u to bf16 at the
+same point on the GPU (from fp32 sums) and here (from fp64). Where h lies
+within an fp32 evaluation's error of a bf16 midpoint, every bf16 value in
+[bf16(h - bound), bf16(h + bound)] is a correct rounding (h_rounding_band,
+with the probabilistic fp32 error bound of fp32_dot_bound), and
+y_rounding_flips gives how each such element moves y. Pins: a planted
+midpoint (both neighbours, and only they), the bf16 roundings of h -+ bound
+by brute force over the bf16 grid, fp32 evaluations in the modelled orders
+staying inside the bound, and y with one element rounded otherwise by brute
+force.
+
+The near-tie gap of route() is the k-th minus the (k+1)-th largest selection
+score (with the selection bias), pinned by planted scores and by the set
+margin min(chosen) - max(others).
+
 Parity unpinned: y on general random inputs has no printed value on any page.
 It rests on the special cases above and on the per-token and grouped forms
 agreeing.
@@ -229,8 +244,9 @@ def bf16_round(a) -> np.ndarray:
 def softmax(logits: np.ndarray) -> np.ndarray:
     """Row softmax in float64: p_e = exp(l_e - max) / sum_e' exp(l_e' - max).
 
-    This is ``probs = self.router(x).softmax(dim=-1)`` in ``route`` ("实现"
-    section). Subtracting the row maximum changes no value mathematically.
+    The router's probabilities in ``route`` ("实现" section) are the softmax
+    of its linear layer's output over the experts. Subtracting the row
+    maximum changes no value mathematically.
     """
     l = np.asarray(logits, dtype=F64)
     z = np.exp(l - l.max(axis=-1, keepdims=True))
@@ -276,8 +292,9 @@ def route(x, w_router, k: int, logit_bias=None, select_bias=None,
           renormalize: bool = True) -> Routing:
     """Router of the layer: linear, softmax, (selection bias), top-k, renormalise.
 
-    Follows ``route`` ("实现" section): ``probs = softmax(router(x))``,
-    ``weights, idx = probs.topk(k)``, ``weights /= weights.sum()``.
+    Follows ``route`` ("实现" section): the probabilities are the softmax of
+    the router's logits; the k largest give the chosen experts and their
+    weights; the weights are then divided by their sum.
 
     The selection-only bias comes from the aux-loss-free balancing bullet of
     the "负载均衡" section: the bias is added to the scores used to choose the
@@ -287,11 +304,11 @@ def route(x, w_router, k: int, logit_bias=None, select_bias=None,
     p = softmax(router_logits(x, w_router, logit_bias))
     s = p if select_bias is None else p + np.asarray(select_bias, dtype=F64)[None, :]
     idx = topk_order(s, k)
-    w = np.take_along_axis(p, idx, axis=1)
-    if renormalize:
-        w = w / w.sum(axis=1, keepdims=True)
+    w = combine_weights(p, idx, renormalize)
     E = p.shape[1]
     if k < E:
+        # the near-tie measure: the k-th largest selection score minus the
+        # (k+1)-th, on s (the scores that choose), not on p
         srt = -np.sort(-s, axis=1)
         gap = srt[:, k - 1] - srt[:, k]
     else:
@@ -299,12 +316,32 @@ def route(x, w_router, k: int, logit_bias=None, select_bias=None,
     return Routing(idx=idx, w=w, probs=p, gap=gap)
 
 
+def combine_weights(probs, idx, renormalize: bool = True) -> np.ndarray:
+    """w[t, j] = p[t, idx[t, j]], divided by the sum over the token's k
+    chosen experts when renormalising ("实现" section, ``route``). Always the
+    unbiased p: the selection bias only chooses ("负载均衡" section)."""
+    w = np.take_along_axis(np.asarray(probs, dtype=F64), np.asarray(idx, dtype=np.int64), axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return w
+
+
+def forced_routing(r: "Routing", idx, renormalize: bool = True) -> "Routing":
+    """The routing with the expert choice replaced by a given idx: p and the
+    near-tie gaps stay those of ``r``; the weights are p at the given experts,
+    renormalised the same way. Each later step of the layer can then be
+    checked on that choice of experts."""
+    idx = np.asarray(idx, dtype=np.int64)
+    return Routing(idx=idx, w=combine_weights(r.probs, idx, renormalize), probs=r.probs, gap=r.gap)
+
+
 # ---------------------------------------------------------------- grouping
 
 def expert_counts(idx: np.ndarray, n_experts: int) -> np.ndarray:
     """counts[e] = number of (token, slot) copies routed to e, before capacity.
 
-    ``torch.bincount(flat_expert, minlength=E)`` in ``forward_grouped``.
+    ``forward_grouped`` ("实现" section) counts the flattened expert ids per
+    expert, empty experts included.
     """
     counts = np.zeros(n_experts, dtype=np.int64)
     for e in np.asarray(idx).reshape(-1):
@@ -396,6 +433,152 @@ def swiglu_expert(X, w_gate, w_up, w_down, round_h: bool) -> np.ndarray:
 WeightSet = Sequence  # indexable by expert id -> 2-D array (converted to float64 on use)
 
 
+# ---------------------------------------------------------------- where two roundings of h are correct
+#
+# The layer rounds h = silu(g) * u to bf16 before the down projection, and the
+# fp32 GPU path and this fp64 oracle round it at the same point. A value of h
+# that lies very close to the midpoint between two bf16 neighbours may round
+# either way, depending only on the last bits of an fp32 evaluation of g and
+# u. Reading: such an element has two correct roundings. The functions below
+# find these elements, under a stated error bound of an fp32 evaluation, and
+# give the change of y for each alternative rounding.
+
+U32 = 2.0 ** -24   # unit roundoff of fp32
+
+
+@dataclass
+class HBand:
+    h: np.ndarray      # [R, F] silu(g) * u in fp64, before rounding
+    ref: np.ndarray    # bf16_round(h)
+    lo: np.ndarray     # the smallest correct bf16 rounding: bf16_round(h - bound)
+    hi: np.ndarray     # the largest: bf16_round(h + bound)
+    bound: np.ndarray  # error bound of an fp32 evaluation of h (absolute)
+    amb: np.ndarray    # lo < hi: more than one rounding is correct
+
+
+LAMBDA = 8.0       # confidence of the probabilistic bound: P(exceeded) <= 2 exp(-LAMBDA^2 / 2) ~ 2.5e-14
+
+
+def fp32_dot_bound(X, W, chunk: int = 16, parts: int = 8, lam: float = LAMBDA) -> np.ndarray:
+    """Probabilistic error bound of an fp32 evaluation of X @ W^T (rows of bf16 values).
+
+    The evaluation model: products of bf16 values are exact in fp32; groups
+    of at most ``chunk`` consecutive products along K are summed (each sum
+    that rounds is within 4 u of its sum of |terms|, u = 2^-24) and added to
+    an fp32 accumulator in K order; K may be cut into at most ``parts``
+    contiguous pieces whose accumulators are added at the end. The bound
+    follows the probabilistic rounding error analysis of Higham and Mary ("A
+    New Approach to Probabilistic Rounding Error Analysis", SIAM J. Sci.
+    Comput. 41(5), 2019): the rounding errors are independent and mean zero,
+    each at most u times the value it rounds, so by the Azuma-Hoeffding
+    inequality their sum exceeds lam * u * sqrt(sum of the squared values)
+    with probability at most 2 exp(-lam^2 / 2). The rounded values are:
+      * the accumulators: the partial sums S_i (sums of the first i groups)
+        of their piece, S_i - S_c for a piece starting at group c, whose
+        squares are at most 2 S_i^2 + 2 M^2 (M = max_i |S_i|); plus at most
+        ``parts`` additions of pieces, each at most 2 M;
+      * the group sums, at most 4 times their sum of |terms| A_c each.
+    Hence, per output element, with n groups,
+        |fp32 - exact| <= lam * u * (sqrt(2 sum_i S_i^2 + (2 n + 4 parts) M^2) + 4 sqrt(sum_c A_c^2)).
+    A worst-case bound (every error at its maximum with the same sign) would
+    be n / sqrt(n) times larger and would mark most elements of a long K.
+    """
+    X = np.atleast_2d(np.asarray(X, dtype=F64))
+    W = np.atleast_2d(np.asarray(W, dtype=F64))
+    R, K = X.shape
+    n = -(-K // chunk)
+    pad = n * chunk - K
+    if pad:
+        X = np.pad(X, ((0, 0), (0, pad)))
+        W = np.pad(W, ((0, 0), (0, pad)))
+    Xc = X.reshape(R, n, chunk)
+    Wc = W.reshape(W.shape[0], n, chunk)
+    S = np.cumsum(np.einsum("rci,fci->rfc", Xc, Wc), axis=2)
+    M = np.max(np.abs(S), axis=2)
+    A = np.einsum("rci,fci->rfc", np.abs(Xc), np.abs(Wc))
+    acc = np.sqrt(2.0 * np.sum(S * S, axis=2) + (2.0 * n + 4.0 * parts) * M * M)
+    grp = 4.0 * np.sqrt(np.sum(A * A, axis=2))
+    return lam * U32 * (acc + grp)
+
+
+def h_rounding_band(X, w_gate, w_up, *, chunk: int = 16, parts: int = 8, scaled: bool = False) -> HBand:
+    """For the rows of X through one expert: h, its bf16 rounding, the range
+    of correct bf16 roundings, and the error bound of an fp32 evaluation.
+
+    An fp32 evaluation lands in [h - bound, h + bound], and rounding to bf16
+    is monotone, so every bf16 value from bf16_round(h - bound) to
+    bf16_round(h + bound) is a correct rounding. Next to a midpoint that is
+    the two neighbours; where the bound exceeds a bf16 step (h near zero
+    after cancellation in g or u) it is more.
+
+    The bound of h combines the bounds of g and u (fp32_dot_bound) through
+    h = silu(g) * u, with a factor 2 for the linearisation, plus 8 units of
+    fp32 roundoff of |h| for the SiLU and the product themselves (exp, a
+    reciprocal, two products and a sum, each within about one unit, taken at
+    their worst).
+    ``scaled``: the weights carry per-row scales applied after the sum
+    (quantised weights), one more fp32 rounding of g and of u.
+    """
+    X = np.atleast_2d(np.asarray(X, dtype=F64))
+    Wg = np.asarray(w_gate, dtype=F64)
+    Wu = np.asarray(w_up, dtype=F64)
+    g = X @ Wg.T
+    u = X @ Wu.T
+    eg = fp32_dot_bound(X, Wg, chunk, parts)
+    eu = fp32_dot_bound(X, Wu, chunk, parts)
+    if scaled:
+        eg = eg + U32 * np.abs(g)
+        eu = eu + U32 * np.abs(u)
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    s = g * sig
+    ds = sig * (1.0 + g * (1.0 - sig))      # d silu / d g
+    h = s * u
+    bound = 2.0 * (np.abs(ds * u) * eg + np.abs(s) * eu) + 8.0 * U32 * np.abs(h) + 2.0 ** -140
+    return HBand(h=h, ref=bf16_round(h), lo=bf16_round(h - bound), hi=bf16_round(h + bound), bound=bound,
+                 amb=bf16_round(h - bound) < bf16_round(h + bound))
+
+
+@dataclass
+class YFlips:
+    """The outputs y_t that other correct roundings of h allow:
+    y_t(choice) = y_t + sum_i V[i] * (h_i - ref[i]) for bf16 values h_i in [lo[i], hi[i]]."""
+    V: np.ndarray      # [m, d]: weight * W_down[:, f] of each ambiguous element
+    ref: np.ndarray    # [m] the oracle's rounding of each
+    lo: np.ndarray     # [m] smallest correct rounding
+    hi: np.ndarray     # [m] largest correct rounding
+
+
+def y_rounding_flips(x_t, experts, shared=None, *, scaled: bool = False) -> YFlips:
+    """The ambiguous h elements of one token's row (h_rounding_band) and how
+    each moves y_t.
+
+    ``experts`` lists the token's kept copies as (weight, w_gate, w_up,
+    w_down); ``shared`` is None or a tuple (s_gate, s_up, s_down) of weight
+    sets (weight 1). Row i of V is weight * W_down[:, f] for one ambiguous
+    element f of one copy: y_t with that element rounded to h instead of ref
+    is y_t + V[i] * (h - ref).
+    """
+    x_t = np.atleast_2d(np.asarray(x_t, dtype=F64))
+    items = list(experts)
+    if shared is not None:
+        sg, su, sd = shared
+        items += [(1.0, sg[s], su[s], sd[s]) for s in range(len(sg))]
+    V, ref, lo, hi = [], [], [], []
+    for wt, wg, wu, wd in items:
+        b = h_rounding_band(x_t, wg, wu, scaled=scaled)
+        f = np.nonzero(b.amb[0])[0]
+        if f.size:
+            V.append(float(wt) * np.asarray(wd, dtype=F64)[:, f].T)
+            ref.append(b.ref[0, f])
+            lo.append(b.lo[0, f])
+            hi.append(b.hi[0, f])
+    if not V:
+        z = np.zeros(0)
+        return YFlips(V=np.zeros((0, x_t.shape[1])), ref=z, lo=z, hi=z)
+    return YFlips(V=np.concatenate(V), ref=np.concatenate(ref), lo=np.concatenate(lo), hi=np.concatenate(hi))
+
+
 def forward_per_token(x, idx, w, keep, w_gate: WeightSet, w_up: WeightSet, w_down: WeightSet,
                       shared=None, round_h: bool = False, rows=None) -> np.ndarray:
     """The per-token form: y_t = sum_j w[t,j] Expert_{idx[t,j]}(x_t) + sum_s Shared_s(x_t).
@@ -482,7 +665,8 @@ def balance_stat(counts, prob_sum, n_tokens: int, top_k: int) -> float:
     This is ``aux_loss`` ("负载均衡" section), written there as
     E * sum_i f_i P_i:
 
-    * f_e = counts_e / (N*k), the share of the copies; ``idx.numel()`` is N*k;
+    * f_e = counts_e / (N*k), the share of the copies: the page divides the
+      counts by the number of entries of idx, which is N*k;
     * P_e = prob_sum_e / N, the mean router probability.
 
     counts are the routed copies before capacity.
@@ -576,11 +760,7 @@ def moe_layer(x, w_router, w_gate, w_up, w_down, k: int, *, shared=None, logit_b
     """
     r = route(x, w_router, k, logit_bias, select_bias, renormalize)
     if forced_idx is not None:
-        idx = np.asarray(forced_idx, dtype=np.int64)
-        wv = np.take_along_axis(r.probs, idx, axis=1)
-        if renormalize:
-            wv = wv / wv.sum(axis=1, keepdims=True)
-        r = Routing(idx=idx, w=wv, probs=r.probs, gap=r.gap)
+        r = forced_routing(r, forced_idx, renormalize)
     E = r.probs.shape[1]
     g = group(r.idx, E, capacity)
     prob_sum = r.probs.sum(axis=0)

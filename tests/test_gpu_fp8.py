@@ -72,6 +72,10 @@ def run_fp8(cfg, layer, x):
     L = _fp8_layer(cfg, layer)
     o = L.out
     o.y.fill_(float("nan"))
+    for name in ("topk_idx", "counts", "offsets", "perm", "slot_pos"):
+        getattr(o, name).fill_(-7)
+    for name in ("topk_w", "prob_sum", "balance_stat"):
+        getattr(o, name).fill_(float("nan"))
     L.forward(to_device(x, DEV))
     torch.cuda.synchronize()
     res = {k: P.to_host(getattr(o, k)) for k in ("y", "topk_idx", "topk_w", "counts", "offsets", "perm",
@@ -88,7 +92,8 @@ def check_fp8(cfg, layer, x, gpu, rows):
     assert np.all(np.isfinite(gpu["y"]))
     t = time.time()
     yref = P.oracle_y(cfg, layer, x, gpu["topk_idx"], rows, "grouped", ref, fp8=True)
-    worst = P.check_y(gpu["y"][rows], yref)
+    flips = P.rounding_flips(cfg, layer, x, gpu["topk_idx"], fp8=True)
+    worst = P.check_y(gpu["y"][rows], yref, flips=flips, tokens=rows)
     log(f"{cfg.name} fp8: y ok on {len(rows)} rows, worst err/rms={worst:.2e}, "
         f"{n_diff} near-tie tokens [{time.time() - t:.1f}s]")
     return worst

@@ -74,6 +74,10 @@ def run_int4(cfg, layer, x):
     L = _int4_layer(cfg, layer)
     o = L.out
     o.y.fill_(float("nan"))
+    for name in ("topk_idx", "counts", "offsets", "perm", "slot_pos"):
+        getattr(o, name).fill_(-7)
+    for name in ("topk_w", "prob_sum", "balance_stat"):
+        getattr(o, name).fill_(float("nan"))
     L.forward(to_device(x, DEV))
     torch.cuda.synchronize()
     res = {k: P.to_host(getattr(o, k)) for k in ("y", "topk_idx", "topk_w", "counts", "offsets", "perm",
@@ -90,7 +94,8 @@ def check_int4(cfg, layer, x, gpu, rows):
     assert np.all(np.isfinite(gpu["y"]))
     t = time.time()
     yref = P.oracle_y(cfg, layer, x, gpu["topk_idx"], rows, "grouped", ref, quant="int4")
-    worst = P.check_y(gpu["y"][rows], yref)
+    flips = P.rounding_flips(cfg, layer, x, gpu["topk_idx"], quant="int4")
+    worst = P.check_y(gpu["y"][rows], yref, flips=flips, tokens=rows)
     log(f"{cfg.name} int4: y ok on {len(rows)} rows, worst err/rms={worst:.2e}, "
         f"{n_diff} near-tie tokens [{time.time() - t:.1f}s]")
     return worst

@@ -3,9 +3,12 @@
 These run on an MI355X through the C ABI (libmoe.so). Small layers compare
 every output row with the oracle's per-token form. Full-size layers compare
 every integer output (routing, counts, offsets, permutation, dropped set).
-For y they compare a seeded row sample, the first and last rows included,
-with the oracle's grouped form, and a smaller sub-sample with the per-token
-form.
+For y they compare a stratified row sample with the oracle's grouped form:
+one copy from every 64-row block of every expert segment and one token from
+every 64-token block (the shared expert's rows), the first and last rows
+included, so that every tile of both grouped GEMMs holds a checked row (the
+K-split tail tiles too). A smaller sub-sample is compared with the per-token
+form. Every output buffer is poisoned before the run.
 """
 import time
 
@@ -47,6 +50,11 @@ def run_gpu(cfg, layer, x):
     o.topk_idx.fill_(-7)
     o.topk_w.fill_(float("nan"))
     o.slot_pos.fill_(-7)
+    o.counts.fill_(-7)
+    o.offsets.fill_(-7)
+    o.perm.fill_(-7)
+    o.prob_sum.fill_(float("nan"))
+    o.balance_stat.fill_(float("nan"))
     L.forward(xd)
     torch.cuda.synchronize()
     res = {k: P.to_host(getattr(o, k)) for k in
@@ -57,7 +65,7 @@ def run_gpu(cfg, layer, x):
     return res
 
 
-def check_all(cfg, layer, x, gpu, y_rows=None, per_token_rows=None):
+def check_all(cfg, layer, x, gpu, y_rows=None, per_token_rows=None, stratified=False):
     N = cfg.n_tokens
     t = time.time()
     ref = P.oracle_route(cfg, layer, x)
@@ -72,15 +80,20 @@ def check_all(cfg, layer, x, gpu, y_rows=None, per_token_rows=None):
         f"stat={stat_ref:.6f}, kept={int(g.offsets[-1])}/{N * cfg.top_k} [{time.time() - t:.1f}s]")
     assert np.all(np.isfinite(gpu["y"])), "y has unwritten (NaN) entries"
     rows = np.arange(N) if y_rows is None else y_rows
+    cover = ""
+    if stratified:
+        rows, cells = P.stratified_rows(g, cfg.top_k, N)
+        cover = f", covering all {cells} (segment, 64-row block) cells"
     t = time.time()
+    flips = P.rounding_flips(cfg, layer, x, gpu["topk_idx"])
     yref = P.oracle_y(cfg, layer, x, gpu["topk_idx"], rows, "grouped", ref)
-    worst = P.check_y(gpu["y"][rows], yref)
-    log(f"{cfg.name}: y ok on {len(rows)} rows (grouped oracle), worst err/rms={worst:.2e} "
+    worst = P.check_y(gpu["y"][rows], yref, flips=flips, tokens=rows)
+    log(f"{cfg.name}: y ok on {len(rows)} rows (grouped oracle){cover}, worst err/rms={worst:.2e} "
         f"[{time.time() - t:.1f}s]")
     if per_token_rows is not None and len(per_token_rows):
         t = time.time()
         yref2 = P.oracle_y(cfg, layer, x, gpu["topk_idx"], per_token_rows, "per_token", ref)
-        worst2 = P.check_y(gpu["y"][per_token_rows], yref2)
+        worst2 = P.check_y(gpu["y"][per_token_rows], yref2, flips=flips, tokens=per_token_rows)
         log(f"{cfg.name}: y ok on {len(per_token_rows)} rows (per-token oracle), "
             f"worst err/rms={worst2:.2e} [{time.time() - t:.1f}s]")
     return ref, g
@@ -107,8 +120,7 @@ def test_dsv3_prefill_full():
     cfg = mi.CONFIGS["dsv3_prefill"]
     layer, x = get_layer(cfg), mi.make_x(cfg)
     gpu = run_gpu(cfg, layer, x)
-    rows = P.sample_rows(cfg.n_tokens, 96)
-    check_all(cfg, layer, x, gpu, y_rows=rows, per_token_rows=rows[:3])
+    check_all(cfg, layer, x, gpu, stratified=True, per_token_rows=np.array([0, 4097, 8191]))
 
 
 @pytest.mark.timeout(900)
@@ -116,8 +128,7 @@ def test_mixtral_full():
     cfg = mi.CONFIGS["mixtral"]
     layer, x = get_layer(cfg), mi.make_x(cfg)
     gpu = run_gpu(cfg, layer, x)
-    rows = P.sample_rows(cfg.n_tokens, 128)
-    check_all(cfg, layer, x, gpu, y_rows=rows, per_token_rows=rows[:4])
+    check_all(cfg, layer, x, gpu, stratified=True, per_token_rows=np.array([0, 1500, 2900, 4095]))
 
 
 @pytest.mark.timeout(900)
@@ -125,8 +136,8 @@ def test_switch_capacity_full():
     cfg = mi.CONFIGS["switch_cap"]
     layer, x = get_layer(cfg), mi.make_x(cfg)
     gpu = run_gpu(cfg, layer, x)
-    rows = P.sample_rows(cfg.n_tokens, 256)
-    ref, g = check_all(cfg, layer, x, gpu, y_rows=rows, per_token_rows=rows[:8])
+    ref, g = check_all(cfg, layer, x, gpu, stratified=True,
+                       per_token_rows=np.array([0, 1, 2, 3, 5000, 9000, 12000, 16383]))
     # every expert holds at most C rows; the overflow copies are dropped
     assert np.all(np.diff(g.offsets) <= cfg.capacity)
     assert int(np.sum(g.slot_pos < 0)) == int(np.sum(g.counts - np.minimum(g.counts, cfg.capacity)))

@@ -202,3 +202,62 @@ def test_backward_dropped_copies_sending_gradient_is_caught(monkeypatch):
     orig_group = OB._grouping
     monkeypatch.setattr(OB, "_grouping", lambda idx, E, capacity=0: orig_group(idx, E, 0))
     _fails(lambda: bpins.test_backward_matches_finite_differences(True))
+
+
+def test_gap_on_unbiased_probs_is_caught(monkeypatch):
+    orig = O.route
+
+    def bad(x, W, k, logit_bias=None, select_bias=None, renormalize=True):
+        r = orig(x, W, k, logit_bias, select_bias, renormalize)
+        if k < r.probs.shape[1]:
+            srt = -np.sort(-r.probs, axis=1)
+            r.gap = srt[:, k - 1] - srt[:, k]
+        return r
+    monkeypatch.setattr(O, "route", bad)
+    _fails(pins.test_route_gap_planted_scores)
+
+
+def test_gap_one_slot_off_is_caught(monkeypatch):
+    orig = O.route
+
+    def bad(x, W, k, logit_bias=None, select_bias=None, renormalize=True):
+        r = orig(x, W, k, logit_bias, select_bias, renormalize)
+        s = r.probs + (0.0 if select_bias is None else np.asarray(select_bias)[None, :])
+        srt = -np.sort(-s, axis=1)
+        if 2 <= k < s.shape[1]:
+            r.gap = srt[:, k - 2] - srt[:, k - 1]
+        return r
+    monkeypatch.setattr(O, "route", bad)
+    _fails(pins.test_route_gap_planted_scores)
+
+
+def test_forced_weights_from_biased_scores_is_caught(monkeypatch):
+    def bad(r, idx, renormalize=True):
+        idx = np.asarray(idx, dtype=np.int64)
+        w = np.take_along_axis(r.probs + 0.01, idx, axis=1)   # a shifted score instead of p
+        if renormalize:
+            w = w / w.sum(axis=1, keepdims=True)
+        return O.Routing(idx=idx, w=w, probs=r.probs, gap=r.gap)
+    monkeypatch.setattr(O, "forced_routing", bad)
+    _fails(pins.test_forced_routing_weights_bruteforce)
+
+
+def test_band_without_error_bound_is_caught(monkeypatch):
+    orig = O.fp32_dot_bound
+    monkeypatch.setattr(O, "fp32_dot_bound", lambda X, W, chunk=16, parts=8, lam=O.LAMBDA:
+                        0.0 * orig(X, W, chunk, parts, lam))
+    monkeypatch.setattr(O, "U32", 0.0)
+    _fails(pins.test_h_band_contains_fp32_evaluations)
+
+
+def test_band_one_sided_range_is_caught(monkeypatch):
+    # only roundings at or above the oracle's own counted as correct
+    orig = O.h_rounding_band
+
+    def bad(*a, **kw):
+        b = orig(*a, **kw)
+        b.lo = b.ref.copy()
+        b.amb = b.lo < b.hi
+        return b
+    monkeypatch.setattr(O, "h_rounding_band", bad)
+    _fails(pins.test_h_band_planted_midpoint)

@@ -613,3 +613,153 @@ def test_int4_layer_is_dense_ffn_with_dequantised_weights():
         tdeq.append((torch.from_numpy(q.astype(np.int64)).double() * torch.from_numpy(s.astype(np.float64))[:, None]).numpy())
     lr = O.moe_layer(x, rng.standard_normal((1, d)), deq[0], deq[1], deq[2], 1)
     np.testing.assert_allclose(lr.y, torch_swiglu(x, tdeq[0], tdeq[1], tdeq[2]), rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------ near-tie gap of the router
+
+def test_route_gap_planted_scores():
+    # p = (0.4, 0.3, 0.2, 0.1) planted as logits log p; selection bias b = (0, 0, 0.12, 0.25), so the
+    # scores s = p + b = (0.4, 0.3, 0.32, 0.35) rank 0, 3, 2, 1. The gap is the k-th largest s minus
+    # the (k+1)-th, on s, not on p: k=1: 0.4 - 0.35; k=2: 0.35 - 0.32; k=3: 0.32 - 0.3; k=E: none.
+    p = np.array([0.4, 0.3, 0.2, 0.1])
+    b = np.array([0.0, 0.0, 0.12, 0.25])
+    want = {1: 0.05, 2: 0.03, 3: 0.02}
+    for k, g in want.items():
+        r = O.route(np.ones((1, 1)), np.log(p)[:, None], k, select_bias=b)
+        assert list(r.idx[0]) == [0, 3, 2, 1][:k]
+        assert abs(r.gap[0] - g) < 1e-12, (k, r.gap[0], g)
+    assert np.isinf(O.route(np.ones((1, 1)), np.log(p)[:, None], 4, select_bias=b).gap[0])
+    # without the bias the gap is taken on p itself: 0.3 - 0.2 for k = 2
+    assert abs(O.route(np.ones((1, 1)), np.log(p)[:, None], 2).gap[0] - 0.1) < 1e-12
+
+
+def test_route_gap_is_the_selection_margin():
+    # the gap equals min over the chosen experts of s minus max over the others (a set margin,
+    # independent of any sort), with and without a selection bias
+    rng = np.random.default_rng(21)
+    x, W = rng.standard_normal((200, 16)), rng.standard_normal((10, 16)) * 0.5
+    for b in (None, rng.uniform(-0.1, 0.1, 10)):
+        for k in (1, 3, 9):
+            r = O.route(x, W, k, select_bias=b)
+            s = r.probs + (0.0 if b is None else b[None, :])
+            chosen = np.zeros_like(s, dtype=bool)
+            np.put_along_axis(chosen, r.idx, True, axis=1)
+            margin = np.where(chosen, s, np.inf).min(1) - np.where(chosen, -np.inf, s).max(1)
+            np.testing.assert_allclose(r.gap, margin, rtol=0, atol=1e-15)
+
+
+def test_forced_routing_weights_bruteforce():
+    # forced routing keeps p and takes the weights at the given experts, renormalised or not
+    rng = np.random.default_rng(22)
+    x, W = rng.standard_normal((40, 8)), rng.standard_normal((6, 8))
+    r = O.route(x, W, 3, select_bias=rng.uniform(-0.1, 0.1, 6))
+    idx = rng.integers(0, 6, size=(40, 3))
+    for renorm in (True, False):
+        f = O.forced_routing(r, idx, renorm)
+        for t in range(40):
+            want = [r.probs[t, e] for e in idx[t]]
+            if renorm:
+                want = [v / sum(want) for v in want]
+            np.testing.assert_allclose(f.w[t], want, rtol=1e-15)
+        np.testing.assert_array_equal(f.probs, r.probs)
+    same = O.forced_routing(r, r.idx, True)
+    np.testing.assert_allclose(same.w, r.w, rtol=1e-15)
+
+
+# ------------------------------------------------------------------ two correct roundings of h
+
+def test_h_band_planted_midpoint():
+    # h planted within ~1e-6 of a bf16 step from the midpoint of 16 and 16.125: both roundings
+    # are correct, and they are the only ones
+    import planting as PL
+    cfg, layer, x, planted = PL.planted_layer()
+    X = mi.to_f64(x)
+    b = O.h_rounding_band(X, mi.to_f64(layer.w_gate[0]), mi.to_f64(layer.w_up[0]))
+    for t, f, h, mid in planted:
+        assert abs(h - mid) < 1e-5 * 0.125
+        assert b.amb[t, f]
+        assert (b.lo[t, f], b.hi[t, f]) == (16.0, 16.125)
+        assert b.ref[t, f] == O.bf16_round(h)
+    # lo and hi are the bf16 roundings of h -+ bound (brute force over the bf16 grid: the nearest
+    # grid value, ties to the even pattern); an element whose interval holds no midpoint has one
+    bits = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    vals = mi.bf16_bits_to_f32(bits)
+    fin = np.isfinite(vals)
+    grid, gbits = vals[fin].astype(np.float64), bits[fin]
+    order = np.argsort(grid, kind="stable")
+    grid, gbits = grid[order], gbits[order]
+
+    def nearest(v):
+        i = np.searchsorted(grid, v)
+        c = [j for j in (i - 1, i) if 0 <= j < grid.shape[0]]
+        best = min(abs(grid[j] - v) for j in c)
+        tie = [j for j in c if abs(grid[j] - v) == best]
+        return grid[tie[0]] if len(tie) == 1 else grid[[j for j in tie if gbits[j] % 2 == 0][0]]
+    rng = np.random.default_rng(24)
+    for t, f in [(0, 20), (3, 40), (5, 63)] + [(p[0], p[1]) for p in planted[:3]] + \
+            [tuple(v) for v in rng.integers(0, [16, 64], size=(20, 2))]:
+        assert b.lo[t, f] == nearest(b.h[t, f] - b.bound[t, f])
+        assert b.hi[t, f] == nearest(b.h[t, f] + b.bound[t, f])
+        assert b.amb[t, f] == (b.lo[t, f] != b.hi[t, f])
+
+
+def _fp32_eval(X, W, parts):
+    """An fp32 evaluation of X @ W^T in the bound's model: exact groups of 16, fp32 accumulators
+    in K order, K cut into `parts` pieces added at the end."""
+    f32 = np.float32
+    K = X.shape[1]
+    cuts = np.linspace(0, K // 16, parts + 1).astype(int) * 16
+    tot = np.zeros((X.shape[0], W.shape[0]), f32)
+    for p in range(parts):
+        acc = np.zeros_like(tot)
+        for c in range(cuts[p], cuts[p + 1], 16):
+            acc = (acc + (X[:, c:c + 16] @ W[:, c:c + 16].T).astype(f32)).astype(f32)
+        tot = (tot + acc).astype(f32)
+    return tot
+
+
+def test_h_band_contains_fp32_evaluations():
+    # the bound holds for fp32 evaluations in the modelled orders (one piece and eight pieces), and
+    # every element that such an evaluation rounds differently from the oracle is marked ambiguous
+    rng = np.random.default_rng(23)
+    f32 = np.float32
+    for d, F in ((64, 128), (512, 256), (2048, 64)):
+        X = O.bf16_round(rng.standard_normal((24, d)))
+        Wg = O.bf16_round(rng.standard_normal((F, d)) / math.sqrt(d))
+        Wu = O.bf16_round(rng.standard_normal((F, d)) / math.sqrt(d))
+        b = O.h_rounding_band(X, Wg, Wu)
+        assert b.amb.mean() < 0.15
+        for parts in (1, 8):
+            g, u = _fp32_eval(X, Wg, parts), _fp32_eval(X, Wu, parts)
+            e = np.exp(-g.astype(np.float64)).astype(f32)
+            h = (g / (f32(1) + e) * u).astype(f32).astype(np.float64)
+            assert np.all(np.abs(h - b.h) <= b.bound)
+            hb = O.bf16_round(h)
+            assert np.all((b.lo <= hb) & (hb <= b.hi))
+            assert np.all(b.amb[hb != b.ref])
+
+
+def test_y_rounding_flips_bruteforce():
+    # y with one ambiguous h element rounded to lo or hi instead of ref is y + V[i] * (h - ref)
+    import planting as PL
+    cfg, layer, x, planted = PL.planted_layer()
+    X = mi.to_f64(x)
+    wg, wu, wd = (mi.to_f64(a[0]) for a in (layer.w_gate, layer.w_up, layer.w_down))
+    for t in (0, 7):
+        fl = O.y_rounding_flips(X[t], [(0.75, wg, wu, wd)])
+        b = O.h_rounding_band(X[t:t + 1], wg, wu)
+        cols = np.nonzero(b.amb[0])[0]
+        assert fl.V.shape == (cols.shape[0], cfg.d_model) and t in cols
+        np.testing.assert_array_equal(fl.lo, b.lo[0, cols])
+        np.testing.assert_array_equal(fl.hi, b.hi[0, cols])
+        y0 = 0.75 * (wd @ b.ref[0])
+        for i, f in enumerate(cols):
+            for v in (fl.lo[i], fl.hi[i]):
+                h = b.ref[0].copy()
+                h[f] = v
+                np.testing.assert_allclose(y0 + fl.V[i] * (v - fl.ref[i]), 0.75 * (wd @ h), rtol=0, atol=1e-13)
+    # a shared expert adds its own rows with weight 1
+    a = O.y_rounding_flips(X[0], [], shared=([wg], [wu], [wd]))
+    c = O.y_rounding_flips(X[0], [(1.0, wg, wu, wd)])
+    np.testing.assert_array_equal(a.V, c.V)
+    np.testing.assert_array_equal(a.lo, c.lo)
