@@ -1,6 +1,6 @@
 """Benchmark: the forward pass of the MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_prefill]
 
 One step is one moe_forward over the whole layer: route, permute, the gate|up
 and down grouped GEMMs, and combine. Inputs are seeded synthetic tensors
@@ -313,7 +313,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="dsv3_prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--cold-reps", type=int, default=20,

@@ -32,6 +32,10 @@ int check_shape(const moe_shape* sp) {
   if (s.n_shared > kMaxShared) return MOE_ERR_UNSUPPORTED;
   const long long N = s.n_tokens;
   if (N * s.top_k >= (1LL << 31) || N * (s.top_k + s.n_shared) >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  // the kernels index rows of x, h and the expert outputs with 32-bit element offsets
+  const long long F = std::max(s.d_ff, s.n_shared > 0 ? s.d_ff_shared : 0);
+  if (N * s.d_model >= (1LL << 31) || N * (s.top_k + s.n_shared) * std::max<long long>(F, s.d_model) >= (1LL << 31))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -109,6 +113,10 @@ int grouped_impl(const moe_shape* shape, int32_t n_groups, int32_t d_ff, const v
   if (!offsets || !w_gate || !w_up || !w_down || (max_rows > 0 && (!x || !out || !ws)))
     return MOE_ERR_INVALID_ARG;
   if (s.d_model % 64 || d_ff % 64 || n_groups > kMaxTileEntries) return MOE_ERR_UNSUPPORTED;
+  // 32-bit element offsets into x and h rows
+  if ((long long)s.n_tokens * s.d_model >= (1LL << 31) ||
+      (long long)max_rows * std::max(d_ff, s.d_model) >= (1LL << 31))
+    return MOE_ERR_UNSUPPORTED;
   const size_t need = align256((size_t)max_rows * d_ff * esize(s));
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (max_rows == 0 || s.n_tokens == 0) return MOE_OK;

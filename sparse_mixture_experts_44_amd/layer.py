@@ -149,9 +149,20 @@ class MoELayer:
         self.int4 = self._quantize("int4", keep_bf16)
         return self.int4
 
+    def _check_x(self, x: torch.Tensor):
+        """x must be [n, d_model], on this layer's device, in the layer's dtype."""
+        want = torch.bfloat16 if self.shape.dtype == N.MOE_DTYPE_BF16 else torch.float32
+        if not getattr(x, "is_cuda", False) or x.device != self.w_router.device:
+            raise ValueError(f"x must be a tensor on {self.w_router.device}")
+        if x.dtype != want:
+            raise ValueError(f"x must be {want} for this layer, not {x.dtype}")
+        if x.dim() != 2 or x.shape[1] != self.shape.d_model:
+            raise ValueError(f"x must be [n, {self.shape.d_model}], not {list(x.shape)}")
+
     def forward(self, x: torch.Tensor, stage_events=None, stream=None, save_for_backward: bool = False) -> Outputs:
         """save_for_backward (bf16 layers): run moe_forward_train, which also keeps the fp32 gate and up
         values for backward() (which then skips recomputing them)."""
+        self._check_x(x)
         if x.shape[0] != self.shape.n_tokens:
             self.shape.n_tokens = x.shape[0]
             self._alloc()
@@ -198,8 +209,11 @@ class MoELayer:
             raise ValueError("bf16 weight gradients are written, not accumulated")
         if self.fp8 is not None or self.int4 is not None:
             raise ValueError("the backward pass needs the bf16 expert weights")
+        self._check_x(x)
         if x.shape[0] != self.shape.n_tokens or tuple(dy.shape) != (self.shape.n_tokens, self.shape.d_model):
             raise ValueError("x and dy must match the last forward's tokens")
+        if not dy.is_cuda or dy.device != x.device or dy.dtype != torch.float32:
+            raise ValueError(f"dy must be a float32 tensor on {x.device}")
         if self.bws is None:
             self.bws = torch.empty(max(1, N.backward_workspace_bytes(self.shape)), dtype=torch.uint8,
                                    device=self.device)

@@ -61,6 +61,11 @@ def route(shape, ws_bytes=1 << 30, **ptrs):
     (dict(d_ff=96), N.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=1024, top_k=2), N.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=64, top_k=33), N.MOE_ERR_UNSUPPORTED),
+    # 32-bit row offsets: N * d, and N * (k + S) * max(d, F, Fs), must stay below 2^31
+    (dict(n_tokens=300_000, d_model=7168, d_ff=2048, n_experts=256, top_k=1), N.MOE_ERR_UNSUPPORTED),
+    (dict(n_tokens=40_000, d_model=7168, d_ff=2048, n_experts=256, top_k=8, n_shared=1, d_ff_shared=2048),
+     N.MOE_ERR_UNSUPPORTED),
+    (dict(n_tokens=160_000, d_model=4096, d_ff=14336, n_experts=8, top_k=2), N.MOE_ERR_UNSUPPORTED),
 ])
 def test_shape_validation(kw, status):
     s = shp(**kw)
@@ -87,6 +92,9 @@ def test_null_pointers_and_workspace():
     assert L.moe_grouped_swiglu(*args(0, 256, 1 << 30)) == N.MOE_ERR_INVALID_ARG
     assert L.moe_grouped_swiglu(*args(4, 200, 1 << 30)) == N.MOE_ERR_UNSUPPORTED
     assert L.moe_grouped_swiglu(*args(4, 256, 1000)) == N.MOE_ERR_WORKSPACE
+    # grouped: rows whose 32-bit element offsets would overflow
+    big = (ctypes.byref(s), 4, 14336, FAKE, FAKE, 2, FAKE, 160_000, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert L.moe_grouped_swiglu(*big) == N.MOE_ERR_UNSUPPORTED
     # combine: shared experts need their output
     s2 = shp(n_shared=1, d_ff_shared=128)
     assert L.moe_combine(ctypes.byref(s2), FAKE, FAKE, FAKE, None, FAKE, None) == N.MOE_ERR_INVALID_ARG
@@ -213,3 +221,86 @@ def test_train_forward_entry_point_validates():
     assert ft(shp(dtype=N.MOE_DTYPE_F32)) == N.MOE_ERR_UNSUPPORTED     # bf16 layers only
     assert ft(s, gu=None) == N.MOE_ERR_INVALID_ARG                      # nowhere to keep G and U
     assert ft(s, ws_bytes=16) == N.MOE_ERR_WORKSPACE
+
+
+# ------------------------------------------------------------------ host-side checks of the binding
+
+class FakeDev:
+    """Stands in for a device tensor on a host without a GPU: only what the binding's checks read."""
+
+    def __init__(self, numel, dtype, device="cuda:0", shape=None):
+        import torch
+        self.is_cuda = True
+        self._n = numel
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.shape = tuple(shape) if shape is not None else (numel,)
+
+    def numel(self):
+        return self._n
+
+    def dim(self):
+        return len(self.shape)
+
+
+def _layer_tensors(s, **over):
+    import torch
+    Nt, d, F, E, k = s.n_tokens, s.d_model, s.d_ff, s.n_experts, s.top_k
+    bf, f32, i32, f64 = torch.bfloat16, torch.float32, torch.int32, torch.float64
+    t = dict(x=FakeDev(Nt * d, bf), w_router=FakeDev(E * d, bf), logit_bias=None, select_bias=None,
+             w_gate=FakeDev(E * F * d, bf), w_up=FakeDev(E * F * d, bf), w_down=FakeDev(E * d * F, bf),
+             s_gate=None, s_up=None, s_down=None, y=FakeDev(Nt * d, f32), topk_idx=FakeDev(Nt * k, i32),
+             topk_w=FakeDev(Nt * k, f32), counts=FakeDev(E, i32), offsets=FakeDev(E + 1, i32),
+             perm=FakeDev(Nt * k, i32), slot_pos=FakeDev(Nt * k, i32), prob_sum=FakeDev(E, f64),
+             balance_stat=FakeDev(1, f64))
+    t.update(over)
+    return t
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    s = shp()
+    with pytest.raises(ValueError, match="device"):
+        N.moe_route(s, torch.zeros(64, 128, dtype=torch.bfloat16), None, None, None, None, None, None, None)
+    with pytest.raises(ValueError, match="device"):
+        N._ptr(torch.zeros(4))
+
+
+@pytest.mark.parametrize("name,bad,match", [
+    ("x", dict(numel=64 * 128 - 1), "elements"),            # too small
+    ("x", dict(dtype="float32"), "must be"),                 # fp32 x on a bf16 layer
+    ("y", dict(numel=10), "elements"),
+    ("topk_idx", dict(dtype="int64"), "must be"),
+    ("w_down", dict(numel=5), "elements"),
+    ("perm", dict(device="cuda:1"), "is on"),               # a second device
+    ("prob_sum", dict(dtype="float32"), "must be"),
+])
+def test_binding_checks_buffers(name, bad, match):
+    import torch
+    s = shp()
+    t = _layer_tensors(s)
+    spec = N._layer_spec(s, **t)
+    N._guard("moe_forward", spec)  # the good set passes
+    ref = t[name]
+    kw = dict(numel=ref.numel(), dtype=ref.dtype, device="cuda:0")
+    kw.update({k: (getattr(torch, v) if k == "dtype" else v) for k, v in bad.items()})
+    t[name] = FakeDev(kw["numel"], kw["dtype"], kw["device"])
+    with pytest.raises(ValueError, match=match):
+        N._guard("moe_forward", N._layer_spec(s, **t))
+
+
+def test_layer_checks_x():
+    import torch
+    from sparse_mixture_experts_44_amd.layer import MoELayer
+
+    class Fake:
+        shape = shp()
+        w_router = FakeDev(8 * 128, torch.bfloat16)
+    MoELayer._check_x(Fake, FakeDev(64 * 128, torch.bfloat16, shape=(64, 128)))
+    for x, match in ((FakeDev(64 * 128, torch.float32, shape=(64, 128)), "must be torch.bfloat16"),
+                     (FakeDev(64 * 256, torch.bfloat16, shape=(64, 256)), r"must be \[n, 128\]"),
+                     (FakeDev(64 * 128, torch.bfloat16, device="cuda:1", shape=(64, 128)), "tensor on")):
+        with pytest.raises(ValueError, match=match):
+            MoELayer._check_x(Fake, x)
+    with pytest.raises(ValueError, match="tensor on"):
+        MoELayer._check_x(Fake, torch.zeros(64, 128, dtype=torch.bfloat16))
