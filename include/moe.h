@@ -192,6 +192,31 @@ int moe_forward(const moe_shape* shape, const void* x, const void* w_router,
                 double* prob_sum, double* balance_stat,
                 void* ws, size_t ws_bytes, hipEvent_t* stage_events, hipStream_t stream);
 
+/* moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same arguments as moe_forward without ws and ws_bytes, and the same
+ * kernels and results (bit for bit, on the same device). The workspace is a
+ * static device array inside the library, MOE_NOALLOC_SCRATCH_BYTES bytes on
+ * each device the entry point runs on, held until the process ends; its
+ * address is looked up on the first call on a device. The call allocates
+ * nothing and needs no zeroed memory (every kernel writes what it later
+ * reads). Every call on a device shares that device's array: calls that can
+ * overlap on one device (other streams, other host threads) race and must
+ * be serialised by the caller.
+ * Errors: as moe_forward; MOE_ERR_UNSUPPORTED when moe_workspace_bytes(shape)
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES (decode-sized layers fit: the
+ * DeepSeek-V3-shaped layer at 64 tokens needs about 51 MiB); MOE_ERR_HIP
+ * when the device or the array's address cannot be obtained. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const moe_shape* shape, const void* x, const void* w_router,
+                        const float* logit_bias, const float* select_bias,
+                        const void* w_gate, const void* w_up, const void* w_down,
+                        const void* s_gate, const void* s_up, const void* s_down,
+                        float* y, int32_t* topk_idx, float* topk_w,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
+                        double* prob_sum, double* balance_stat, hipEvent_t* stage_events,
+                        hipStream_t stream);
+
 /* Training forward: moe_forward (bf16 layers) that also keeps, in the
  * caller's gu_save, the fp32 gate and up values G = x W_gate^T and
  * U = x W_up^T of every computed row, for moe_backward (which then skips

@@ -9,7 +9,7 @@ from ._native import (  # noqa: F401
     LIB_PATH, MOE_DTYPE_BF16, MOE_DTYPE_F32, MOE_ERR_HIP, MOE_GRAD_ACCUMULATE, MOE_GRAD_WRITE, MOE_GRAD_WRITE_BF16, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE, MOE_OK, MOE_STAGE_EVENTS, STAGES, MoEError, MoEFp8Scales, MoEShape,
     MoEWeightScales, backward_workspace_bytes, fp8_scales, lib, moe_backward, moe_combine, moe_forward,
-    moe_forward_fp8, moe_forward_int4, moe_forward_train, moe_grouped_swiglu, moe_grouped_swiglu_fp8,
+    MOE_NOALLOC_SCRATCH_BYTES, moe_forward_fp8, moe_forward_int4, moe_forward_noalloc, moe_forward_train, moe_grouped_swiglu, moe_grouped_swiglu_fp8,
     moe_grouped_swiglu_int4, moe_permute, moe_dequantize_fp8, moe_quantize_fp8, moe_quantize_int4, moe_route, moe_router_aux,
     moe_update_select_bias, status_string, train_save_floats, weight_scales, workspace_bytes,
 )

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_STAGE_EVENTS = 6
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 STAGES = ("route", "permute", "gate_up", "down", "combine")
 
 
@@ -65,6 +66,8 @@ _SIGS = {
                                    _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "moe_quantize_fp8": (ctypes.c_int, [ctypes.c_int64, _I, _P, _P, _P, _P]),
     "moe_dequantize_fp8": (ctypes.c_int, [ctypes.c_int64, _I, _P, _P, _P, _P]),
+    "moe_forward_noalloc": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, _P, _P, _P, _P]),
     "moe_train_save_floats": (_SZ, [_SHP]),
     "moe_forward_train": (ctypes.c_int, [_SHP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
@@ -258,6 +261,26 @@ def moe_forward(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_dow
         _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(slot_pos),
         _ptr(prob_sum), _ptr(balance_stat), _ptr(ws),
         ws.numel() * ws.element_size() if ws is not None else 0,
+        ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)))
+
+
+def moe_forward_noalloc(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
+                        s_down, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
+                        balance_stat, stage_events: Optional[Sequence[int]] = None, stream=None):
+    """moe_forward with the library's static device workspace (no ws argument)."""
+    _guard("moe_forward_noalloc", _layer_spec(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down,
+                                              s_gate, s_up, s_down, y, topk_idx, topk_w, counts, offsets, perm,
+                                              slot_pos, prob_sum, balance_stat))
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != MOE_STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {MOE_STAGE_EVENTS} hipEvent_t handles")
+        ev = (ctypes.c_void_p * MOE_STAGE_EVENTS)(*stage_events)
+    _check("moe_forward_noalloc", lib().moe_forward_noalloc(
+        ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias),
+        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(y),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(slot_pos),
+        _ptr(prob_sum), _ptr(balance_stat),
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)))
 
 

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <utility>
 
 #include "moe_common.h"
@@ -745,6 +746,55 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
                     stream));
 #undef MOE_TRY
   return MOE_OK;
+}
+
+
+// ---------------------------------------------------------------------
+// moe_forward without a workspace argument: the workspace is a static device
+// array of this file, one per device, held until the process ends.
+
+// The scratch array. Its host-side name only stands in for the symbol:
+// kernels and copies use the device address that hipGetSymbolAddress returns
+// for the current device (scratch_address below), never the name.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (with that device current) and kept.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_forward_noalloc(const moe_shape* shape, const void* x, const void* w_router, const float* logit_bias,
+                        const float* select_bias, const void* w_gate, const void* w_up, const void* w_down,
+                        const void* s_gate, const void* s_up, const void* s_down, float* y,
+                        int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* slot_pos, double* prob_sum, double* balance_stat, hipEvent_t* stage_events,
+                        hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  // the same workspace layout as moe_forward, so the kernels and their results are the same
+  const size_t need = layout(*shape).total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return forward_impl(shape, x, w_router, logit_bias, select_bias, w_gate, w_up, w_down, s_gate, s_up,
+                      s_down, 0, nullptr, y, topk_idx, topk_w, counts, offsets, perm, slot_pos, prob_sum,
+                      balance_stat, ws, need, stage_events, stream);
 }
 
 }  // extern "C"

@@ -304,3 +304,13 @@ def test_layer_checks_x():
             MoELayer._check_x(Fake, x)
     with pytest.raises(ValueError, match="tensor on"):
         MoELayer._check_x(Fake, torch.zeros(64, 128, dtype=torch.bfloat16))
+
+
+def test_noalloc_rejects_shapes_beyond_its_array_before_any_launch():
+    # moe_forward_noalloc checks the shape's workspace against its static array first
+    L = moe.lib()
+    big = N.MoEShape.make(4096, 4096, 14336, 8, 2)
+    assert L.moe_workspace_bytes(ctypes.byref(big)) > N.MOE_NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(ctypes.byref(big), *([FAKE] * 19), None, None) == N.MOE_ERR_UNSUPPORTED
+    assert L.moe_forward_noalloc(ctypes.byref(shp(top_k=0)), *([FAKE] * 19), None, None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_noalloc(None, *([FAKE] * 19), None, None) == N.MOE_ERR_INVALID_ARG
