@@ -47,6 +47,64 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return __builtin_shufflevector(ab, ce, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// ------------------------------------------------------------------ LDS staging (grouped GEMM, router)
+
+// LDS tile rows hold BK bf16 of K: PPR = BK/8 pieces of 16 bytes, stored at
+// piece ^ swz(row). A wave's MFMA operand read has lanes 0..31 on 32
+// consecutive rows at the same logical piece. These XOR patterns spread every
+// group of 8 lanes (128 bytes per clock) and every group of 16 lanes (256
+// bytes per clock) over distinct banks:
+//   PPR = 8 (128-byte rows): g(r) = (r & 7) ^ ((r >> 3) & 1)
+//   PPR = 4 (64-byte rows):  g(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1)
+//   PPR = 2 (32-byte rows of int4 weights, read 16 bytes per lane per step):
+//                            g(r) = ((r >> 2) ^ (r >> 3)) & 1
+template <int PPR>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (PPR == 8) return (row & 7) ^ ((row >> 3) & 1);
+  else if constexpr (PPR == 4) return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+  else return ((row >> 2) ^ (row >> 3)) & 1;
+}
+
+// Copy 16 bytes per lane from global memory straight into LDS at
+// lds_addr + 16 * lane (global_load_lds_dwordx4; no VGPR staging, counted by
+// vmcnt). It is written as an instruction rather than the builtin: the
+// compiler treats the builtin's LDS write as aliasing every LDS read and
+// would drain all copies in flight (vmcnt(0)) before each fragment read,
+// which defeats the multi-stage prefetch. The instruction has no output
+// registers; the explicit vmcnt waits below order the reads after the copies.
+// On gfx9 an LDS copy needs one wait state after a scalar write of M0 (the
+// compiler inserts it for the builtin, not inside inline asm): hence the nop.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding, then a workgroup barrier. The barrier is written out (not
+// __syncthreads) so that the compiler does not also wait for the LDS copies
+// of later stages that are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// wait_vm_barrier<n> for a wave-uniform n in [0, MAXN] known only at run time
+// (a chain of scalar compares; anything out of range waits for everything).
+template <int MAXN>
+__device__ __forceinline__ void wait_vm_barrier_rt(int n) {
+  if constexpr (MAXN == 0) {
+    wait_vm_barrier<0>();
+  } else {
+    if (n == MAXN) wait_vm_barrier<MAXN>();
+    else wait_vm_barrier_rt<MAXN - 1>(n);
+  }
+}
+
 // ------------------------------------------------------------------ router
 // `partials`: route_blocks(s) x E doubles; `logits`: route_logits_floats(s) floats (workspace).
 int launch_route(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,

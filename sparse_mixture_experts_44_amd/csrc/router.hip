@@ -4,9 +4,16 @@
 // "实现：逐 token 与按专家分组". The bias for selection only is the
 // aux-loss-free balancing of its section "负载均衡".
 //
-// Three kernels:
-//   1. logits_kernel: a VALU GEMM (the matrix cores are kept for the expert
-//      GEMMs).
+// Two forms:
+//   Fused (bf16 layers with 64 <= E <= 256 and at least 1024 tokens):
+//     route_fused_kernel does the whole route() of a tile of tokens in one
+//     kernel: the logits against every expert on the matrix cores (the
+//     logits are a dense contraction of K = d; on the VALU they would take
+//     several times longer), the softmax, selection and renormalisation of
+//     each token by one wavefront from LDS (select_token), and the tile's
+//     fp64 probability sums. prob_sum_kernel then adds the tiles' sums.
+//   Otherwise (small batches, fp32 layers, other E):
+//   1. logits_kernel: a VALU GEMM.
 //      - Grid: (token tile) x (K split) x (expert tile), sized to give every
 //        CU more than one workgroup also at decode sizes (N = 64). At most 8
 //        K splits; few tokens get one output per thread and expert tiles.
@@ -18,7 +25,7 @@
 //      - Each chunk is summed into a fresh partial before it is added to the
 //        running sum.
 //      - Output: fp32 partial logits [split][N][E].
-//   2. select_kernel: one wavefront per token.
+//   2. select_kernel: one wavefront per token (select_token).
 //      - Sums the splits in split order, adds the logit bias, then softmax
 //        with butterfly reductions in a fixed order, the selection score, and
 //        k rounds of a wave arg-max. A larger score wins; on equal scores the
@@ -27,6 +34,9 @@
 //      - Adds p into fp64 per-workgroup sums in a fixed order.
 //   3. prob_sum_kernel: one wavefront per expert adds the workgroup sums with
 //      a fixed tree, so prob_sum is bit-reproducible.
+// The router z-loss and the backward pass recompute the logits alone; large
+// bf16 routers run that as one grouped GEMM on the matrix cores
+// (compute_logits).
 #include <math.h>
 
 #include "moe_common.h"
@@ -186,6 +196,74 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const uint32_t* __rest
 
 // ---------------------------------------------------------------- 2. select
 
+// One token's selection, by one wavefront. v holds the token's logits (with
+// the logit bias), EL per lane: expert e = lane + 64 m, -inf past E. Softmax
+// with butterfly reductions in a fixed order, the selection score s = p +
+// select bias, k rounds of a wave arg-max (a larger score wins; on equal
+// scores the lower expert index), the k weights (renormalised or not), and p
+// added into pacc.
+template <int EL>
+__device__ __forceinline__ void select_token(float (&v)[EL], const float (&sb)[EL], int lane, int E, int k,
+                                             int renorm, int32_t* __restrict__ idx_row,
+                                             float* __restrict__ w_row, double (&pacc)[EL]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int m = 0; m < EL; ++m) mx = fmaxf(mx, v[m]);
+  mx = wave_max(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int m = 0; m < EL; ++m) {
+    const int e = lane + kWave * m;
+    v[m] = (e < E) ? expf(v[m] - mx) : 0.f;
+    sum += v[m];
+  }
+  sum = wave_sum(sum);
+  float p[EL], s[EL];
+#pragma unroll
+  for (int m = 0; m < EL; ++m) {
+    p[m] = v[m] / sum;
+    pacc[m] += (double)p[m];
+    s[m] = p[m] + sb[m];
+  }
+  uint32_t taken = 0;
+  float sel_sum = 0.f, mine_p = 0.f;
+  int mine_idx = -1;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY, bp = 0.f;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int m = 0; m < EL; ++m) {
+      const int e = lane + kWave * m;
+      if (e < E && !((taken >> m) & 1u) && (s[m] > bv || (s[m] == bv && e < bi))) {
+        bv = s[m];
+        bi = e;
+        bp = p[m];
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      const float op = __shfl_xor(bp, o, kWave);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+        bp = op;
+      }
+    }
+    if (bi < E && (bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+    if (lane == j) {
+      mine_idx = bi < E ? bi : -1;
+      mine_p = bp;
+    }
+    sel_sum += bp;
+  }
+  if (lane < k) {
+    idx_row[lane] = mine_idx;
+    w_row[lane] = renorm ? mine_p / sel_sum : mine_p;
+  }
+}
+
 template <int EL>  // experts per lane: E <= 64 * EL
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const float* __restrict__ part, int splits, const float* __restrict__ logit_bias,
@@ -208,8 +286,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   for (int tt = wv; tt < tpb; tt += kThreads / kWave) {
     const int t = t0 + tt;
     if (t >= N) break;
-    float v[EL], p[EL], s[EL];
-    float mx = -INFINITY;
+    float v[EL];
 #pragma unroll
     for (int m = 0; m < EL; ++m) {
       const int e = lane + kWave * m;
@@ -229,60 +306,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         l += lb[m];
       }
       v[m] = l;
-      mx = fmaxf(mx, l);
     }
-    mx = wave_max(mx);
-    float sum = 0.f;
-#pragma unroll
-    for (int m = 0; m < EL; ++m) {
-      const int e = lane + kWave * m;
-      v[m] = (e < E) ? expf(v[m] - mx) : 0.f;
-      sum += v[m];
-    }
-    sum = wave_sum(sum);
-#pragma unroll
-    for (int m = 0; m < EL; ++m) {
-      p[m] = v[m] / sum;
-      pacc[m] += (double)p[m];
-      s[m] = p[m] + sb[m];
-    }
-    uint32_t taken = 0;
-    float sel_sum = 0.f, mine_p = 0.f;
-    int mine_idx = -1;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY, bp = 0.f;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int m = 0; m < EL; ++m) {
-        const int e = lane + kWave * m;
-        if (e < E && !((taken >> m) & 1u) && (s[m] > bv || (s[m] == bv && e < bi))) {
-          bv = s[m];
-          bi = e;
-          bp = p[m];
-        }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oi = __shfl_xor(bi, o, kWave);
-        const float op = __shfl_xor(bp, o, kWave);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-          bp = op;
-        }
-      }
-      if (bi < E && (bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-      if (lane == j) {
-        mine_idx = bi < E ? bi : -1;
-        mine_p = bp;
-      }
-      sel_sum += bp;
-    }
-    if (lane < k) {
-      topk_idx[(size_t)t * k + lane] = mine_idx;
-      topk_w[(size_t)t * k + lane] = renorm ? mine_p / sel_sum : mine_p;
-    }
+    select_token<EL>(v, sb, lane, E, k, renorm, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, pacc);
   }
   // per-workgroup probability sums, waves combined in a fixed order
 #pragma unroll
@@ -292,6 +317,130 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     double a = s_part[0][e];
 #pragma unroll
     for (int q = 1; q < kThreads / kWave; ++q) a += s_part[q][e];
+    partials[(size_t)blockIdx.x * E + e] = a;
+  }
+}
+
+// ---------------------------------------------------------------- 2b. fused router (bf16, prefill)
+
+// The whole route() for a tile of TM tokens in one kernel: the logits against
+// all experts on the matrix cores, then the selection of 2. from LDS, then
+// the tile's probability sums.
+// - 8 waves as WT x WE; wave (wt, we) computes tokens 32 wt .. + 32 of the
+//   tile against experts 32 we .. + 32 (v_mfma_f32_32x32x16_bf16, fp32 sums of
+//   exact bf16 products). TM = 32 WT, and the tile spans EP = 32 WE >= E
+//   experts.
+// - K runs in steps of 64 through NS LDS stages. A stage holds the TM x rows,
+//   then the EP W_r rows, 128 bytes each, filled by direct global->LDS copies
+//   of 8 rows per instruction (coalesced 128-byte row pieces), 16-byte pieces
+//   XOR-swizzled by row so that the MFMA operand reads hit distinct banks.
+//   W_r is read by every workgroup and stays in L2.
+// - Rows past N or E re-read the last row; their results are never used.
+template <int WT, int NS, bool ROT>
+__global__ __launch_bounds__(512, 1) void route_fused_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const float* __restrict__ logit_bias,
+    const float* __restrict__ select_bias, int N, int d, int E, int k, int renorm,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, double* __restrict__ partials) {
+  constexpr int NW = 8, NT = NW * kWave;
+  constexpr int WE = NW / WT;
+  constexpr int TM = 32 * WT, EP = 32 * WE;
+  constexpr int EL = (EP + kWave - 1) / kWave;  // experts per lane in the selection
+  constexpr int ROWS = TM + EP;                 // stage rows: x, then W_r
+  constexpr int STAGE = ROWS * 128;
+  constexpr int INS = ROWS / 8;                 // 1 KB copy instructions per stage
+  constexpr int PER = (INS + NW - 1) / NW;      // per wave, at most
+  constexpr int LS = EP + 4;                    // row stride of the logits tile (floats)
+  static_assert(INS * 8 == ROWS && NS * STAGE >= TM * LS * 4 + NW * kWave * EL * 8, "tile shape");
+  __shared__ __attribute__((aligned(1024))) uint8_t s_tile[NS * STAGE];  // later: logits tile, then sums
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave / WE, we = wave % WE;
+  const int t0 = blockIdx.x * TM;
+
+  // copy i of this wave: instruction c = wave + NW i fills rows 8c .. 8c + 7; the lane writes
+  // piece lane % 8 of row 8c + lane / 8, which holds the logical piece (lane % 8) ^ swz(row)
+  const int cnt = (INS - wave + NW - 1) / NW;  // this wave's copies per stage (wave-uniform)
+  const bf16_t* src[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = min(wave + NW * i, INS - 1);
+    const int r = 8 * c + (lane >> 3);
+    const int pc = ((lane & 7) ^ swz<8>(r)) * 8;
+    src[i] = r < TM ? x + (size_t)min(t0 + r, N - 1) * d + pc : w + (size_t)min(r - TM, E - 1) * d + pc;
+  }
+  const uint32_t lds0 = lds_addr(&s_tile[0]);
+  const int nk = d / 64;
+  // ROT: workgroup b walks K from step b mod nk on, wrapping, so that the
+  // workgroups do not all read the same W_r lines at once
+  const int rot = ROT ? (int)(blockIdx.x % (unsigned)nk) : 0;
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (kt % NS) * STAGE;
+    int ks = kt + rot;
+    ks -= ks >= nk ? nk : 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (i < cnt) dma16(src[i] + ks * 64, st + (wave + NW * i) * 1024);
+  };
+
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < NS - 1; ++s2)
+    if (s2 < nk) issue(s2);
+  const int ra = wt * 32 + (lane & 31), rb = TM + we * 32 + (lane & 31);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed once at most (stages issued after it) * cnt copies of this wave are
+    // outstanding (loads complete in order); the barrier covers the other waves' copies
+    const int later = min(NS - 2, nk - 1 - kt);  // stages issued after stage kt
+    if (cnt == PER) wait_vm_barrier_rt<(NS - 2) * PER>(later * PER);
+    else wait_vm_barrier_rt<(NS - 2) * (PER - 1)>(later * (PER - 1));
+    if (kt + NS - 1 < nk) issue(kt + NS - 1);  // the buffer of stage kt - 1, read by every wave already
+    const uint8_t* sa = &s_tile[(kt % NS) * STAGE];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int chunk = ks * 2 + (lane >> 5);
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(sa + ra * 128 + ((chunk ^ swz<8>(ra)) << 4));
+      const bf16x8_t bf = *reinterpret_cast<const bf16x8_t*>(sa + rb * 128 + ((chunk ^ swz<8>(rb)) << 4));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave is done with the stages: the logits tile reuses them
+  float* s_l = reinterpret_cast<float*>(s_tile);
+  // acc[v]: token 8 (v / 4) + 4 (lane / 32) + (v % 4) of the wave's 32, expert lane % 32 of its 32
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    s_l[(wt * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * LS + we * 32 + (lane & 31)] = acc[v];
+  __syncthreads();
+
+  double pacc[EL];
+  float lb[EL], sb[EL];
+#pragma unroll
+  for (int m = 0; m < EL; ++m) {
+    const int e = lane + kWave * m;
+    pacc[m] = 0.0;
+    lb[m] = (logit_bias && e < E) ? logit_bias[e] : 0.f;
+    sb[m] = (select_bias && e < E) ? select_bias[e] : 0.f;
+  }
+  for (int tt = wave; tt < TM; tt += NW) {
+    const int t = t0 + tt;
+    if (t >= N) break;
+    float v[EL];
+#pragma unroll
+    for (int m = 0; m < EL; ++m) {
+      const int e = lane + kWave * m;
+      v[m] = (e < E) ? s_l[tt * LS + e] + lb[m] : -INFINITY;
+    }
+    select_token<EL>(v, sb, lane, E, k, renorm, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, pacc);
+  }
+  double* s_part = reinterpret_cast<double*>(s_tile + TM * LS * 4);  // past the logits tile
+#pragma unroll
+  for (int m = 0; m < EL; ++m) s_part[wave * kWave * EL + lane + kWave * m] = pacc[m];
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    double a = s_part[e];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) a += s_part[q * kWave * EL + e];
     partials[(size_t)blockIdx.x * E + e] = a;
   }
 }
@@ -544,9 +693,38 @@ size_t route_logits_floats(const moe_shape& s) {
   return (size_t)L.splits * s.n_tokens * s.n_experts;
 }
 
+// The fused router (2b) serves bf16 layers with 64 <= E <= 256 and enough tokens
+// to give the chip a workgroup per CU or so; the others take logits + select.
+bool route_fused(const moe_shape& s) {
+  return s.dtype == MOE_DTYPE_BF16 && s.n_experts >= 64 && s.n_experts <= 256 && s.n_tokens >= 1024;
+}
+
+template <int WT, int NS, bool ROT>
+void launch_route_fused_t(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
+                          const float* select_bias, int32_t* topk_idx, float* topk_w, double* partials, int* nb,
+                          hipStream_t st) {
+  constexpr int TM = 32 * WT;
+  *nb = (s.n_tokens + TM - 1) / TM;
+  hipLaunchKernelGGL((route_fused_kernel<WT, NS, ROT>), dim3(*nb), dim3(512), 0, st, static_cast<const bf16_t*>(x),
+                     static_cast<const bf16_t*>(w_router), logit_bias, select_bias, s.n_tokens, s.d_model,
+                     s.n_experts, s.top_k, s.renormalize, topk_idx, topk_w, partials);
+}
+
 int launch_route(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                  const float* select_bias, int32_t* topk_idx, float* topk_w, double* prob_sum,
                  double* partials, float* logits, float* split_ws, size_t split_bytes, hipStream_t stream) {
+  if (route_fused(s)) {
+    int nb = 0;
+    if (s.n_experts <= 64)        // 128 tokens x 64 experts per workgroup
+      launch_route_fused_t<4, 4, true>(s, x, w_router, logit_bias, select_bias, topk_idx, topk_w, partials, &nb, stream);
+    else if (s.n_experts <= 128)  // 64 x 128
+      launch_route_fused_t<2, 4, true>(s, x, w_router, logit_bias, select_bias, topk_idx, topk_w, partials, &nb, stream);
+    else                          // 32 x 256
+      launch_route_fused_t<1, 4, true>(s, x, w_router, logit_bias, select_bias, topk_idx, topk_w, partials, &nb, stream);
+    hipLaunchKernelGGL(prob_sum_kernel, dim3((s.n_experts + 3) / 4), dim3(kThreads), 0, stream, partials, nb,
+                       s.n_experts, prob_sum);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
   int splits = 1;
   if (const int st = compute_logits(s, x, w_router, logits, split_ws, split_bytes, &splits, stream)) return st;
   const int nb = route_blocks(s);

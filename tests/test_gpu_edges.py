@@ -52,6 +52,10 @@ CASES = {
                             d_ff=256, n_shared=1, d_ff_shared=128),
     # router logits on the matrix cores with 8 tiles of K = 1024: the K loops split over extra workgroups
     "wide_router": small("wide_router", n_tokens=2048, n_experts=256, top_k=8, d_model=1024, d_ff=64),
+    # 256 rows per expert on average, but a selection bias piles them on a few experts (tall and
+    # short segments in one launch of 256-row tiles), and a shared expert
+    "large_and_small": small("large_and_small", n_tokens=2048, n_experts=32, top_k=4, d_model=256, d_ff=256,
+                             n_shared=1, d_ff_shared=128, select_bias=0.1),
 }
 
 
@@ -134,6 +138,9 @@ def _run_grouped(cfg, lay, x, offs, perm, rpt, max_rows, extra_ws=0):
     ("bf16", [1279, 0, 1100, 33, 1250, 1270], 0, 0),                # the same class, ragged, empty, tiny
     ("bf16", [1279, 0, 1100, 33, 1250, 1270], 64 << 20, 3 * 4932),  # max_rows 4x the rows: a grid 4x the
                                                                     # tiles, so both phases split along K
+    # 256-row tiles with segments of 1, 2, 31..33 and 63..65 rows among them
+    ("bf16", [1, 2, 31, 32, 33, 63, 64, 65, 600, 700, 800, 0, 900], 0, 0),
+    ("bf16", [1, 2, 31, 32, 33, 63, 64, 65, 600, 700, 800, 0, 900], 64 << 20, 0),
 ])
 def test_grouped_segment_edges(dtype, sizes, extra_ws, slack):
     d, F = 128, 256
