@@ -143,7 +143,18 @@ def _run_grouped(cfg, lay, x, offs, perm, rpt, max_rows, extra_ws=0):
     ("bf16", [1, 2, 31, 32, 33, 63, 64, 65, 600, 700, 800, 0, 900], 64 << 20, 0),
 ])
 def test_grouped_segment_edges(dtype, sizes, extra_ws, slack):
-    d, F = 128, 256
+    _segment_edges(dtype, sizes, extra_ws, slack, 128, 256)
+
+
+@pytest.mark.parametrize("sizes,extra_ws", [
+    ([0, 1, 63, 64, 65, 0, 150, 191, 192, 100], 0),       # 64 to 191 mean rows: 64 x 512 gate|up tiles,
+    ([0, 1, 63, 64, 65, 0, 150, 191, 192, 100], 1 << 20),  # a partial second n-tile (F = 320), split tails
+])
+def test_grouped_wide_gate_up_edges(sizes, extra_ws):
+    _segment_edges("bf16", sizes, extra_ws, 0, 192, 320)
+
+
+def _segment_edges(dtype, sizes, extra_ws, slack, d, F):
     cfg, lay, x, offs, perm = _grouped_case(sizes, d, F, dtype)
     rpt = 3
     out = _run_grouped(cfg, lay, x, offs, perm, rpt, int(offs[-1]) + slack, extra_ws)
