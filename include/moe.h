@@ -348,16 +348,17 @@ int moe_forward_fp8(const moe_shape* shape, const void* x, const void* w_router,
  * Packed format: a row of K codes is K/2 bytes, in blocks of 64 codes (32
  * bytes). In the block of codes [k0, k0 + 64), the little-endian 32-bit
  * word at byte 16*h + 4*s (h = 0, 1; s = 0..3) holds codes
- * k0 + 16*s + 8*h + j, j = 0..7, each as u = q + 8 in a 4-bit field: code j
- * in nibble j/2 when j is even and in nibble 4 + j/2 when j is odd (nibble
- * n = bits [4n, 4n + 4)). K must be a multiple of 64.
+ * k0 + 16*s + 8*h + j, j = 0..7, each in a 4-bit sign and magnitude field
+ * (bit 3 set for q < 0, bits 0..2 = |q|): code j in byte j % 4 of the word,
+ * its low nibble for j < 4 and its high nibble for j >= 4. K must be a
+ * multiple of 64.
  * --------------------------------------------------------------------- */
 
 /* Quantise a bf16 matrix [rows, cols], row by row:
  *   scales[r] = max_c |w[r, c]| / 7                             (fp32 division)
  *   q[r, c]   = w[r, c] / scales[r] rounded to the nearest integer, ties to
  *               even (fp32 division), clamped to [-7, 7]
- * An all-zero row gets scale 0 and codes 0 (bytes 0x88).
+ * An all-zero row gets scale 0 and codes 0 (bytes 0x00).
  *   w_bf16 [rows, cols] bf16 in;  packed [rows, cols/2] uint8 out (format
  *   above);  scales [rows] fp32 out
  * cols must be a multiple of 64 and rows < 2^31 (else MOE_ERR_UNSUPPORTED). */

@@ -170,7 +170,13 @@ def dequantize_fp8_rows(codes, scales) -> np.ndarray:
 # ---------------------------------------------------------------- int4 weights (W4A16)
 
 INT4_MAX = 7
-_INT4_NIBBLE = np.array([0, 4, 1, 5, 2, 6, 3, 7])  # nibble holding code j of a packed word
+_INT4_SHIFT = np.array([8 * (j % 4) + 4 * (j // 4) for j in range(8)])  # bit position of code j in its word
+
+
+def _int4_field(q):
+    """The 4-bit sign and magnitude field of int4 codes: 8 + |q| for q < 0, else q."""
+    q = np.asarray(q, dtype=np.int64)
+    return np.where(q < 0, 8 - q, q)
 
 
 def quantize_int4_rows(w) -> tuple:
@@ -196,15 +202,17 @@ def dequantize_int4_rows(codes, scales) -> np.ndarray:
 def pack_int4_rows(codes) -> np.ndarray:
     """The packed storage of int4 codes [rows, cols] (cols a multiple of 64):
     per block of 64 codes, the little-endian 32-bit word at byte 16 h + 4 s
-    holds codes 16 s + 8 h + j (j = 0..7) as q + 8, code j in nibble j / 2 (j
-    even) or 4 + j / 2 (j odd). Returns uint8 [rows, cols / 2]."""
+    holds codes 16 s + 8 h + j (j = 0..7), each as a 4-bit sign and
+    magnitude field (8 + |q| for q < 0, else q), code j in byte j % 4 of the
+    word, low nibble for j < 4 and high nibble for j >= 4. Returns uint8
+    [rows, cols / 2]."""
     q = np.asarray(codes, dtype=np.int64)
     rows, cols = q.shape
-    u = (q + 8).reshape(rows, cols // 64, 4, 2, 8).astype(np.uint64)   # [row, block, s, h, j]
+    f = _int4_field(q).reshape(rows, cols // 64, 4, 2, 8).astype(np.uint64)   # [row, block, s, h, j]
     words = np.zeros((rows, cols // 64, 4, 2), dtype=np.uint64)
     for j in range(8):
-        words |= u[..., j] << np.uint64(4 * _INT4_NIBBLE[j])
-    words = words.transpose(0, 1, 3, 2)                                # [row, block, h, s]
+        words |= f[..., j] << np.uint64(_INT4_SHIFT[j])
+    words = words.transpose(0, 1, 3, 2)                                                   # [row, block, h, s]
     return np.ascontiguousarray(words.astype("<u4")).view(np.uint8).reshape(rows, cols // 2)
 
 
@@ -216,7 +224,8 @@ def unpack_int4_rows(packed, cols: int) -> np.ndarray:
     words = words.transpose(0, 1, 3, 2).astype(np.int64)                           # [row, block, s, h]
     q = np.zeros((rows, cols // 64, 4, 2, 8), dtype=np.int64)
     for j in range(8):
-        q[..., j] = ((words >> (4 * int(_INT4_NIBBLE[j]))) & 0xF) - 8
+        f = (words >> int(_INT4_SHIFT[j])) & 0xF
+        q[..., j] = np.where(f & 8, -(f & 7), f & 7)
     return q.reshape(rows, cols).astype(np.int8)
 
 

@@ -202,22 +202,20 @@ __device__ __forceinline__ int nmajor_offset(int k, int n) {
 
 constexpr int kBandM = 8;  // m-tiles per band of the tile order
 
-// Int4 weights: 8 offset-binary codes u = q + 8 (nibbles of w) -> the bf16
-// values 128 + u, exactly (a bf16 with exponent 2^7 steps by 1 up to 255):
-// each nibble goes into the low mantissa bits of 0x4300 (= 128). Element 2i
-// takes nibble i and element 2i + 1 nibble i + 4, which fixes the packing.
-// The MFMA then sums x * (q + 136); the 136 * sum(x) part is removed in the
-// epilogue (an extra MFMA per row block against a fragment of 136s).
-__device__ __forceinline__ bf16x8_t int4x8_to_bf16_biased(uint32_t w) {
-  constexpr uint32_t kMask = 0x000F000Fu, kExp = 0x43004300u;
-  u32x4_t r;
-  r.x = (w & kMask) | kExp;
-  r.y = ((w >> 4) & kMask) | kExp;
-  r.z = ((w >> 8) & kMask) | kExp;
-  r.w = ((w >> 12) & kMask) | kExp;
-  return __builtin_bit_cast(bf16x8_t, r);
+// Int4 weights: a 32-bit word holds 8 codes q in [-7, 7] as 4-bit sign and
+// magnitude (bit 3 the sign, bits 0..2 |q|); code j sits in byte j % 4, in
+// its low nibble for j < 4 and its high nibble for j >= 4. Moving the sign
+// bit to bit 7 of its byte makes each code the E4M3 byte whose value is
+// q * 2^-9 (exponent field 0: a subnormal with mantissa |q|), which the FP8
+// widening turns into bf16 exactly: the 8 operands of one k16 step, in code
+// order. The MFMA then sums x * q * 2^-9 exactly product by product, and the
+// epilogue multiplies by 2^9 times the row scale.
+__device__ __forceinline__ bf16x8_t int4x8_to_bf16(uint32_t w) {
+  const uint32_t lo = ((w << 4) & 0x80808080u) | (w & 0x07070707u);  // codes 0..3
+  const uint32_t hi = (w & 0x80808080u) | ((w >> 4) & 0x07070707u);  // codes 4..7
+  return fp8x8_to_bf16(lo, hi);
 }
-constexpr uint32_t kBf16Of136 = 0x4308u;  // 136 = 128 + 8: the offset of the biased int4 values
+constexpr float kInt4Unit = 512.f;  // 2^9: the widened int4 operands are q * 2^-9
 
 // Where tile T lies: its entry (group of a set), rows and columns.
 struct TileGeom {
@@ -296,14 +294,14 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int G, long long cap_
 // (lane & 31) and row 8 (v / 4) + 4 (lane / 32) + (v % 4) of 32x32 block
 // (i, j). Phase 1 writes h = bf16(silu(g) * u), phase 2 writes fp32 O;
 // with quantised weights (WQ = 8: FP8, 4: int4) each column is first
-// multiplied by its weight row's scale, and with int4 weights the offset
-// sums corr[i] (136 * sum(x) of each row) are subtracted before that (none
-// when corr is NULL: the K-parts of split tiles are stored already reduced).
+// multiplied by its weight row's scale (int4: times 2^9, the unit of the
+// widened codes).
 template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE, int FM, int NB, bool OBF = false,
           bool ACC = false>
 __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetView& S, const TileGeom& t,
-                                           int d, int lane, int wm, int wn, const f32x16_t* corr = nullptr) {
-  constexpr bool WS = WQ != 0, W4 = WQ == 4;
+                                           int d, int lane, int wm, int wn) {
+  constexpr bool WS = WQ != 0;
+  constexpr float unit = WQ == 4 ? kInt4Unit : 1.f;
   constexpr int TM = BM / WGM;
   constexpr int BH = P1 ? BN / 2 : BN;
   constexpr int TN = BH / WGN;
@@ -319,10 +317,10 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
     if constexpr (WS) {
       const int c = min(col0 + j * 32, ncols - 1);
       if constexpr (P1) {
-        sc0[j] = S.sg[(size_t)g * F + c];
-        sc1[j] = S.su[(size_t)g * F + c];
+        sc0[j] = S.sg[(size_t)g * F + c] * unit;
+        sc1[j] = S.su[(size_t)g * F + c] * unit;
       } else {
-        sc0[j] = S.sd[(size_t)g * d + c];
+        sc0[j] = S.sd[(size_t)g * d + c] * unit;
       }
     }
   }
@@ -359,8 +357,6 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
         const int r = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
         if (decltype(check)::value && r >= t.mvalid) continue;
         const size_t row = (size_t)(t.start + t.m0 + r);
-        float c = 0.f;
-        if constexpr (W4) c = corr ? corr[i][v] : 0.f;
         if constexpr (P1) {
           bf16_t* hrow = static_cast<bf16_t*>(S.h) + row * F + col0;
           if constexpr (SAVE) {  // training: keep the gate and up values for the backward pass
@@ -374,7 +370,7 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             if (col0 + j * 32 < ncols)
-              hrow[j * 32] = WS ? silu_mul_bf16((acc[i][j][v] - c) * sc0[j], (acc[i][j + FN][v] - c) * sc1[j])
+              hrow[j * 32] = WS ? silu_mul_bf16(acc[i][j][v] * sc0[j], acc[i][j + FN][v] * sc1[j])
                                 : silu_mul_bf16(acc[i][j][v], acc[i][j + FN][v]);
         } else if constexpr (OBF) {  // bf16 output (round to nearest even)
           bf16_t* orow = reinterpret_cast<bf16_t*>(S.out) + row * d + col0;
@@ -385,7 +381,7 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
           float* orow = S.out + row * d + col0;
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            if (col0 + j * 32 < ncols) orow[j * 32] = WS ? (acc[i][j][v] - c) * sc0[j] : acc[i][j][v];
+            if (col0 + j * 32 < ncols) orow[j * 32] = WS ? acc[i][j][v] * sc0[j] : acc[i][j][v];
         }
       }
     }
@@ -404,9 +400,8 @@ __device__ __forceinline__ void store_tile(f32x16_t (&acc)[FM][NB], const SetVie
 // and each output column is multiplied by its weight row's scale in the
 // epilogue. WQ = 4: int4 codes, two per byte (a quarter of the bytes). Each
 // lane reads its 16 bytes of a B row once per step (the 4 words of its 4
-// k16 steps) and widens a word per k16 step to the biased values 128 + u;
-// an extra MFMA per row block accumulates 136 * sum(x), which the epilogue
-// subtracts before the scale.
+// k16 steps) and widens a word per k16 step to q * 2^-9 exactly
+// (int4x8_to_bf16).
 // SPREAD: the copies that refill a stage go out in equal pieces, one before
 // each k16 step of the first half of the step, instead of all at its start,
 // so that fewer copies queue at once behind the barrier (3-5% faster on
@@ -601,17 +596,12 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     };
 
     f32x16_t acc[FM][NB];
-    f32x16_t corr[W4 ? FM : 1];  // int4: 136 * sum(x) per row
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-      if constexpr (W4)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) corr[i][v] = 0.f;
-    }
 
     // 32-row MFMA blocks of this wave that hold segment rows: a segment's last
     // tile is often short, and its empty blocks skip their reads and MFMAs.
@@ -662,7 +652,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
             const i16x4_t lo = lds_read_tr16(pt), hi = lds_read_tr16(pt + 4 * ROWBN);            \
             bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)); \
           } else if constexpr (W4) {                                                             \
-            bfr[j] = int4x8_to_bf16_biased(wq[j][ks]);                                           \
+            bfr[j] = int4x8_to_bf16(wq[j][ks]);                                                  \
           } else if constexpr (W8) {                                                             \
             /* piece ks holds the 16 codes of this k16 step; lanes 32-63 take its upper 8 */     \
             const u32x2_t q = *reinterpret_cast<const u32x2_t*>(sb + r * ROWB + ((ks ^ swz<PPB>(r)) << 4) + ((lane >> 5) << 3)); \
@@ -675,11 +665,6 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
           if (!(ACTIVE(i))) continue;                                                            \
           _Pragma("unroll") for (int j = 0; j < NB; ++j)                                         \
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0); \
-          if constexpr (W4) {                                                                    \
-            const u32x4_t k136 = {kBf16Of136 * 0x10001u, kBf16Of136 * 0x10001u,                  \
-                                  kBf16Of136 * 0x10001u, kBf16Of136 * 0x10001u};                \
-            corr[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], __builtin_bit_cast(bf16x8_t, k136), corr[i], 0, 0, 0); \
-          }                                                                                      \
         }                                                                                        \
       }                                                                                          \
     }
@@ -701,7 +686,6 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     // ---- epilogue
     if (part >= 0) {
       // a K-part of a split tail tile: raw accumulators, thread-major, for the reduce kernel
-      // (int4: with this part's offset sum removed, so that the parts add up to sum(x * q))
       float* dst = p.split_ws + kSplitHeader + ((size_t)(T - sp.base) * sp.S + part) * (BM * BN);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -709,10 +693,10 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
         for (int j = 0; j < NB; ++j)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            dst[((i * NB + j) * 16 + v) * NT + tid] = W4 ? acc[i][j][v] - corr[i][v] : acc[i][j][v];
+            dst[((i * NB + j) * 16 + v) * NT + tid] = acc[i][j][v];
       continue;
     }
-    store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF, ACC>(acc, S, tg, d, lane, wm, wn, corr);
+    store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF, ACC>(acc, S, tg, d, lane, wm, wn);
   }
 }
 

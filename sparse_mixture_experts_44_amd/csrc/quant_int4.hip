@@ -14,10 +14,11 @@
 // Packed layout (what the grouped GEMM reads): a row of K codes takes K / 2
 // bytes, in blocks of 64 codes (32 bytes). In the block of codes
 // [k0, k0 + 64), the 32-bit word at byte 16 h + 4 s (h = 0, 1; s = 0..3)
-// holds the 8 codes k0 + 16 s + 8 h + j (j = 0..7) as u = q + 8: code j in
-// nibble j / 2 when j is even, in nibble 4 + j / 2 when j is odd (nibble n =
-// bits [4n, 4n + 4)). That is the order in which the GEMM widens a word into
-// the 8 bf16 operands of one lane's k16 step.
+// holds the 8 codes k0 + 16 s + 8 h + j (j = 0..7), each as 4-bit sign and
+// magnitude (bit 3 set for q < 0, bits 0..2 = |q|): code j in byte j % 4 of
+// the word, in its low nibble for j < 4 and its high nibble for j >= 4. That
+// is the order in which the GEMM widens a word into the 8 bf16 operands of
+// one lane's k16 step.
 #include <math.h>
 
 #include "moe_common.h"
@@ -27,8 +28,8 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// nibble of code j (0..7) within its 32-bit word
-__device__ __forceinline__ int nibble_of(int j) { return (j & 1) ? 4 + (j >> 1) : (j >> 1); }
+// bit position of code j (0..7) within its 32-bit word: byte j % 4, high nibble for j >= 4
+__device__ __forceinline__ int shift_of(int j) { return 8 * (j & 3) + 4 * (j >> 2); }
 
 // One workgroup per weight row: the row maximum, then one 64-code block per thread per pass.
 __global__ __launch_bounds__(kThreads) void quantize_int4_kernel(const u32x4_t* __restrict__ w, int cols,
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void quantize_int4_kernel(const u32x4_t* 
         const float x = __uint_as_float((j & 1) ? (two & 0xffff0000u) : (two << 16));
         int q = 0;
         if (scale > 0.f) q = (int)fminf(fmaxf(rintf(x / scale), -7.f), 7.f);
-        acc |= (uint32_t)(q + 8) << (4 * nibble_of(j));
+        acc |= (uint32_t)(q < 0 ? 8 - q : q) << shift_of(j);  // sign and magnitude
       }
       word[h * 4 + s] = acc;
     }

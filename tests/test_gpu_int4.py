@@ -40,7 +40,7 @@ def test_int4_quantize_bit_exact():
     rng = np.random.default_rng(50)
     R, C = 300, 192
     w = (rng.standard_normal((R, C)) * np.exp2(rng.uniform(-12, 6, (R, 1)))).astype(np.float32)
-    w[3] = 0.0                                   # all-zero row: scale 0, codes 0 (bytes 0x88)
+    w[3] = 0.0                                   # all-zero row: scale 0, codes 0 (bytes 0x00)
     w[4] = -0.0
     w[5, :] = 1e-3
     w[5, 7] = -7.0                               # one dominant entry: the rest round to 0
@@ -53,7 +53,7 @@ def test_int4_quantize_bit_exact():
     np.testing.assert_array_equal(scales.view(np.uint32), rs.view(np.uint32))
     np.testing.assert_array_equal(packed, O.pack_int4_rows(rq))
     np.testing.assert_array_equal(O.unpack_int4_rows(packed, C)[8, :8], [7, 0, 2, 2, 0, -2, -2, 4])
-    assert scales[3] == 0 and np.all(packed[3] == 0x88) and np.all(packed[4] == 0x88)
+    assert scales[3] == 0 and np.all(packed[3] == 0x00) and np.all(packed[4] == 0x00)
 
 
 def _int4_layer(cfg, layer):
@@ -159,5 +159,21 @@ def test_int4_dsv3_decode_full():
     t = time.time()
     layer, x = mi.make_layer(cfg), mi.make_x(cfg)
     log(f"generated {cfg.name} in {time.time() - t:.1f}s")
+    gpu = run_int4(cfg, layer, x)
+    check_int4(cfg, layer, x, gpu, np.arange(cfg.n_tokens))
+
+
+@pytest.mark.parametrize("kw", [
+    # layers of the forward sweep's generator with N = 1000, E = 128, k = 2, d = 192, d_ff = 128 and no
+    # renormalisation, the shape where an earlier int4 widening (x (q + 136) minus 136 sum(x)) lost precision
+    dict(layer_id=1000, x_id=1000),
+    dict(layer_id=1003, x_id=1003, n_shared=2, d_ff_shared=128),
+    dict(layer_id=1012, x_id=1012, n_shared=2, d_ff_shared=64, select_bias=0.05, logit_skew=1.0),
+    dict(layer_id=1007, x_id=1007),
+])
+def test_int4_sweep_shaped_layers_every_row(kw):
+    cfg = mi.MoEConfig(name="int4_sweep", n_tokens=1000, d_model=192, d_ff=128, n_experts=128, top_k=2,
+                       renormalize=False, dtype="bf16", **kw)
+    layer, x = mi.make_layer(cfg), mi.make_x(cfg)
     gpu = run_int4(cfg, layer, x)
     check_int4(cfg, layer, x, gpu, np.arange(cfg.n_tokens))

@@ -30,9 +30,21 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def staged_h(cfg, layer, x):
-    """route, permute and the routed grouped SwiGLU through the C ABI; returns the GPU's top-k,
-    grouping and h (fp64 values of the bf16 rows in grouped order)."""
+def _quantised(a, quant):
+    """Expert weights [G, R, C] quantised on the device: (codes, row scales)."""
+    w = to_device(np.ascontiguousarray(a), DEV)
+    rows, cols = w.numel() // w.shape[-1], w.shape[-1]
+    per = 2 if quant == "int4" else 1
+    codes = torch.empty(tuple(w.shape[:-1]) + (cols // per,), dtype=torch.uint8, device=DEV)
+    scales = torch.empty(w.shape[:-1], dtype=torch.float32, device=DEV)
+    (moe.moe_quantize_int4 if quant == "int4" else moe.moe_quantize_fp8)(rows, cols, w, codes, scales)
+    return codes, scales
+
+
+def staged_h(cfg, layer, x, quant=None):
+    """route, permute and the routed grouped SwiGLU through the C ABI (quant "fp8"/"int4": with the
+    expert weights quantised on the device); returns the GPU's top-k, grouping and h (fp64 values
+    of the bf16 rows in grouped order)."""
     shape = moe.shape_for(cfg)
     dv = lambda a: to_device(a, DEV)
     N, k, E, d, F = cfg.n_tokens, cfg.top_k, cfg.n_experts, cfg.d_model, cfg.d_ff
@@ -50,8 +62,13 @@ def staged_h(cfg, layer, x):
     moe.moe_permute(shape, idx, ps, counts, offs, perm, slot, None, ws)
     out = torch.empty(N * k, d, dtype=f32, device=DEV)
     hws = torch.full((N * k * F * 2 + (64 << 20),), 0xFF, dtype=torch.uint8, device=DEV)  # NaN-poisoned h
-    moe.moe_grouped_swiglu(shape, E, F, xd, perm, k, offs, N * k, dv(layer.w_gate), dv(layer.w_up),
-                           dv(layer.w_down), out, hws)
+    if quant is None:
+        moe.moe_grouped_swiglu(shape, E, F, xd, perm, k, offs, N * k, dv(layer.w_gate), dv(layer.w_up),
+                               dv(layer.w_down), out, hws)
+    else:
+        (qg, sg), (qu, su), (qd, sd) = (_quantised(a, quant) for a in (layer.w_gate, layer.w_up, layer.w_down))
+        fn = moe.moe_grouped_swiglu_int4 if quant == "int4" else moe.moe_grouped_swiglu_fp8
+        fn(shape, E, F, xd, perm, k, offs, N * k, qg, qu, qd, sg, su, sd, out, hws)
     torch.cuda.synchronize()
     offs_h = P.to_host(offs)
     rows = int(offs_h[-1])
@@ -59,18 +76,20 @@ def staged_h(cfg, layer, x):
     return P.to_host(idx), offs_h, P.to_host(perm)[:rows], mi.to_f64(hb)
 
 
-def check_h(cfg, layer, x, gpu_idx, offs, perm, h_gpu):
+def check_h(cfg, layer, x, gpu_idx, offs, perm, h_gpu, quant=None):
     """Every element of the GPU's h is a correct bf16 rounding: the oracle's own, or, only where
-    the band allows more than one, a value in [lo, hi]. Returns (elements, ambiguous, rounded
-    differently from the oracle)."""
+    the band allows more than one, a value in [lo, hi]. quant: the band of the layer on the
+    oracle's dequantised weights (row scales applied after the sums). Returns (elements,
+    ambiguous, rounded differently from the oracle)."""
     X = mi.to_f64(x)
     k = cfg.top_k
+    (vg, vu, _), _ = P.oracle_views(layer, quant=quant)
     n_amb = n_other = 0
     for e in range(cfg.n_experts):
         a, b = int(offs[e]), int(offs[e + 1])
         if a == b:
             continue
-        band = O.h_rounding_band(X[perm[a:b] // k], mi.to_f64(layer.w_gate[e]), mi.to_f64(layer.w_up[e]))
+        band = O.h_rounding_band(X[perm[a:b] // k], vg[e], vu[e], scaled=quant is not None)
         hg = h_gpu[a:b]
         ok = (hg == band.ref) | (band.amb & (band.lo <= hg) & (hg <= band.hi))
         assert np.all(ok), (f"expert {e}: {int((~ok).sum())} h elements are not a correct rounding; first at "
@@ -117,6 +136,18 @@ def test_h_elementwise_random_layers(kw):
     idx, offs, perm, h = staged_h(cfg, layer, x)
     n, amb, alt = check_h(cfg, layer, x, idx, offs, perm, h)
     log(f"{kw}: h elementwise ok: {n} elements, {amb} ambiguous, {alt} rounded the other way")
+
+
+@pytest.mark.parametrize("quant", ["fp8", "int4"])
+def test_h_elementwise_quantised_weights(quant):
+    # the FP8 and int4 codes widen to bf16 exactly, so h is the layer's on the dequantised weights
+    # up to fp32 rounding (and one more rounding for the row scale)
+    cfg = mi.small_config("hq", dtype="bf16", layer_id=795, x_id=795, n_tokens=300, n_experts=16, top_k=4,
+                          d_model=512, d_ff=256, select_bias=0.05)
+    layer, x = mi.make_layer(cfg), mi.make_x(cfg)
+    idx, offs, perm, h = staged_h(cfg, layer, x, quant)
+    n, amb, alt = check_h(cfg, layer, x, idx, offs, perm, h, quant)
+    log(f"{quant}: h elementwise ok: {n} elements, {amb} ambiguous, {alt} rounded the other way")
 
 
 def test_sweep_layer_n333_e128_k4_capacity6():

@@ -174,7 +174,13 @@ def test_int4_scale_over_eight_is_caught(monkeypatch):
 
 
 def test_int4_natural_nibble_order_is_caught(monkeypatch):
-    monkeypatch.setattr(O, "_INT4_NIBBLE", np.arange(8))
+    monkeypatch.setattr(O, "_INT4_SHIFT", 4 * np.arange(8))
+    _fails(pins.test_int4_packing_matches_worked_block_and_round_trips)
+
+
+def test_int4_offset_binary_field_is_caught(monkeypatch):
+    # codes stored as q + 8 instead of sign and magnitude
+    monkeypatch.setattr(O, "_int4_field", lambda q: np.asarray(q, dtype=np.int64) + 8)
     _fails(pins.test_int4_packing_matches_worked_block_and_round_trips)
 
 

@@ -594,10 +594,12 @@ def test_int4_packing_matches_worked_block_and_round_trips():
         want = [int(b, 16) for b in hexbytes.split()]
         np.testing.assert_array_equal(packed[0, int(off):int(off) + len(want)], want)
     rng = np.random.default_rng(42)
-    qq = rng.integers(-8, 8, (6, 192)).astype(np.int8)
+    qq = rng.integers(-7, 8, (6, 192)).astype(np.int8)   # the code range [-7, 7]
     np.testing.assert_array_equal(O.unpack_int4_rows(O.pack_int4_rows(qq), 192), qq)
-    # all-zero codes are bytes 0x88
-    assert np.all(O.pack_int4_rows(np.zeros((2, 64), np.int8)) == 0x88)
+    # all-zero codes are bytes 0x00; -7 and 7 differ only in the sign bit
+    assert np.all(O.pack_int4_rows(np.zeros((2, 64), np.int8)) == 0x00)
+    assert np.all(O.pack_int4_rows(np.full((1, 64), -7, np.int8)) == 0xFF)
+    assert np.all(O.pack_int4_rows(np.full((1, 64), 7, np.int8)) == 0x77)
 
 
 def test_int4_layer_is_dense_ffn_with_dequantised_weights():
