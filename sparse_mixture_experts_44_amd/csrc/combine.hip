@@ -7,8 +7,9 @@
 // shared-expert rows. They are added in a fixed order (slot 0 .. k-1, then
 // shared 0 .. S-1) and y is written once with 16-byte stores. The result is
 // bit-reproducible. A dropped copy (slot_pos -1) adds nothing, and a row with
-// nothing to add is exactly +0. The rows of one batch of slots are loaded
-// together before they are added, so the loads overlap.
+// nothing to add is exactly +0. The rows of one batch of slots, and the first
+// shared-expert row, are loaded together before they are added, so the loads
+// overlap; every row is read once, with non-temporal loads.
 #include "moe_common.h"
 
 namespace moe {
@@ -16,6 +17,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBatch = 8;  // slots loaded together
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_nt(const float4* p) {
+  const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restrict__ O,
                                                            const int32_t* __restrict__ slot_pos,
@@ -33,12 +41,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restr
   const int c = blockIdx.y * kThreads + threadIdx.x;
   if (c >= d4) return;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 sh0 = S > 0 ? load_nt(&shared[(size_t)t * d4 + c]) : a;
   for (int j0 = 0; j0 < k; j0 += kBatch) {
     float4 o[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int sp = j0 + u < k ? s_slot[j0 + u] : -1;
-      o[u] = sp >= 0 ? O[(size_t)sp * d4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      o[u] = sp >= 0 ? load_nt(&O[(size_t)sp * d4 + c]) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -51,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float4* __restr
     }
   }
   for (int s = 0; s < S; ++s) {
-    const float4 o = shared[((size_t)s * N + t) * d4 + c];
+    const float4 o = s == 0 ? sh0 : load_nt(&shared[((size_t)s * N + t) * d4 + c]);
     a.x += o.x;
     a.y += o.y;
     a.z += o.z;

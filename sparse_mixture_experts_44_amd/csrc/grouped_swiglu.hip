@@ -270,7 +270,12 @@ __device__ __forceinline__ TileGeom tile_geom(const GroupedParams& p, const Tabl
 // header with tail and S); an element-wise kernel adds the S parts in part
 // order into part 0, and a third kernel applies the epilogue to part 0.
 constexpr int kMaxSplit = 8;
-constexpr int kSplitHeader = 64;  // floats before the parts: [0] tail, [1] S (as int32)
+// Split workspace: a header ([0] tail tiles, [1] K-parts S, [2] first tail
+// tile, int32), then one geometry record per tail tile (the tail is shorter
+// than the grid, which is at most kSplitRecords workgroups), then the parts.
+constexpr int kSplitRecords = 512;
+constexpr int kSplitRecInts = 8;
+constexpr int kSplitHeader = 64 + kSplitRecords * kSplitRecInts;  // floats before the parts
 struct SplitPlan {
   int base, tail, S;
 };
@@ -282,7 +287,7 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int G, long long cap_
   sp.S = 1;
   // with four or more full rounds the idle part of the last one costs less
   // than writing and adding the parts
-  if (sp.tail > 0 && cap_floats > 0 && total < 4 * G) {
+  if (sp.tail > 0 && sp.tail <= kSplitRecords && cap_floats > 0 && total < 4 * G) {
     int S = min(kMaxSplit, G / sp.tail);
     while (S > 1 && (long long)sp.tail * S * tile_floats > cap_floats) --S;
     sp.S = max(S, 1);
@@ -463,7 +468,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
 
   const SplitPlan sp = split_plan(total, gridDim.x, p.split_cap - kSplitHeader, BM * BN);
   const int units = sp.base + sp.tail * sp.S;
-  if (p.split_ws && blockIdx.x == 0 && tid == 0) {  // for the part-sum kernel
+  if (p.split_ws && blockIdx.x == 0 && tid == 0) {  // for the finishing kernel
     reinterpret_cast<int*>(p.split_ws)[0] = sp.S > 1 ? sp.tail : 0;
     reinterpret_cast<int*>(p.split_ws)[1] = sp.S;
   }
@@ -685,7 +690,17 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
 
     // ---- epilogue
     if (part >= 0) {
-      // a K-part of a split tail tile: raw accumulators, thread-major, for the reduce kernel
+      // a K-part of a split tail tile: raw accumulators, thread-major, for the finishing
+      // kernel; part 0 also records the tile's geometry
+      if (part == 0 && tid == 0) {
+        int* rec = reinterpret_cast<int*>(p.split_ws) + 64 + (T - sp.base) * kSplitRecInts;
+        rec[0] = tg.si;
+        rec[1] = tg.g;
+        rec[2] = tg.start;
+        rec[3] = tg.m0;
+        rec[4] = tg.mvalid;
+        rec[5] = tg.n0;
+      }
       float* dst = p.split_ws + kSplitHeader + ((size_t)(T - sp.base) * sp.S + part) * (BM * BN);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -700,57 +715,62 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
   }
 }
 
-// Adds the K-parts of every split tail tile, element by element in part
-// order, into part 0 (grid-stride; the count comes from the header).
-template <int TILE>
-__global__ __launch_bounds__(256) void split_sum_kernel(float* __restrict__ ws) {
-  const int tail = reinterpret_cast<const int*>(ws)[0], S = reinterpret_cast<const int*>(ws)[1];
-  if (tail <= 0 || S <= 1) return;
-  float* parts = ws + kSplitHeader;
-  const size_t n = (size_t)tail * TILE;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
-    float* t0 = parts + (e / TILE) * S * TILE + e % TILE;
-    float a = t0[0];
-    for (int q = 1; q < S; ++q) a += t0[(size_t)q * TILE];
-    t0[0] = a;
-  }
-}
-
-// The epilogue of the split tail tiles of the launch before it (same
-// parameters, `main_grid` workgroups), from part 0: workgroup b finishes
-// tail tile b. Workgroups past the tail exit.
+// Finishes the split tail tiles of the launch before it (same parameters),
+// one wave per workgroup: workgroup b takes wave b % NW of tail tile b / NW,
+// adds that wave's accumulators over the S K-parts in part order and runs the
+// wave's share of the tile epilogue. The tail, S and each tail tile's
+// geometry come from the header and records the launch wrote; workgroups
+// past the tail exit at once.
 template <int BM, int BN, int WGM, int WGN, int WQ, bool P1, bool SAVE = false, bool OBF = false, bool ACC = false>
-__global__ __launch_bounds__(WGM * WGN * 64) void split_reduce_kernel(GroupedParams p, int main_grid) {
+__global__ __launch_bounds__(kWave) void split_finish_kernel(GroupedParams p) {
+  constexpr int NW = WGM * WGN;
   constexpr int TM = BM / WGM, FM = TM / 32;
   constexpr int BH = P1 ? BN / 2 : BN;
   constexpr int TN = BH / WGN, FN = TN / 32;
   constexpr int NB = P1 ? 2 * FN : FN;
-  constexpr int NT = WGM * WGN * kWave;
-  __shared__ TableLds tab;
-  __shared__ int scratch[NT];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WGN, wn = wave % WGN;
+  constexpr int NT = NW * kWave;  // threads of the GEMM workgroup that wrote the parts
+  const int* hdr = reinterpret_cast<const int*>(p.split_ws);
+  const int tail = hdr[0], S = hdr[1];
+  const int tt = blockIdx.x / NW, w = blockIdx.x % NW;
+  if (S <= 1 || tt >= tail) return;
+  const int lane = threadIdx.x;
+  const int wm = w / WGN, wn = w % WGN;
   const int d = p.d_model;
-  const int nt0 = ((P1 ? p.set[0].d_ff : d) + BH - 1) / BH;
-  const int nt1 = p.n_sets > 1 ? ((P1 ? p.set[1].d_ff : d) + BH - 1) / BH : 0;
-  const int G0 = p.set[0].n_groups;
-  const int nent = G0 + (p.n_sets > 1 ? p.set[1].n_groups : 0);
-  const int total = build_table<BM, NT>(p, nt0, nt1, tab, scratch);
-  const SplitPlan sp = split_plan(total, main_grid, p.split_cap - kSplitHeader, BM * BN);
-  if (sp.S <= 1 || (int)blockIdx.x >= sp.tail) return;  // whole workgroup: no barrier follows
-  const int T = sp.base + blockIdx.x;
-  const TileGeom tg = tile_geom<BM, BH>(p, tab, nent, G0, T);
-  const SetView S = pick(p, tg.si);
+  const int* rec = hdr + 64 + tt * kSplitRecInts;
+  TileGeom tg;
+  tg.si = rec[0];
+  tg.g = rec[1];
+  tg.start = rec[2];
+  tg.m0 = rec[3];
+  tg.mvalid = rec[4];
+  tg.n0 = rec[5];
+  const SetView Sv = pick(p, tg.si);
   f32x16_t acc[FM][NB];
-  const float* src = p.split_ws + kSplitHeader + (size_t)blockIdx.x * sp.S * (BM * BN) + tid;
+  const float* src = p.split_ws + kSplitHeader + (size_t)tt * S * (BM * BN) + w * kWave + lane;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = src[((size_t)(i * NB + j) * 16 + v) * NT];
-  store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF, ACC>(acc, S, tg, d, lane, wm, wn);
+  for (int q = 1; q < S; ++q) {
+    // the whole part is loaded before any of it is added, so that its loads are in flight together
+    const float* sq = src + (size_t)q * (BM * BN);
+    float t[FM][NB][16];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) t[i][j][v] = __builtin_nontemporal_load(&sq[((size_t)(i * NB + j) * 16 + v) * NT]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] += t[i][j][v];
+  }
+  store_tile<BM, BN, WGM, WGN, WQ, P1, SAVE, FM, NB, OBF, ACC>(acc, Sv, tg, d, lane, wm, wn);
 }
 
 // =====================================================================  fp32 SIMT
@@ -907,22 +927,19 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
                        dim3(WGM * WGN * 64), 0, st, p);
   }
   if (p.split_ws && p.split_cap > kSplitHeader) {
-    hipLaunchKernelGGL(split_sum_kernel<BM * BN>, dim3(1024), dim3(256), 0, st, p.split_ws);
+    // one wave per workgroup; the tail holds fewer tiles than the grid has workgroups
+    const dim3 fg(grid * WGM * WGN), fb(kWave);
     if (phase == 1 && save)
-      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, true, WQ == 0>), dim3(grid),
-                         dim3(WGM * WGN * 64), 0, st, p, grid);
+      hipLaunchKernelGGL((split_finish_kernel<BM, BN, WGM, WGN, WQ, true, WQ == 0>), fg, fb, 0, st, p);
     else if (phase == 1)
-      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, true>), dim3(grid), dim3(WGM * WGN * 64),
-                         0, st, p, grid);
+      hipLaunchKernelGGL((split_finish_kernel<BM, BN, WGM, WGN, WQ, true>), fg, fb, 0, st, p);
     else if (obf)
-      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false, false, WQ == 0>), dim3(grid),
-                         dim3(WGM * WGN * 64), 0, st, p, grid);
+      hipLaunchKernelGGL((split_finish_kernel<BM, BN, WGM, WGN, WQ, false, false, WQ == 0>), fg, fb, 0, st, p);
     else if (accum)
-      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false, false, false, WQ == 0>), dim3(grid),
-                         dim3(WGM * WGN * 64), 0, st, p, grid);
+      hipLaunchKernelGGL((split_finish_kernel<BM, BN, WGM, WGN, WQ, false, false, false, WQ == 0>), fg, fb, 0, st,
+                         p);
     else
-      hipLaunchKernelGGL((split_reduce_kernel<BM, BN, WGM, WGN, WQ, false>), dim3(grid), dim3(WGM * WGN * 64),
-                         0, st, p, grid);
+      hipLaunchKernelGGL((split_finish_kernel<BM, BN, WGM, WGN, WQ, false>), fg, fb, 0, st, p);
   }
 }
 
@@ -988,9 +1005,10 @@ void launch_class(const GroupedParams& p, int phase, hipStream_t stream) {
 
 size_t grouped_split_bytes(long long rows, int groups) {
   // the parts of one launch fill at most one tile per workgroup: G = CUs x workgroups per CU
+  // (the tallest large tile has 320 rows), after the header and the tail tile records
   const bool large = large_tiles(rows, groups);
   const size_t G = (size_t)num_cus() * (large ? 1 : 2);
-  return G * (large ? 256 * 256 : 64 * 256) * sizeof(float);
+  return (kSplitHeader + G * (large ? 320 * 256 : 64 * 256)) * sizeof(float);
 }
 
 int launch_grouped(const GroupedParams& p, int phase, hipStream_t stream) {

@@ -51,7 +51,7 @@ Layout layout(const moe_shape& s) {
   const size_t S = (size_t)s.n_shared;
   size_t off = 0;
   L.partials = off;
-  off += align256((size_t)route_blocks(s) * E * sizeof(double));
+  off += align256(route_partials_bytes(s));
   L.logits = off;
   off += align256(route_logits_floats(s) * sizeof(float));
   L.hist = off;

@@ -106,11 +106,12 @@ __device__ __forceinline__ void wait_vm_barrier_rt(int n) {
 }
 
 // ------------------------------------------------------------------ router
-// `partials`: route_blocks(s) x E doubles; `logits`: route_logits_floats(s) floats (workspace).
+// `partials`: route_partials_bytes(s) bytes; `logits`: route_logits_floats(s) floats (workspace).
 int launch_route(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                  const float* select_bias, int32_t* topk_idx, float* topk_w, double* prob_sum,
                  double* partials, float* logits, float* split_ws, size_t split_bytes, hipStream_t stream);
 int route_blocks(const moe_shape& s);
+size_t route_partials_bytes(const moe_shape& s);  // the partials region: route_blocks(s) x E doubles + a counter
 // Training-side statistics: z-loss (recomputes the logits), importance and its CV^2; any output may be NULL.
 int launch_router_aux(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                       const int32_t* topk_idx, const float* topk_w, double* z_loss, double* imp,

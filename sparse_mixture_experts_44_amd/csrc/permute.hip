@@ -103,6 +103,16 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(const int32_t*
   int e = in ? idx[c] : -1;
   if ((unsigned)e >= (unsigned)E) e = -1;  // past the end, or out of range: no expert
   s_e[tid] = e;
+  // the balance statistic's prob_sum terms, loaded now so that their latency
+  // overlaps the counting (wave 0 of workgroup 0; lane l holds experts l + 64 q)
+  constexpr int kPs = kMaxExperts / kWave;
+  double ps[kPs];
+  const bool do_stat = blockIdx.x == 0 && stat && wave == 0;
+#pragma unroll
+  for (int q = 0; q < kPs; ++q) {
+    const int x = lane + kWave * q;
+    ps[q] = (do_stat && x < E) ? prob_sum[x] : 0.0;
+  }
   for (int x = tid; x < E; x += kScatterThreads) {
     s_cnt[x] = single ? 0 : counts[x];
     s_run[x] = single ? 0 : base[(size_t)blockIdx.x * E + x];
@@ -137,13 +147,17 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(const int32_t*
       }
     }
     if (lane == kWave - 1) s_off[E] = incl;
-    if (blockIdx.x == 0 && stat) {
+    if (do_stat) {
       // E * sum_e (counts_e / (N k)) (prob_sum_e / N): lane-strided sums, then a fixed butterfly
       // (no copies: the statistic is defined as 0)
       const double nk = (double)N * (double)k, n = (double)N;
       double a = 0.0;
       if (N > 0)
-        for (int x = lane; x < E; x += kWave) a += ((double)s_cnt[x] / nk) * (prob_sum[x] / n);
+#pragma unroll
+        for (int q = 0; q < kPs; ++q) {
+          const int x = lane + kWave * q;
+          if (x < E) a += ((double)s_cnt[x] / nk) * (ps[q] / n);
+        }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
       if (lane == 0) *stat = (double)E * a;

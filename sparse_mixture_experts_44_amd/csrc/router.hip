@@ -27,13 +27,17 @@
 //      - Output: fp32 partial logits [split][N][E].
 //   2. select_kernel: one wavefront per token (select_token).
 //      - Sums the splits in split order, adds the logit bias, then softmax
-//        with butterfly reductions in a fixed order, the selection score, and
-//        k rounds of a wave arg-max. A larger score wins; on equal scores the
-//        lower expert index wins.
+//        with wave reductions in a fixed order (on the DPP lane network),
+//        the selection score, and k rounds of a wave arg-max. A larger
+//        score wins; on equal scores the lower expert index wins.
 //      - Renormalises the k weights.
 //      - Adds p into fp64 per-workgroup sums in a fixed order.
-//   3. prob_sum_kernel: one wavefront per expert adds the workgroup sums with
-//      a fixed tree, so prob_sum is bit-reproducible.
+//      - With at most 64 workgroups, the last one to finish (a counter that
+//        the logits kernel cleared) adds the workgroup sums into prob_sum,
+//        workgroup by workgroup in index order.
+//   3. prob_sum_kernel (more select workgroups, the fused form, or logits
+//      from the matrix cores): one wavefront per expert adds the workgroup
+//      sums with a fixed tree. Either way prob_sum is bit-reproducible.
 // The router z-loss and the backward pass recompute the logits alone; large
 // bf16 routers run that as one grouped GEMM on the matrix cores
 // (compute_logits).
@@ -67,16 +71,40 @@ __device__ __forceinline__ float mac(uint32_t a, uint32_t b, float c) {
 // chunks).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Wave reductions on the DPP lane network: two quad permutations, the
+// half-row mirror and the row mirror leave every lane of each 16-lane row
+// with the row's reduction (the two operands of every step are the same pair
+// in every lane of the row, so the rows agree bit for bit); the four row
+// values are then read into scalars and combined in a fixed order. Each DPP
+// step is a VALU operand modifier, with no LDS round trip as a cross-lane
+// shuffle takes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuad1032 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuad2301 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+__device__ __forceinline__ float rows_of(float v, int r) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp<kDppQuad1032>(v));
+  v = fmaxf(v, dpp<kDppQuad2301>(v));
+  v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppRowMirror>(v));
+  return fmaxf(fmaxf(rows_of(v, 0), rows_of(v, 1)), fmaxf(rows_of(v, 2), rows_of(v, 3)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp<kDppQuad1032>(v);
+  v += dpp<kDppQuad2301>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  return (rows_of(v, 0) + rows_of(v, 1)) + (rows_of(v, 2) + rows_of(v, 3));
 }
 
 // ---------------------------------------------------------------- 1. logits
@@ -87,7 +115,8 @@ template <bool BF16, int EG, int EPT, int TPT, int PD>
 __global__ __launch_bounds__(kThreads) void logits_kernel(const uint32_t* __restrict__ x,
                                                           const uint32_t* __restrict__ w, int N,
                                                           int dw, int E, int chunks_per_split,
-                                                          float* __restrict__ part) {
+                                                          float* __restrict__ part,
+                                                          unsigned int* __restrict__ clear) {
   constexpr int TG = kThreads / EG;
   constexpr int TT = TG * TPT;        // tokens per workgroup
   constexpr int EROWS = EG * EPT;     // expert rows covered
@@ -97,6 +126,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const uint32_t* __rest
   __shared__ uint32_t s_x[TT * kRow];
 
   const int tid = threadIdx.x;
+  if (clear && (blockIdx.x | blockIdx.y | blockIdx.z | tid) == 0) *clear = 0u;  // the select kernel's counter
   const int eg = tid % EG, tg = tid / EG;
   const int t0 = blockIdx.x * TT;
   const int split = blockIdx.y;
@@ -225,35 +255,38 @@ __device__ __forceinline__ void select_token(float (&v)[EL], const float (&sb)[E
     pacc[m] += (double)p[m];
     s[m] = p[m] + sb[m];
   }
-  uint32_t taken = 0;
+  // k rounds. Each takes the largest remaining score (a wave max), then the
+  // lowest expert index that holds it: expert e = lane + 64 m, so that is the
+  // lowest lane of the first m whose ballot is not empty. Its p is read from
+  // the owner lane, which then drops the expert from its candidates.
+  uint32_t avail = 0;  // bit m: expert lane + 64 m is still a candidate
+#pragma unroll
+  for (int m = 0; m < EL; ++m)
+    if (lane + kWave * m < E) avail |= 1u << m;
   float sel_sum = 0.f, mine_p = 0.f;
   int mine_idx = -1;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY, bp = 0.f;
-    int bi = 0x7fffffff;
+    float lm = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < EL; ++m)
+      if ((avail >> m) & 1u) lm = fmaxf(lm, s[m]);
+    const float top = wave_max(lm);
+    int bm = -1, bl = 0;
 #pragma unroll
     for (int m = 0; m < EL; ++m) {
-      const int e = lane + kWave * m;
-      if (e < E && !((taken >> m) & 1u) && (s[m] > bv || (s[m] == bv && e < bi))) {
-        bv = s[m];
-        bi = e;
-        bp = p[m];
+      const unsigned long long b = __ballot(((avail >> m) & 1u) && s[m] == top);
+      if (bm < 0 && b != 0ull) {
+        bm = m;
+        bl = __builtin_ctzll(b);
       }
     }
+    float bp = 0.f;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      const float op = __shfl_xor(bp, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-        bp = op;
-      }
-    }
-    if (bi < E && (bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+    for (int m = 0; m < EL; ++m)
+      if (m == bm) bp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[m]), bl));
+    if (bm >= 0 && lane == bl) avail &= ~(1u << bm);
     if (lane == j) {
-      mine_idx = bi < E ? bi : -1;
+      mine_idx = bm >= 0 ? kWave * bm + bl : -1;
       mine_p = bp;
     }
     sel_sum += bp;
@@ -264,12 +297,35 @@ __device__ __forceinline__ void select_token(float (&v)[EL], const float (&sb)[E
   }
 }
 
+// prob_sum[e] for e = threadIdx.x + kThreads * i, by the select kernel's last
+// workgroup when there are at most kFoldBlocks workgroup sums: added in
+// workgroup order, their loads issued in batches of 16 so that they overlap.
+constexpr int kFoldBlocks = 64;
+
+__device__ __forceinline__ void add_prob_sums(const double* __restrict__ partials, int nb, int E,
+                                              double* __restrict__ prob_sum) {
+  for (int e = (int)threadIdx.x; e < E; e += kThreads) {
+    double a = 0.0;
+    for (int b0 = 0; b0 < nb; b0 += 16) {
+      double v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = b0 + u < nb ? partials[(size_t)(b0 + u) * E + e] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (b0 + u < nb) a += v[u];
+    }
+    prob_sum[e] = a;
+  }
+}
+
 template <int EL>  // experts per lane: E <= 64 * EL
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const float* __restrict__ part, int splits, const float* __restrict__ logit_bias,
     const float* __restrict__ select_bias, int N, int E, int k, int renorm, int tpb,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, double* __restrict__ partials) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, double* __restrict__ partials,
+    unsigned int* __restrict__ done, double* __restrict__ prob_sum) {
   __shared__ double s_part[kThreads / kWave][64 * EL];
+  __shared__ unsigned int s_ticket;
   const int tid = threadIdx.x;
   const int wv = tid >> 6, lane = tid & 63;
   const int t0 = blockIdx.x * tpb;
@@ -319,6 +375,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     for (int q = 1; q < kThreads / kWave; ++q) a += s_part[q][e];
     partials[(size_t)blockIdx.x * E + e] = a;
   }
+  if (!done) return;  // prob_sum_kernel follows
+  // the last workgroup to get here adds every workgroup's sums: release this
+  // workgroup's sums before taking a ticket, acquire the others' after
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_ticket = atomicAdd(done, 1u);
+  __syncthreads();
+  if (s_ticket != gridDim.x - 1) return;
+  __threadfence();
+  add_prob_sums(partials, gridDim.x, E, prob_sum);
+  if (tid == 0) *done = 0u;
 }
 
 // ---------------------------------------------------------------- 2b. fused router (bf16, prefill)
@@ -615,27 +682,29 @@ LogitsPlan plan_logits(const moe_shape& s) {
 
 template <bool BF16, int EG, int EPT, int TPT>
 void launch_logits_t(const moe_shape& s, const LogitsPlan& L, const void* x, const void* w,
-                     float* part, hipStream_t st) {
+                     float* part, unsigned int* clear, hipStream_t st) {
   const int dw = BF16 ? s.d_model / 2 : s.d_model;
-  constexpr int PD = TPT == 1 ? 4 : 1;  // one output per thread: registers to spare for prefetch
+  // one output per thread: registers to spare for a deep prefetch ring (a split of up to 16
+  // chunks then has every load in flight at once)
+  constexpr int PD = TPT == 1 ? 16 : 1;
   hipLaunchKernelGGL((logits_kernel<BF16, EG, EPT, TPT, PD>), dim3(L.tiles, L.splits, L.etiles), dim3(kThreads), 0, st,
                      static_cast<const uint32_t*>(x), static_cast<const uint32_t*>(w), s.n_tokens, dw,
-                     s.n_experts, L.chunks_per_split, part);
+                     s.n_experts, L.chunks_per_split, part, clear);
 }
 
 template <bool BF16>
 void launch_logits(const moe_shape& s, const LogitsPlan& L, const void* x, const void* w, float* part,
-                   hipStream_t st) {
+                   unsigned int* clear, hipStream_t st) {
   if (L.tpt == 1) {
-    if (L.eg == 8) launch_logits_t<BF16, 8, 1, 1>(s, L, x, w, part, st);
-    else launch_logits_t<BF16, 32, 1, 1>(s, L, x, w, part, st);
-  } else if (L.eg == 8) launch_logits_t<BF16, 8, 1, 4>(s, L, x, w, part, st);
-  else if (L.ept == 1) launch_logits_t<BF16, 32, 1, 4>(s, L, x, w, part, st);
-  else if (L.ept == 2) launch_logits_t<BF16, 32, 2, 4>(s, L, x, w, part, st);
-  else if (L.ept == 4 && L.tpt == 8) launch_logits_t<BF16, 32, 4, 8>(s, L, x, w, part, st);
-  else if (L.ept == 4) launch_logits_t<BF16, 32, 4, 4>(s, L, x, w, part, st);
-  else if (L.ept == 8) launch_logits_t<BF16, 32, 8, 4>(s, L, x, w, part, st);
-  else launch_logits_t<BF16, 32, 16, 2>(s, L, x, w, part, st);
+    if (L.eg == 8) launch_logits_t<BF16, 8, 1, 1>(s, L, x, w, part, clear, st);
+    else launch_logits_t<BF16, 32, 1, 1>(s, L, x, w, part, clear, st);
+  } else if (L.eg == 8) launch_logits_t<BF16, 8, 1, 4>(s, L, x, w, part, clear, st);
+  else if (L.ept == 1) launch_logits_t<BF16, 32, 1, 4>(s, L, x, w, part, clear, st);
+  else if (L.ept == 2) launch_logits_t<BF16, 32, 2, 4>(s, L, x, w, part, clear, st);
+  else if (L.ept == 4 && L.tpt == 8) launch_logits_t<BF16, 32, 4, 8>(s, L, x, w, part, clear, st);
+  else if (L.ept == 4) launch_logits_t<BF16, 32, 4, 4>(s, L, x, w, part, clear, st);
+  else if (L.ept == 8) launch_logits_t<BF16, 32, 8, 4>(s, L, x, w, part, clear, st);
+  else launch_logits_t<BF16, 32, 16, 2>(s, L, x, w, part, clear, st);
 }
 
 }  // namespace
@@ -650,6 +719,14 @@ int route_blocks(const moe_shape& s) {
   return (s.n_tokens + tpb - 1) / tpb;
 }
 
+size_t route_partials_bytes(const moe_shape& s) {
+  return (size_t)route_blocks(s) * s.n_experts * sizeof(double) + 64;  // the sums, then the select counter
+}
+
+unsigned int* route_counter(const moe_shape& s, double* partials) {
+  return reinterpret_cast<unsigned int*>(partials + (size_t)route_blocks(s) * s.n_experts);
+}
+
 // Large bf16 routers go to the matrix cores: logits = x W_r^T is then one grouped
 // GEMM (one segment of N rows, K = d, W_r as the [E, d] weight), fp32 sums of exact
 // bf16 products as on the VALU path, in another order.
@@ -657,8 +734,10 @@ bool logits_by_mfma(const moe_shape& s) {
   return s.dtype == MOE_DTYPE_BF16 && s.n_experts >= 64 && s.n_tokens >= 256;
 }
 
+// clear: a counter for the select kernel, zeroed by the VALU logits kernel
+// (nothing is written to it when the logits run on the matrix cores).
 int compute_logits(const moe_shape& s, const void* x, const void* w_router, float* logits, float* split_ws,
-                   size_t split_bytes, int* splits, hipStream_t st) {
+                   size_t split_bytes, int* splits, hipStream_t st, unsigned int* clear = nullptr) {
   if (logits_by_mfma(s)) {
     GroupedParams p{};
     p.n_sets = 1;
@@ -681,8 +760,8 @@ int compute_logits(const moe_shape& s, const void* x, const void* w_router, floa
     return launch_grouped(p, 2, st);
   }
   const LogitsPlan L = plan_logits(s);
-  if (s.dtype == MOE_DTYPE_BF16) launch_logits<true>(s, L, x, w_router, logits, st);
-  else launch_logits<false>(s, L, x, w_router, logits, st);
+  if (s.dtype == MOE_DTYPE_BF16) launch_logits<true>(s, L, x, w_router, logits, clear, st);
+  else launch_logits<false>(s, L, x, w_router, logits, clear, st);
   *splits = L.splits;
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -725,21 +804,25 @@ int launch_route(const moe_shape& s, const void* x, const void* w_router, const 
                        s.n_experts, prob_sum);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
-  int splits = 1;
-  if (const int st = compute_logits(s, x, w_router, logits, split_ws, split_bytes, &splits, stream)) return st;
   const int nb = route_blocks(s);
+  // the select kernel's counter sits after the workgroup sums; the VALU logits
+  // kernel clears it, and then the last select workgroup adds the sums
+  unsigned int* done = logits_by_mfma(s) || nb > kFoldBlocks ? nullptr : route_counter(s, partials);
+  int splits = 1;
+  if (const int st = compute_logits(s, x, w_router, logits, split_ws, split_bytes, &splits, stream, done)) return st;
   const int el = (s.n_experts + kWave - 1) / kWave;
 #define MOE_SELECT(EL_)                                                                          \
   hipLaunchKernelGGL(select_kernel<EL_>, dim3(nb), dim3(kThreads), 0, stream, logits, splits, \
                      logit_bias, select_bias, s.n_tokens, s.n_experts, s.top_k, s.renormalize,   \
-                     select_tpb(s), topk_idx, topk_w, partials)
+                     select_tpb(s), topk_idx, topk_w, partials, done, prob_sum)
   if (el <= 1) MOE_SELECT(1);
   else if (el <= 2) MOE_SELECT(2);
   else if (el <= 4) MOE_SELECT(4);
   else MOE_SELECT(8);
 #undef MOE_SELECT
-  hipLaunchKernelGGL(prob_sum_kernel, dim3((s.n_experts + 3) / 4), dim3(kThreads), 0, stream,
-                     partials, nb, s.n_experts, prob_sum);
+  if (!done)
+    hipLaunchKernelGGL(prob_sum_kernel, dim3((s.n_experts + 3) / 4), dim3(kThreads), 0, stream, partials, nb,
+                       s.n_experts, prob_sum);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
