@@ -469,6 +469,15 @@ __global__ void fill_f32_kernel(float* p, size_t n, float v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+// Workgroup (b, g): slice b of group g's output block, when K_g = 0.
+__global__ void zero_empty_groups_kernel(uint4* out, const int32_t* __restrict__ kofs, size_t n16) {
+  const int g = blockIdx.y;
+  if (kofs[g + 1] != kofs[g]) return;
+  uint4* p = out + (size_t)g * n16;
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x) p[i] = z;
+}
+
 }  // namespace
 
 int launch_gather_rows(const void* x, const float* dy, const float* topk_w, const int32_t* perm,
@@ -572,6 +581,15 @@ int launch_split_hilo(const float* dl, int N, int E, void* dlh, void* dlT, hipSt
   if (N <= 0 || E <= 0) return MOE_OK;
   hipLaunchKernelGGL(split_hilo_kernel, dim3((E + 63) / 64, (N + 63) / 64), dim3(kT), 0, st, dl, N, E,
                      static_cast<bf16_t*>(dlh), static_cast<bf16_t*>(dlT));
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int launch_zero_empty_groups(void* out, const int32_t* kofs, int G, size_t block_bytes, hipStream_t st) {
+  if (G <= 0 || block_bytes == 0) return MOE_OK;
+  if (block_bytes % 16) return MOE_ERR_UNSUPPORTED;
+  const size_t n16 = block_bytes / 16;
+  const int nb = (int)std::min<size_t>(64, (n16 + kT - 1) / kT);
+  hipLaunchKernelGGL(zero_empty_groups_kernel, dim3(nb, G), dim3(kT), 0, st, static_cast<uint4*>(out), kofs, n16);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

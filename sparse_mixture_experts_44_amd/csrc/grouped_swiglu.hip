@@ -92,6 +92,7 @@ __device__ __forceinline__ void seg_bounds(const SegSet& S, int g, int& start, i
   }
   a = max(0, min(a, S.max_rows));
   b = max(a, min(b, S.max_rows));
+  if (S.k_offsets && S.skip_empty_k && S.k_offsets[g + 1] == S.k_offsets[g]) b = a;  // K_g = 0: no tiles
   start = a;
   rows = b - a;
 }

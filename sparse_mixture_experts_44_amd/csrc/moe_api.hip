@@ -219,7 +219,7 @@ BwLayout bw_layout(const moe_shape& s) {
 // out[g*M + m, n] = sum over group g's K range of A[m, k] B[n, k].
 int grouped_gemm(int n_groups, const int32_t* offsets, int uniform, long long max_rows, int K_or_stride, int ncols,
                  const void* A, const void* B, float* out, const int32_t* kofs, float* split_ws, size_t split_bytes,
-                 hipStream_t st, int accumulate = 0, int out_bf16 = 0) {
+                 hipStream_t st, int accumulate = 0, int out_bf16 = 0, int skip_empty_k = 0) {
   GroupedParams p{};
   p.n_sets = 1;
   p.x = A;
@@ -239,6 +239,7 @@ int grouped_gemm(int n_groups, const int32_t* offsets, int uniform, long long ma
   S.h = const_cast<void*>(A);
   S.out = out;
   S.k_offsets = kofs;
+  S.skip_empty_k = skip_empty_k;
   S.accumulate = accumulate;
   S.out_bf16 = out_bf16;
   return launch_grouped(p, 2, st);
@@ -683,12 +684,20 @@ int moe_backward(const moe_shape* shape, const void* x, const void* w_router, co
   MOE_TRY(launch_transpose_padded(P(L.dGU), 2 * F, 0, F, offsets, 0, 0, Pi(L.kofs), E, P(L.dGT), Kmax, stream));
   MOE_TRY(launch_transpose_padded(P(L.dGU), 2 * F, F, F, offsets, 0, 0, Pi(L.kofs), E, P(L.dUT), Kmax, stream));
   MOE_TRY(launch_transpose_padded(P(L.Xg), d, 0, d, offsets, 0, 0, Pi(L.kofs), E, P(L.XT), Kmax, stream));
+  // experts with no kept copy get no GEMM tiles: their gradient blocks are zeroed by a fill
+  // (or, when accumulating, left as they are)
+  if (!accumulate) {
+    const size_t blk = (size_t)d * F * (wbf16 ? 2 : 4);
+    MOE_TRY(launch_zero_empty_groups(dw_down, Pi(L.kofs), E, blk, stream));
+    MOE_TRY(launch_zero_empty_groups(dw_gate, Pi(L.kofs), E, blk, stream));
+    MOE_TRY(launch_zero_empty_groups(dw_up, Pi(L.kofs), E, blk, stream));
+  }
   MOE_TRY(grouped_gemm(E, nullptr, d, (long long)E * d, Kmax, F, P(L.dOT), P(L.hT), dw_down, Pi(L.kofs), split,
-                       split_bytes, stream, accumulate, wbf16));
+                       split_bytes, stream, accumulate, wbf16, 1));
   MOE_TRY(grouped_gemm(E, nullptr, F, (long long)E * F, Kmax, d, P(L.dGT), P(L.XT), dw_gate, Pi(L.kofs), split,
-                       split_bytes, stream, accumulate, wbf16));
+                       split_bytes, stream, accumulate, wbf16, 1));
   MOE_TRY(grouped_gemm(E, nullptr, F, (long long)E * F, Kmax, d, P(L.dUT), P(L.XT), dw_up, Pi(L.kofs), split,
-                       split_bytes, stream, accumulate, wbf16));
+                       split_bytes, stream, accumulate, wbf16, 1));
   // ---- shared experts: every token, weight 1
   if (S > 0) {
     const int RS = S * N, KS = (int)L.KSmax;

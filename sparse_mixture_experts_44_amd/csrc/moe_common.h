@@ -158,6 +158,9 @@ struct SegSet {
   // h + M * k_offsets[g] holds [M, K_g] and w_down + d_model * k_offsets[g]
   // holds [d_model, K_g], each row-major: out[g*M + m, n] = sum_k h_g[m, k] * w_g[n, k].
   const int32_t* k_offsets;
+  // With k_offsets: groups with K_g = 0 get no tiles, and their output is left
+  // as it is (the caller zeroes it, or leaves it when accumulating).
+  int32_t skip_empty_k;
   // N-major weights (phase 2 only, bf16, not with k_offsets): when b_nmajor is
   // set, group g's operand is read as K rows of d_model values each (the
   // weight in its stored orientation: out[r, n] = sum_k h[r, k] * B_g[k, n]).
@@ -232,6 +235,9 @@ int launch_split_hilo(const float* dl, int N, int E, void* dlh, void* dlT, hipSt
 // d_logit_bias[e] = sum_t dl[t][e] (added to d_logit_bias when accumulating)
 int launch_logit_bias_grad(const float* dl, int N, int E, float* dlb, int accumulate, hipStream_t st);
 int launch_fill_f32(float* p, size_t n, float v, hipStream_t st);
+// Zeroes block g (block_bytes at out + g * block_bytes, a multiple of 16) of every group g < G
+// with K_g = kofs[g + 1] - kofs[g] = 0.
+int launch_zero_empty_groups(void* out, const int32_t* kofs, int G, size_t block_bytes, hipStream_t st);
 
 // ------------------------------------------------------------------ combine
 int launch_combine(const moe_shape& s, const float* expert_out, const int32_t* slot_pos,

@@ -21,8 +21,9 @@
 //                 offsets = exclusive scan of kept in LDS. Workgroup 0 also
 //                 writes offsets and the balance statistic.
 //               - A copy's rank within its expert = the chunk base + the
-//                 earlier copies of the chunk with that expert, which each
-//                 thread counts by scanning the chunk's experts in LDS.
+//                 earlier copies of the chunk with that expert: those of
+//                 earlier waves from per-wave histograms in LDS, those of its
+//                 own wave by a scan of the wave's experts.
 //               - Rank < C keeps the copy at offsets[e] + rank.
 // Every output is a pure function of topk_idx: there are no races and no
 // order-dependent atomics.
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(256) void colscan_kernel(const int32_t* __restrict_
 // counts (the chunk's histogram is the expert counts, and every base is 0),
 // in place of hist_kernel and colscan_kernel.
 constexpr int kScatterThreads = kChunk;
+constexpr int kScatterWaves = kScatterThreads / kWave;
 
 __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(const int32_t* __restrict__ idx, int NK,
                                                                   int E, int C, int N, int k,
@@ -94,6 +96,7 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(const int32_t*
   __shared__ int32_t s_cnt[kMaxExperts];
   __shared__ int32_t s_off[kMaxExperts + 1];
   __shared__ __attribute__((aligned(16))) int32_t s_e[kChunk];
+  __shared__ int32_t s_wh[kScatterWaves][kMaxExperts];  // per-wave expert histograms of the chunk
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const bool single = base == nullptr;
@@ -117,12 +120,15 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(const int32_t*
     s_cnt[x] = single ? 0 : counts[x];
     s_run[x] = single ? 0 : base[(size_t)blockIdx.x * E + x];
   }
+  for (int x = tid; x < kScatterWaves * E; x += kScatterThreads) s_wh[x / E][x % E] = 0;
   __syncthreads();
-  if (single) {
-    if (e >= 0) atomicAdd(&s_cnt[e], 1);  // the order of the additions does not matter
-    __syncthreads();
-    for (int x = tid; x < E; x += kScatterThreads) counts[x] = s_cnt[x];
+  if (e >= 0) {  // the order of the additions does not matter
+    atomicAdd(&s_wh[wave][e], 1);
+    if (single) atomicAdd(&s_cnt[e], 1);
   }
+  __syncthreads();
+  if (single)
+    for (int x = tid; x < E; x += kScatterThreads) counts[x] = s_cnt[x];
   // offsets = exclusive scan of kept = min(counts, C): wave 0, lane l owning experts [l*per, (l+1)*per)
   if (wave == 0) {
     const int per = (E + kWave - 1) / kWave;
@@ -171,11 +177,13 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(const int32_t*
     slot_pos[c] = -1;
     return;
   }
-  // rank within the expert: the chunk's base plus the earlier copies of this
-  // chunk with the same expert (a scan of the chunk's experts in LDS)
+  // rank within the expert: the chunk's base, plus the copies of earlier waves
+  // with the same expert (their histograms), plus the earlier copies of this
+  // wave with the same expert (a scan of at most 63 entries in LDS)
   int rank = s_run[e];
+  for (int w = 0; w < wave; ++w) rank += s_wh[w][e];
   const int full = tid & ~3;
-  for (int j = 0; j < full; j += 4) {
+  for (int j = wave * kWave; j < full; j += 4) {
     const int4 v = *reinterpret_cast<const int4*>(&s_e[j]);
     rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
   }

@@ -11,6 +11,7 @@ Small seeded layers, compared with the CPU oracle. Covered:
   and fp32;
 * bitwise determinism across two runs;
 * a large router (N = 2048, E = 256, d = 1024) whose logits GEMM splits its K loops;
+* a top-1 layer of 4099 tokens (the combine's four-token workgroups, the last one partial);
 * a seeded random sweep of 16 small layers, every knob drawn at once (bf16 and fp32).
 * the staged entry points against moe_forward.
 """
@@ -56,6 +57,10 @@ CASES = {
     # short segments in one launch of 256-row tiles), and a shared expert
     "large_and_small": small("large_and_small", n_tokens=2048, n_experts=32, top_k=4, d_model=256, d_ff=256,
                              n_shared=1, d_ff_shared=128, select_bias=0.1),
+    # a top-1 layer with 4099 tokens: the combine takes four tokens per workgroup, the last one ragged,
+    # and a capacity drops copies
+    "top1_many": small("top1_many", n_tokens=4099, n_experts=16, top_k=1, d_model=128, d_ff=64,
+                       capacity=300, logit_skew=1.0),
 }
 
 
