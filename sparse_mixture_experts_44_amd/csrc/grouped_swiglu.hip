@@ -256,10 +256,19 @@ __device__ __forceinline__ TileGeom tile_geom(const GroupedParams& p, const Tabl
     mtile = full_bands * kBandM + (in - ntile * rem);
   }
   // A segment of `rows` rows takes mt = ceil(rows / BM) m-tiles: either BM
-  // rows each and a short last one, or (balance_m) an even split, so that
-  // the tiles sharing a weight tile take the same time.
-  t.m0 = p.balance_m ? (int)((long long)mtile * rows / mt) : mtile * BM;
-  t.mvalid = p.balance_m ? (int)((long long)(mtile + 1) * rows / mt) - t.m0 : min(BM, rows - t.m0);
+  // rows each and a short last one, or (balance_m) an even split of its
+  // 32-row MFMA blocks, so that the tiles sharing a weight tile take the same
+  // time and only the segment's last block holds empty rows (an even split
+  // of the rows themselves leaves a partial block in every tile).
+  if (p.balance_m) {
+    const int nb = (rows + 31) / 32;  // mt <= nb, and no tile gets more than BM / 32 blocks
+    const int b0 = (int)((long long)mtile * nb / mt), b1 = (int)((long long)(mtile + 1) * nb / mt);
+    t.m0 = 32 * b0;
+    t.mvalid = min(32 * b1, rows) - t.m0;
+  } else {
+    t.m0 = mtile * BM;
+    t.mvalid = min(BM, rows - t.m0);
+  }
   t.n0 = ntile * BH;
   return t;
 }
@@ -267,13 +276,13 @@ __device__ __forceinline__ TileGeom tile_geom(const GroupedParams& p, const Tabl
 // Tail split. With G workgroups, tiles [base, total) form a last, partial
 // round. When workspace is given, each of those `tail` tiles is split along
 // K into S parts (S <= G / tail), so the last round keeps every CU busy.
-// Each part writes its fp32 accumulators to the workspace (after a small
-// header with tail and S); an element-wise kernel adds the S parts in part
-// order into part 0, and a third kernel applies the epilogue to part 0.
+// Each part writes its fp32 accumulators to the workspace, and the launch
+// after it (split_finish_kernel) adds the S parts in part order and applies
+// the epilogue.
 constexpr int kMaxSplit = 8;
-// Split workspace: a header ([0] tail tiles, [1] K-parts S, [2] first tail
-// tile, int32), then one geometry record per tail tile (the tail is shorter
-// than the grid, which is at most kSplitRecords workgroups), then the parts.
+// Split workspace: a header ([0] tail tiles, [1] K-parts S, int32), then one
+// geometry record per tail tile (the tail is shorter than the grid, which is
+// at most kSplitRecords workgroups), then the parts.
 constexpr int kSplitRecords = 512;
 constexpr int kSplitRecInts = 8;
 constexpr int kSplitHeader = 64 + kSplitRecords * kSplitRecInts;  // floats before the parts
