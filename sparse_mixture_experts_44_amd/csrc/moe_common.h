@@ -58,9 +58,12 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 //   PPR = 4 (64-byte rows):  g(r) = ((r >> 1) & 3) ^ ((r >> 3) & 1)
 //   PPR = 2 (32-byte rows of int4 weights, read 16 bytes per lane per step):
 //                            g(r) = ((r >> 2) ^ (r >> 3)) & 1
+//   PPR = 16, 32 (256- and 512-byte rows, which all start on bank 0):
+//                            g(r) = r & 15 (16 rows on 16 distinct 16-byte bank groups)
 template <int PPR>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (PPR == 8) return (row & 7) ^ ((row >> 3) & 1);
+  if constexpr (PPR >= 16) return row & 15;
+  else if constexpr (PPR == 8) return (row & 7) ^ ((row >> 3) & 1);
   else if constexpr (PPR == 4) return ((row >> 1) & 3) ^ ((row >> 3) & 1);
   else return ((row >> 2) ^ (row >> 3)) & 1;
 }

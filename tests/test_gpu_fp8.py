@@ -112,12 +112,13 @@ def test_fp8_small_layers_every_row(kw):
     check_fp8(cfg, layer, x, gpu, np.arange(cfg.n_tokens))
 
 
+@pytest.mark.parametrize("d", [128, 192])   # d = 192: gate|up on 64-K stages; 128: on 128-K stages
 @pytest.mark.parametrize("sizes", [
     [0, 1, 255, 256, 257, 0, 513, 2, 300],   # 256-row tiles
     [0, 1, 63, 64, 65, 0, 3, 127, 0, 0],     # 64-row tiles
 ])
-def test_fp8_grouped_segment_edges(sizes):
-    d, F, rpt = 128, 256, 3
+def test_fp8_grouped_segment_edges(sizes, d):
+    F, rpt = 256, 3
     rng = np.random.default_rng(len(sizes) * 7 + d)
     G = len(sizes)
     offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)

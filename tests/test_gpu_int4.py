@@ -114,13 +114,15 @@ def test_int4_small_layers_every_row(kw):
     check_int4(cfg, layer, x, gpu, np.arange(cfg.n_tokens))
 
 
+@pytest.mark.parametrize("d", [128, 512])             # d = 512: gate|up on 32-row tiles with 256-K stages
 @pytest.mark.parametrize("extra_ws", [0, 64 << 20])   # with room past h, the tail tiles split along K
 @pytest.mark.parametrize("sizes", [
     [0, 1, 255, 256, 257, 0, 513, 2, 300],
     [0, 1, 63, 64, 65, 0, 3, 127, 0, 0],
+    [0, 31, 32, 33, 0, 95, 1],
 ])
-def test_int4_grouped_segment_edges(sizes, extra_ws):
-    d, F, rpt = 128, 256, 3
+def test_int4_grouped_segment_edges(sizes, extra_ws, d):
+    F, rpt = 256, 3
     rng = np.random.default_rng(len(sizes) * 11 + d)
     G = len(sizes)
     offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
