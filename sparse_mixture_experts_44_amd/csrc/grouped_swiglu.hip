@@ -592,9 +592,20 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     const int a_act = min(A_INS, max(0, (mvalid + RPIA - 1) / RPIA - wave * A_INS));
     const int lw = a_act + B_INS;
 
+    // Down projections on the small classes walk K from one start per XCD (the
+    // XCD's workgroups together, 1/8 of K apart between XCDs): their weight rows
+    // are d_ff apart, and in step on every XCD they load the same row offsets at
+    // once (DeepSeek-shaped decode down 0.205 -> 0.195 ms). Gate|up keeps the
+    // natural K order, in which the rounding of h to bf16 is checked, and so do
+    // the balanced large tiles, whose m-tiles share operand panels in L2.
+    const int rot = (!P1 && !NMAJ && !S.kofs && !p.balance_m) ? (int)(blockIdx.x % kXcds) * nk / kXcds : 0;
+    auto kstep = [&](int kt) {
+      const int kk = kt + rot;
+      return kk >= nk ? kk - nk : kk;
+    };
     auto issue = [&](int kt) {
       const int st = kt % NS;
-      const int ko = (k_lo + kt) * BK;
+      const int ko = (k_lo + kstep(kt)) * BK;
 #pragma unroll
       for (int i = 0; i < A_INS; ++i)
         if (i < a_act) dma16(a_base + a_off[i] + ko, a_lds0 + st * STAGE + i * 1024);
@@ -605,7 +616,7 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
     // copies [c0, c1) of stage kt, in the order A (active ones) then B
     auto issue_part = [&](int kt, int c0, int c1) {
       const int st = kt % NS;
-      const int ko = (k_lo + kt) * BK;
+      const int ko = (k_lo + kstep(kt)) * BK;
 #pragma unroll
       for (int c = 0; c < L; ++c) {
         if (c < c0 || c >= c1) continue;
