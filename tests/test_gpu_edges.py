@@ -106,6 +106,20 @@ def test_deterministic_bitwise():
         np.testing.assert_array_equal(a[k].view(np.uint8), b[k].view(np.uint8), err_msg=k)
 
 
+def test_deterministic_bitwise_small_batch():
+    """A decode-sized batch: the last select workgroup adds the probability sums (its counter
+    cleared by the logits launch each call), and the gate|up tail tiles split along K. Three
+    calls in a row give the same bits."""
+    cfg = small("det_small", n_tokens=64, n_experts=64, top_k=6, d_model=512, d_ff=256, n_shared=1,
+                d_ff_shared=128, select_bias=0.05)
+    layer, x = mi.make_layer(cfg), mi.make_x(cfg)
+    runs = [run_gpu(cfg, layer, x) for _ in range(3)]
+    for r in runs[1:]:
+        for k in runs[0]:
+            np.testing.assert_array_equal(runs[0][k].view(np.uint8), r[k].view(np.uint8), err_msg=k)
+    check_all(cfg, layer, x, runs[0])
+
+
 def _grouped_case(sizes, d, F, dtype, identity=False):
     rng = np.random.default_rng(len(sizes) * 7 + d)
     G = len(sizes)
