@@ -80,24 +80,27 @@ int zero_f64(double* p, int n, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// defer_nb: see launch_route (the forward hands the last step to the permutation)
 int do_route(const moe_shape& s, const void* x, const void* w_router, const float* lb, const float* sb,
-             int32_t* idx, float* tw, double* prob_sum, void* ws, hipStream_t st) {
+             int32_t* idx, float* tw, double* prob_sum, void* ws, hipStream_t st, int* defer_nb = nullptr) {
+  if (defer_nb) *defer_nb = 0;
   if (s.n_tokens == 0) return zero_f64(prob_sum, s.n_experts, st);
   const Layout L = layout(s);
   // the grouped GEMMs' split region is idle while routing: a large router's GEMM uses it
   return launch_route(s, x, w_router, lb, sb, idx, tw, prob_sum,
                       reinterpret_cast<double*>(at(ws, L.partials)),
                       reinterpret_cast<float*>(at(ws, L.logits)), reinterpret_cast<float*>(at(ws, L.split)),
-                      L.h_routed - L.split, st);
+                      L.h_routed - L.split, st, defer_nb);
 }
 
 int do_permute(const moe_shape& s, const int32_t* idx, const double* prob_sum, int32_t* counts,
                int32_t* offsets, int32_t* perm, int32_t* slot_pos, double* stat, void* ws,
-               hipStream_t st) {
+               hipStream_t st, int nb = 0, double* sum_out = nullptr) {
   const Layout L = layout(s);
   return launch_permute(s, idx, prob_sum, counts, offsets, perm, slot_pos, stat,
                         reinterpret_cast<int32_t*>(at(ws, L.hist)),
-                        reinterpret_cast<int32_t*>(at(ws, L.base)), st);
+                        reinterpret_cast<int32_t*>(at(ws, L.base)), st,
+                        nb > 0 ? reinterpret_cast<const double*>(at(ws, L.partials)) : nullptr, nb, sum_out);
 }
 
 // wq: expert weight format (0 bf16/fp32, 8 FP8 codes, 4 packed int4 codes; the last two with row scales)
@@ -418,11 +421,19 @@ static int forward_impl(const moe_shape* shape, const void* x, const void* w_rou
     if (stage_events && stage_events[i]) hipEventRecord(stage_events[i], stream);
   };
   mark(0);
-  if ((st = do_route(s, x, w_router, logit_bias, select_bias, topk_idx, topk_w, prob_sum, ws, stream)))
+  // The router's last step (adding its per-workgroup probability sums) rides in
+  // the permutation's column scan when that kernel runs (more than one chunk).
+  int pnb = 0;
+  if ((st = do_route(s, x, w_router, logit_bias, select_bias, topk_idx, topk_w, prob_sum, ws, stream, &pnb)))
+    return st;
+  const bool fold_in_scan = pnb > 0 && permute_chunks(s) > 1;
+  if (pnb > 0 && !fold_in_scan &&
+      (st = launch_prob_sum(reinterpret_cast<const double*>(at(ws, L.partials)), pnb, s.n_experts, prob_sum,
+                            stream)))
     return st;
   mark(1);
-  if ((st = do_permute(s, topk_idx, prob_sum, counts, offsets, perm, slot_pos, balance_stat, ws,
-                       stream)))
+  if ((st = do_permute(s, topk_idx, prob_sum, counts, offsets, perm, slot_pos, balance_stat, ws, stream,
+                       fold_in_scan ? pnb : 0, prob_sum)))
     return st;
   mark(2);
   const size_t NK = (size_t)s.n_tokens * s.top_k;

@@ -109,10 +109,28 @@ __device__ __forceinline__ void wait_vm_barrier_rt(int n) {
 }
 
 // ------------------------------------------------------------------ router
+
+// prob_sum[e] from the router's nb per-workgroup sums (rows of E doubles), by
+// one wavefront: lane-strided sums, then a fixed butterfly. The router's own
+// launch and the permute's column scan (which takes this step over when the
+// forward defers it) both use it, so prob_sum is the same bits either way.
+__device__ __forceinline__ double prob_sum_wave(const double* __restrict__ partials, int nb, int E, int e,
+                                                int lane) {
+  double a = 0.0;
+  for (int b = lane; b < nb; b += kWave) a += partials[(size_t)b * E + e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+  return a;
+}
 // `partials`: route_partials_bytes(s) bytes; `logits`: route_logits_floats(s) floats (workspace).
+// defer_nb != NULL: where the last step would be a launch of its own that adds
+// the per-workgroup sums into prob_sum, it is left out and *defer_nb is their
+// count (the partials rows), for the caller to take over (else *defer_nb = 0).
 int launch_route(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                  const float* select_bias, int32_t* topk_idx, float* topk_w, double* prob_sum,
-                 double* partials, float* logits, float* split_ws, size_t split_bytes, hipStream_t stream);
+                 double* partials, float* logits, float* split_ws, size_t split_bytes, hipStream_t stream,
+                 int* defer_nb = nullptr);
+int launch_prob_sum(const double* partials, int nb, int E, double* prob_sum, hipStream_t stream);
 int route_blocks(const moe_shape& s);
 size_t route_partials_bytes(const moe_shape& s);  // the partials region: route_blocks(s) x E doubles + a counter
 // Training-side statistics: z-loss (recomputes the logits), importance and its CV^2; any output may be NULL.
@@ -131,9 +149,13 @@ int launch_router_logits(const moe_shape& s, const void* x, const void* w_router
 
 // ------------------------------------------------------------------ permute
 int permute_chunks(const moe_shape& s);
+// partials, nb > 0: the router's deferred per-workgroup sums; the column scan
+// adds them into sum_out (the same E doubles as prob_sum) before the scatter
+// reads prob_sum. Needs more than one chunk (permute_chunks(s) > 1).
 int launch_permute(const moe_shape& s, const int32_t* topk_idx, const double* prob_sum,
                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
-                   double* balance_stat, int32_t* hist, int32_t* base, hipStream_t stream);
+                   double* balance_stat, int32_t* hist, int32_t* base, hipStream_t stream,
+                   const double* partials = nullptr, int nb = 0, double* sum_out = nullptr);
 
 // ------------------------------------------------------------------ grouped SwiGLU
 // One set of segments (the routed experts, or the shared experts).

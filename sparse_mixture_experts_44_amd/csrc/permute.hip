@@ -59,12 +59,20 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 }
 
 // One wavefront per expert: base[b][e] = sum_{b' < b} hist[b'][e]; counts[e] = total.
+// With the router's per-workgroup sums (partials, nb > 0) it also adds them
+// into prob_sum[e]: the router's last step, which the forward can defer to here.
 __global__ __launch_bounds__(256) void colscan_kernel(const int32_t* __restrict__ hist, int nchunks,
                                                       int E, int32_t* __restrict__ base,
-                                                      int32_t* __restrict__ counts) {
+                                                      int32_t* __restrict__ counts,
+                                                      const double* __restrict__ partials, int nb,
+                                                      double* __restrict__ prob_sum) {
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (e >= E) return;
+  if (nb > 0) {
+    const double a = prob_sum_wave(partials, nb, E, e, lane);
+    if (lane == 0) prob_sum[e] = a;
+  }
   int run = 0;
   for (int b0 = 0; b0 < nchunks; b0 += kWave) {
     const int b = b0 + lane;
@@ -215,7 +223,8 @@ int permute_chunks(const moe_shape& s) {
 
 int launch_permute(const moe_shape& s, const int32_t* topk_idx, const double* prob_sum,
                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_pos,
-                   double* balance_stat, int32_t* hist, int32_t* base, hipStream_t stream) {
+                   double* balance_stat, int32_t* hist, int32_t* base, hipStream_t stream,
+                   const double* partials, int nb, double* sum_out) {
   const int NK = s.n_tokens * s.top_k;
   const int nch = permute_chunks(s);
   const int C = s.capacity > 0 ? s.capacity : 0;
@@ -225,7 +234,8 @@ int launch_permute(const moe_shape& s, const int32_t* topk_idx, const double* pr
   } else {
     if (nch > 1) {
       hipLaunchKernelGGL(hist_kernel, dim3(nch), dim3(256), 0, stream, topk_idx, NK, E, hist);
-      hipLaunchKernelGGL(colscan_kernel, dim3((E + 3) / 4), dim3(256), 0, stream, hist, nch, E, base, counts);
+      hipLaunchKernelGGL(colscan_kernel, dim3((E + 3) / 4), dim3(256), 0, stream, hist, nch, E, base, counts,
+                         partials, nb, sum_out);
     }
     hipLaunchKernelGGL(scatter_kernel, dim3(nch), dim3(kScatterThreads), 0, stream, topk_idx, NK, E, C,
                        s.n_tokens, s.top_k, nch > 1 ? base : nullptr, counts, offsets, perm, slot_pos,

@@ -521,10 +521,7 @@ __global__ __launch_bounds__(kThreads) void prob_sum_kernel(const double* __rest
   const int e = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (e >= E) return;
-  double a = 0.0;
-  for (int b = lane; b < nb; b += kWave) a += partials[(size_t)b * E + e];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, kWave);
+  const double a = prob_sum_wave(partials, nb, E, e, lane);
   if (lane == 0) prob_sum[e] = a;
 }
 
@@ -789,9 +786,16 @@ void launch_route_fused_t(const moe_shape& s, const void* x, const void* w_route
                      s.n_experts, s.top_k, s.renormalize, topk_idx, topk_w, partials);
 }
 
+int launch_prob_sum(const double* partials, int nb, int E, double* prob_sum, hipStream_t stream) {
+  hipLaunchKernelGGL(prob_sum_kernel, dim3((E + 3) / 4), dim3(kThreads), 0, stream, partials, nb, E, prob_sum);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 int launch_route(const moe_shape& s, const void* x, const void* w_router, const float* logit_bias,
                  const float* select_bias, int32_t* topk_idx, float* topk_w, double* prob_sum,
-                 double* partials, float* logits, float* split_ws, size_t split_bytes, hipStream_t stream) {
+                 double* partials, float* logits, float* split_ws, size_t split_bytes, hipStream_t stream,
+                 int* defer_nb) {
+  if (defer_nb) *defer_nb = 0;
   if (route_fused(s)) {
     int nb = 0;
     if (s.n_experts <= 64)        // 128 tokens x 64 experts per workgroup
@@ -800,9 +804,11 @@ int launch_route(const moe_shape& s, const void* x, const void* w_router, const 
       launch_route_fused_t<2, 4, true>(s, x, w_router, logit_bias, select_bias, topk_idx, topk_w, partials, &nb, stream);
     else                          // 32 x 256
       launch_route_fused_t<1, 4, true>(s, x, w_router, logit_bias, select_bias, topk_idx, topk_w, partials, &nb, stream);
-    hipLaunchKernelGGL(prob_sum_kernel, dim3((s.n_experts + 3) / 4), dim3(kThreads), 0, stream, partials, nb,
-                       s.n_experts, prob_sum);
-    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    if (defer_nb) {
+      *defer_nb = nb;
+      return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    }
+    return launch_prob_sum(partials, nb, s.n_experts, prob_sum, stream);
   }
   const int nb = route_blocks(s);
   // the select kernel's counter sits after the workgroup sums; the VALU logits
@@ -820,10 +826,12 @@ int launch_route(const moe_shape& s, const void* x, const void* w_router, const 
   else if (el <= 4) MOE_SELECT(4);
   else MOE_SELECT(8);
 #undef MOE_SELECT
-  if (!done)
-    hipLaunchKernelGGL(prob_sum_kernel, dim3((s.n_experts + 3) / 4), dim3(kThreads), 0, stream, partials, nb,
-                       s.n_experts, prob_sum);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  if (done) return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  if (defer_nb) {
+    *defer_nb = nb;
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
+  return launch_prob_sum(partials, nb, s.n_experts, prob_sum, stream);
 }
 
 int launch_router_logits(const moe_shape& s, const void* x, const void* w_router, float* logits, int* splits,
