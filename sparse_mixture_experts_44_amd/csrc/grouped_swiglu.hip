@@ -447,14 +447,18 @@ __global__ __launch_bounds__(WGM * WGN * 64, MINB) void grouped_mfma_kernel(Grou
   constexpr int NB = P1 ? 2 * FN : FN;  // B fragments per k16 step
   constexpr int WAVES = WGM * WGN;
   constexpr int NT = WAVES * kWave;
-  constexpr int A_INS = BM / RPIA / WAVES;  // copy instructions per wave per stage
+  // copy instructions per wave per stage; with BM / RPIA not a multiple of the
+  // wave count the last waves have fewer A copies (a_act below never counts a
+  // copy past BM, since mvalid <= BM)
+  constexpr int A_INS = (BM / RPIA + WAVES - 1) / WAVES;
   constexpr int B_INS = BN / RPIB / WAVES;
   constexpr int L = A_INS + B_INS;          // vector-memory ops per wave per stage
   constexpr int STAGE_A = BM * ROWA, STAGE = STAGE_A + BN * ROWB;
   static_assert(WS ? (BK == 64 || BK == 128 || BK == 256) : (BK == 32 || BK == 64), "K step");
   constexpr int QB = BK / 64;  // int4: 64-code blocks (32 bytes) per B row per stage
   static_assert(A_INS >= 1 && B_INS >= 1 && FM >= 1 && FN >= 1 && NS >= 2 && NS <= 6, "tile shape");
-  static_assert(A_INS * RPIA * WAVES == BM && B_INS * RPIB * WAVES == BN, "copy slots cover the tile");
+  static_assert(BM % RPIA == 0 && A_INS * RPIA * WAVES >= BM && B_INS * RPIB * WAVES == BN,
+                "copy slots cover the tile");
   static_assert(!P1 || (BN / 2) % (RPIB * B_INS) == 0, "a wave's B rows come from one matrix");
   // N-major B: a 1 KB copy fills 1024 / (2 BN) k-rows
   constexpr int ROWBN = BN * 2;
@@ -909,6 +913,13 @@ int grid_for(long long ub, int per_cu) {
   return (int)((g + kXcds - 1) / kXcds * kXcds);
 }
 
+// A tile shape that can run gate|up: each wave takes whole 32-column blocks of
+// the tile's BN / 2 gate (and as many up) rows. Launchers instantiate the
+// gate|up kernels only for these (a class used only for the down projection
+// may be narrower).
+template <int BN, int WGN>
+constexpr bool kGateUpShape = BN / 2 / WGN >= 32;
+
 // per_cu: workgroups launched per CU at most. 1 is a persistent grid (each
 // workgroup walks the tile list with stride gridDim.x); a large value
 // launches about one workgroup per tile.
@@ -939,12 +950,15 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
     else
       hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, true>), dim3(grid),
                          dim3(WGM * WGN * 64), 0, st, p);
-  } else if (phase == 1 && save) {
-    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD, false, WQ == 0>),
-                       dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
   } else if (phase == 1) {
-    hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD>), dim3(grid),
-                       dim3(WGM * WGN * 64), 0, st, p);
+    if constexpr (kGateUpShape<BN, WGN>) {
+      if (save)
+        hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD, false, WQ == 0>),
+                           dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
+      else
+        hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, true, SPREAD>), dim3(grid),
+                           dim3(WGM * WGN * 64), 0, st, p);
+    }
   } else if (obf) {
     hipLaunchKernelGGL((grouped_mfma_kernel<BM, BN, BK, WGM, WGN, NS, MINB, WQ, false, SPREAD, false, false, WQ == 0>),
                        dim3(grid), dim3(WGM * WGN * 64), 0, st, p);
@@ -959,11 +973,14 @@ void launch_mfma(const GroupedParams& p, int phase, int per_cu, hipStream_t st) 
   if (p.split_ws && p.split_cap > kSplitHeader) {
     // one wave per workgroup; the tail holds fewer tiles than the grid has workgroups
     const dim3 fg(grid * WGM * WGN), fb(kWave);
-    if (phase == 1 && save)
-      hipLaunchKernelGGL((split_finish_kernel<BM, BN, WGM, WGN, WQ, true, WQ == 0>), fg, fb, 0, st, p);
-    else if (phase == 1)
-      hipLaunchKernelGGL((split_finish_kernel<BM, BN, WGM, WGN, WQ, true>), fg, fb, 0, st, p);
-    else if (obf)
+    if (phase == 1) {
+      if constexpr (kGateUpShape<BN, WGN>) {
+        if (save)
+          hipLaunchKernelGGL((split_finish_kernel<BM, BN, WGM, WGN, WQ, true, WQ == 0>), fg, fb, 0, st, p);
+        else
+          hipLaunchKernelGGL((split_finish_kernel<BM, BN, WGM, WGN, WQ, true>), fg, fb, 0, st, p);
+      }
+    } else if (obf)
       hipLaunchKernelGGL((split_finish_kernel<BM, BN, WGM, WGN, WQ, false, false, WQ == 0>), fg, fb, 0, st, p);
     else if (accum)
       hipLaunchKernelGGL((split_finish_kernel<BM, BN, WGM, WGN, WQ, false, false, false, WQ == 0>), fg, fb, 0, st,
@@ -985,6 +1002,9 @@ bool wide_gate_up(long long rows, int groups) {
   const long long m = rows / std::max(1, groups);
   return m >= 64 && m < 192;
 }
+
+// Segments that a capacity bounds at 65-160 rows fit one 160-row tile.
+bool one_tall_tile(int group_rows_max) { return group_rows_max > 64 && group_rows_max <= 160; }
 
 // Few, tall segments (bf16 layers): 320-row tiles when they need at least 20%
 // fewer m-tiles than 256-row ones. Tile time there scales with the tile count
@@ -1029,9 +1049,17 @@ void launch_class(const GroupedParams& p, int phase, hipStream_t stream) {
   } else if (WQ == 0 && phase == 2 && p.set[0].b_nmajor) {
     launch_mfma<64, 256, 64, 1, 4, 3, 0, false, 1, true>(p, 2, 1, stream);
   } else if (WQ == 0 && phase == 1 && !p.set[0].g_save && wide_gate_up(p.set[0].max_rows, p.set[0].n_groups)) {
-    // 64 x 512 tiles, 8 waves, two stages: half the tiles of 64 x 256 (half the x-row
-    // re-reads and per-tile starts); Switch-shaped capacity layer gate|up 0.38 -> 0.37 ms
-    launch_mfma<64, 512, 64, 1, 8, 2, 0, false>(p, phase, 1, stream);
+    if (one_tall_tile(p.set[0].group_rows_max)) {
+      // a capacity of 65-160 rows: one 160 x 512 tile per segment and weight tile,
+      // so each weight panel is read once (with 64-row tiles, up to three times);
+      // 32 K values per stage leave room for three stages. Switch-shaped capacity
+      // layer gate|up 0.366 -> 0.342 ms, the same bits
+      launch_mfma<160, 512, 32, 1, 8, 3, 0, false>(p, phase, 1, stream);
+    } else {
+      // 64 x 512 tiles, 8 waves, two stages: half the tiles of 64 x 256 (half the x-row
+      // re-reads and per-tile starts); Switch-shaped capacity layer gate|up 0.38 -> 0.37 ms
+      launch_mfma<64, 512, 64, 1, 8, 2, 0, false>(p, phase, 1, stream);
+    }
   } else if (WQ == 8 && phase == 1 && p.d_model % 128 == 0) {
     // FP8 gate|up: 128 K values per stage, whole 128-byte weight row pieces
     // (DeepSeek-shaped decode gate|up 0.221 -> 0.205 ms; the down projection's

@@ -456,6 +456,8 @@ static int forward_impl(const moe_shape* shape, const void* x, const void* w_rou
     R.n_groups = s.n_experts;
     R.rows_per_token = s.top_k;
     R.max_rows = (int32_t)NK;
+    // a token takes k distinct experts, so no expert gets more than N rows (C with a capacity)
+    R.group_rows_max = s.capacity > 0 ? std::min(s.capacity, s.n_tokens) : s.n_tokens;
     R.d_ff = s.d_ff;
     R.w_gate = w_gate;
     R.w_up = w_up;

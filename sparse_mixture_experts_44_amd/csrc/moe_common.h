@@ -166,6 +166,7 @@ struct SegSet {
   int32_t uniform_rows;
   int32_t rows_per_token;
   int32_t max_rows;        // rows at or past this are never computed
+  int32_t group_rows_max;  // a bound on every group's rows known on the host (a capacity), or 0
   int32_t d_ff;
   const void* w_gate;      // [G, d_ff, d]  (bf16, fp32, FP8 E4M3 codes, or [G, d_ff, d/2] packed int4)
   const void* w_up;        // [G, d_ff, d]

@@ -12,6 +12,7 @@ Small seeded layers, compared with the CPU oracle. Covered:
 * bitwise determinism across two runs;
 * a large router (N = 2048, E = 256, d = 1024) whose logits GEMM splits its K loops;
 * a top-1 layer of 4099 tokens (the combine's four-token workgroups, the last one partial);
+* capacities of 150 and 100 rows, whose gate|up runs one 160-row tile per expert;
 * a seeded random sweep of 16 small layers, every knob drawn at once (bf16 and fp32).
 * the staged entry points against moe_forward.
 """
@@ -61,6 +62,13 @@ CASES = {
     # and a capacity drops copies
     "top1_many": small("top1_many", n_tokens=4099, n_experts=16, top_k=1, d_model=128, d_ff=64,
                        capacity=300, logit_skew=1.0),
+    # a capacity of 65-160 rows with 64-191 mean rows per expert: gate|up on one 160-row tile per
+    # expert and weight tile. C = 150 (the last 32-row block ragged) with d_ff = 320 (the second
+    # 256-column n-tile partial); C = 100 (the tile's fifth block empty), skewed so most experts fill up
+    "cap150_tall": small("cap150_tall", n_tokens=2048, n_experts=16, top_k=1, d_model=256, d_ff=320,
+                         capacity=150, logit_skew=1.0),
+    "cap100_tall": small("cap100_tall", n_tokens=1200, n_experts=16, top_k=2, d_model=192, d_ff=256,
+                         capacity=100, logit_skew=1.5, n_shared=1, d_ff_shared=128),
 }
 
 
