@@ -105,14 +105,39 @@ def backward_work(cfg, kept):
       shared expert; the router: dW_r and dl W_r (4 N E d);
     * executed: moe_backward also recomputes G and U (4 d F per copy) and the
       router logits (2 N E d) instead of keeping them from the forward pass.
+
+    And the bytes it must move at least (bf16 layer):
+    * read: x, dy (fp32), W_r, the weights of every touched expert and of the
+      shared experts;
+    * written: dx (fp32), dW_r and the logit-bias gradient (fp32), and the
+      expert weight gradients: every expert's in fp32 when writing them (the
+      experts no copy reached get zeros), the touched and shared experts' read
+      and written back when accumulating, every expert's in bf16 for bf16
+      weight gradients.
     """
     import numpy as np
     d, F, E, N = cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.n_tokens
     S, Fs = cfg.n_shared, cfg.d_ff_shared
     n_kept = int(np.sum(kept))
+    touched = int(np.sum(np.asarray(kept) > 0))
     alg = 12 * d * F * n_kept + S * N * 12 * d * Fs + 4 * N * E * d
     exe = alg + 4 * d * F * n_kept + S * N * 4 * d * Fs + 2 * N * E * d
-    return dict(flops_algorithmic=alg, flops_executed=exe)
+    common = N * d * 2 + N * d * 4 + E * d * 2 + (touched * expert_params(d, F) + S * expert_params(d, Fs)) * 2 \
+        + N * d * 4 + E * d * 4 + E * 4
+    grads_all = E * expert_params(d, F) + S * expert_params(d, Fs)
+    grads_touched = touched * expert_params(d, F) + S * expert_params(d, Fs)
+    return dict(flops_algorithmic=alg, flops_executed=exe,
+                bytes_write=common + grads_all * 4, bytes_accumulate=common + grads_touched * 8,
+                bytes_bf16_weight_grads=common + grads_all * 2)
+
+
+def backward_roofline(flops, byts, ms):
+    """The roofline a backward time is closest to: MFMA (bf16 peak) or HBM, whichever takes longer at peak."""
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = byts / (PEAK_HBM_GBS * 1e9)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    return {"bound": bound, "frac": (t_mfma if bound == "mfma" else t_hbm) / (ms * 1e-3),
+            "mfma_frac": t_mfma / (ms * 1e-3), "hbm_frac": t_hbm / (ms * 1e-3)}
 
 
 def time_backward(L, xd, cfg, steps, warmup, kept):
@@ -150,8 +175,12 @@ def time_backward(L, xd, cfg, steps, warmup, kept):
     ms_saved = timed(False)
     w = backward_work(cfg, kept)
     tf = w["flops_algorithmic"] / (ms * 1e-3) / 1e12
+    fl = w["flops_algorithmic"]
     return {"ms": ms, "steps": steps, "tflops_algorithmic": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS,
             "tflops_executed": w["flops_executed"] / (ms * 1e-3) / 1e12, **w,
+            "roofline": {"write": backward_roofline(fl, w["bytes_write"], ms),
+                         "accumulate": backward_roofline(fl, w["bytes_accumulate"], ms_acc),
+                         "bf16_weight_grads": backward_roofline(fl, w["bytes_bf16_weight_grads"], ms_bf16)},
             "ms_accumulate": ms_acc, "ms_bf16_weight_grads": ms_bf16, "forward_train_ms": ms_fwd_train,
             "ms_with_saved_gate_up": ms_saved,
             "note": "moe_backward alone (gradients of x, W_r, logit bias, every expert weight), writing the "
