@@ -87,9 +87,14 @@ The near-tie gap of route() is the k-th minus the (k+1)-th largest selection
 score (with the selection bias), pinned by planted scores and by the set
 margin min(chosen) - max(others).
 
-Parity unpinned: y on general random inputs has no printed value on any page.
-It rests on the special cases above and on the per-token and grouped forms
-agreeing.
+No page prints a value of y. On general inputs (any E, k, capacity, both
+biases, shared experts) y is pinned by properties that hold for every input:
+it is the sum of its single-expert shares (the layer with every other
+expert's down projection zeroed, which leaves the routing as it is), each
+share being w times torch's dense SwiGLU FFN on the tokens whose kept copy
+chose that expert and zero elsewhere; it does not change when the experts
+are relabelled; and without a capacity its rows follow the token order.
+The per-token and grouped forms agree.
 """
 from __future__ import annotations
 

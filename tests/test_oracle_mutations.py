@@ -267,3 +267,44 @@ def test_band_one_sided_range_is_caught(monkeypatch):
         return b
     monkeypatch.setattr(O, "h_rounding_band", bad)
     _fails(pins.test_h_band_planted_midpoint)
+
+
+def test_weights_paired_with_wrong_slot_are_caught(monkeypatch):
+    orig = O.forward_per_token
+    monkeypatch.setattr(O, "forward_per_token",
+                        lambda x, idx, w, keep, *a, **kw: orig(x, idx, np.roll(w, 1, axis=1), keep, *a, **kw))
+    _fails(lambda: pins.test_y_superposition_over_experts(0, True, False))
+
+
+def test_dropped_copies_contributing_are_caught(monkeypatch):
+    orig = O.forward_per_token
+    monkeypatch.setattr(O, "forward_per_token",
+                        lambda x, idx, w, keep, *a, **kw: orig(x, idx, w, np.ones_like(keep), *a, **kw))
+    _fails(lambda: pins.test_y_superposition_over_experts(9, False, False))
+
+
+def test_expert_weights_off_by_one_are_caught(monkeypatch):
+    class Shift:
+        def __init__(self, a):
+            self.a = a
+
+        def __getitem__(self, e):
+            return self.a[(e + 1) % len(self.a)]
+
+        def __len__(self):
+            return len(self.a)
+
+    orig = O.forward_per_token
+    monkeypatch.setattr(O, "forward_per_token",
+                        lambda x, idx, w, keep, g, u, d, *a, **kw: orig(x, idx, w, keep, Shift(g), Shift(u), Shift(d),
+                                                                         *a, **kw))
+    _fails(lambda: pins.test_y_superposition_over_experts(0, True, False))
+    _fails(lambda: pins.test_y_invariant_under_expert_relabelling(0))
+
+
+def test_logit_bias_left_with_its_index_is_caught(monkeypatch):
+    # the logit bias applied by position after the experts were relabelled would break the invariance
+    orig = O.route
+    monkeypatch.setattr(O, "route", lambda x, W, k, logit_bias=None, select_bias=None, renormalize=True:
+                        orig(x, W, k, None if logit_bias is None else np.sort(logit_bias), select_bias, renormalize))
+    _fails(lambda: pins.test_y_invariant_under_expert_relabelling(0))

@@ -255,6 +255,87 @@ def test_single_copy_against_torch_expert():
         np.testing.assert_allclose(lr2.y[t], ref, rtol=1e-12, atol=1e-13)
 
 
+# y on general inputs: properties that hold for any input, and the single-expert case, which reduces to
+# torch's dense SwiGLU FFN
+
+def _general_layer(rng, N=37, d=24, f=40, E=7, k=3, S=1):
+    x = rng.standard_normal((N, d))
+    Wr = rng.standard_normal((E, d)) * 0.5
+    wg, wu, wd, shared = rand_layer(rng, E, d, f, S=S)
+    lb = rng.uniform(-0.3, 0.3, E)
+    sb = rng.uniform(-0.05, 0.05, E)
+    return x, Wr, wg, wu, wd, shared, lb, sb
+
+
+@pytest.mark.parametrize("C,renorm,round_h", [(0, True, False), (5, True, True), (9, False, False)])
+def test_y_superposition_over_experts(C, renorm, round_h):
+    # The routing does not read the down projections, so zeroing every expert's but e's keeps the
+    # routing and the dropped set, and leaves expert e's share of y: the shares sum to y less the
+    # shared experts. Without rounding of h, the share of e on token t is w[t, j] times torch's dense
+    # SwiGLU of expert e at x_t for the kept copy of t in slot j with idx[t, j] = e, and 0 when t has
+    # no kept copy on e.
+    rng = np.random.default_rng(31)
+    x, Wr, wg, wu, wd, shared, lb, sb = _general_layer(rng)
+    N, E, k = x.shape[0], Wr.shape[0], 3
+    kw = dict(logit_bias=lb, select_bias=sb, capacity=C, renormalize=renorm, round_h=round_h)
+    full = O.moe_layer(x, Wr, wg, wu, wd, k, shared=shared, **kw)
+    idx, w = full.routing.idx, full.routing.w
+    keep = (full.grouping.slot_pos >= 0).reshape(N, k)
+    if C:
+        assert (~keep).any(), "the capacity must drop copies"
+    total = O.moe_layer(x, Wr, wg, wu, np.zeros_like(wd), k, shared=shared, **kw).y  # the shared experts
+    for e in range(E):
+        wd_e = np.zeros_like(wd)
+        wd_e[e] = wd[e]
+        ye = O.moe_layer(x, Wr, wg, wu, wd_e, k, **kw).y
+        total = total + ye
+        if round_h:
+            continue
+        ffn = torch_swiglu(x, wg[e], wu[e], wd[e])
+        for t in range(N):
+            ref = sum(w[t, j] * ffn[t] for j in range(k) if idx[t, j] == e and keep[t, j])
+            if isinstance(ref, int):
+                assert np.all(ye[t] == 0.0)
+            else:
+                np.testing.assert_allclose(ye[t], ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(total, full.y, rtol=1e-12, atol=1e-12)
+    if shared is not None and not round_h:
+        dense = sum(torch_swiglu(x, shared[0][s], shared[1][s], shared[2][s]) for s in range(len(shared[0])))
+        np.testing.assert_allclose(O.moe_layer(x, Wr, wg, wu, np.zeros_like(wd), k, shared=shared, **kw).y, dense,
+                                   rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("C", [0, 6])
+def test_y_invariant_under_expert_relabelling(C):
+    # Relabel the experts (router rows, both biases and every expert weight, by one permutation): the
+    # scores move with their experts, so every token picks the same experts in the same slots, the same
+    # copies compete for capacity, and y and the statistic stay as they are; counts move with the labels.
+    rng = np.random.default_rng(32)
+    x, Wr, wg, wu, wd, shared, lb, sb = _general_layer(rng)
+    k = 3
+    a = O.moe_layer(x, Wr, wg, wu, wd, k, shared=shared, logit_bias=lb, select_bias=sb, capacity=C)
+    pi = rng.permutation(Wr.shape[0])
+    b = O.moe_layer(x, Wr[pi], wg[pi], wu[pi], wd[pi], k, shared=shared, logit_bias=lb[pi], select_bias=sb[pi],
+                    capacity=C)
+    np.testing.assert_array_equal(pi[b.routing.idx], a.routing.idx)
+    np.testing.assert_array_equal(b.grouping.counts, a.grouping.counts[pi])
+    np.testing.assert_allclose(b.y, a.y, rtol=1e-12, atol=1e-13)
+    assert abs(b.stat - a.stat) <= 1e-12 * abs(a.stat)
+
+
+def test_y_follows_token_order_without_capacity():
+    # Without a capacity each token's output depends on its own row alone: permuting the tokens
+    # permutes the rows of y (and of idx and w).
+    rng = np.random.default_rng(33)
+    x, Wr, wg, wu, wd, shared, lb, sb = _general_layer(rng)
+    k = 3
+    a = O.moe_layer(x, Wr, wg, wu, wd, k, shared=shared, logit_bias=lb, select_bias=sb)
+    sig = rng.permutation(x.shape[0])
+    b = O.moe_layer(x[sig], Wr, wg, wu, wd, k, shared=shared, logit_bias=lb, select_bias=sb)
+    np.testing.assert_array_equal(b.routing.idx, a.routing.idx[sig])
+    np.testing.assert_allclose(b.y, a.y[sig], rtol=1e-12, atol=1e-13)
+
+
 def test_naive_equals_grouped_page_shape():
     g = read_golden("naive_vs_grouped.txt")
     cfg = mi.CONFIGS["p2_shape"]
