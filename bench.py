@@ -341,6 +341,67 @@ def cpu_baseline(cfg, layer, x, budget_s=20.0, weights="bf16"):
                       f"grouped fp64 experts+combine, {dt:.1f} s"}
 
 
+def library_reference(cfg, kept, ours_ms, dev, reps=5):
+    """The grouped forward as a per-expert loop of vendor GEMMs, for context beside our kernels.
+
+    The pages' grouped form runs one dense product per expert over that
+    expert's rows. Here each product is torch.mm (hipBLASLt on this GPU) on
+    bf16 operands of the layer's shapes and value scale (rows ~ N(0, 1),
+    weights ~ N(0, 1/K)), one weight matrix per segment, over the same segment
+    sizes as the layer's last forward (kept rows per routed expert, then the
+    shared experts' N rows). The gather of x, the SwiGLU and the combine are
+    left out, which favours the loop. The same phases as one dense GEMM over
+    all rows with a single weight give the library's own rate on this data.
+    """
+    import numpy as np
+    import torch
+
+    d, F, Fs = cfg.d_model, cfg.d_ff, cfg.d_ff_shared or cfg.d_ff
+    segs = [(int(r), F) for r in kept if r > 0] + [(cfg.n_tokens, Fs)] * cfg.n_shared
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    bf = torch.bfloat16
+
+    def rnd(*shape, scale=1.0):
+        return torch.randn(*shape, device=dev, dtype=bf, generator=g) * scale
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    out = {"kind": "per-expert loop of torch.mm (hipBLASLt) over the layer's segments; random bf16 operands of "
+                   "the same shapes and scale; gather, SwiGLU and combine not included",
+           "segments": len(segs)}
+    for phase, name in ((1, "gate_up"), (2, "down")):
+        if phase == 1:
+            ops = [(rnd(r, d), rnd(d, 2 * f, scale=d ** -0.5)) for r, f in segs]
+        else:
+            ops = [(rnd(r, f), rnd(f, d, scale=f ** -0.5)) for r, f in segs]
+        ms = timed(lambda: [torch.mm(a, w) for a, w in ops])
+        flops = sum(2 * a.shape[0] * a.shape[1] * w.shape[1] for a, w in ops)
+        rows = sum(a.shape[0] for a, _ in ops)
+        a_all, w0 = rnd(rows, ops[0][0].shape[1]), ops[0][1]
+        del ops
+        dense_ms = timed(lambda: torch.mm(a_all, w0))
+        dense_flops = 2 * rows * a_all.shape[1] * w0.shape[1]
+        del a_all, w0
+        torch.cuda.empty_cache()
+        out[name] = {"loop_ms": ms, "loop_tflops": flops / ms / 1e9, "ours_ms": ours_ms[name],
+                     "ours_speedup": ms / ours_ms[name], "dense_one_weight_ms": dense_ms,
+                     "dense_one_weight_tflops": dense_flops / dense_ms / 1e9,
+                     "dense_one_weight_frac": dense_flops / dense_ms / 1e9 / PEAK_BF16_TFLOPS}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +417,8 @@ def main():
                     help="skip timing moe_backward and the training forward (bf16 workloads; reported as "
                          "backward, outside the headline value)")
     ap.add_argument("--backward", dest="backward", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--no-library-reference", dest="library_reference", action="store_false",
+                    help="skip the per-expert vendor-GEMM loop timed for context (bf16 workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -477,6 +540,11 @@ def main():
                   "touched_experts": work["touched"], "kept_copies": work["kept"],
                   "balance_stat": float(L.out.balance_stat.item()), "cold": cold},
     }
+    if args.library_reference and weights == "bf16" and cfg.dtype == "bf16":
+        try:
+            out["library_reference"] = library_reference(cfg, kept, avg, dev)
+        except Exception as e:  # context only: never hides the forward line
+            out["library_reference"] = {"error": f"{type(e).__name__}: {e}"}
     if args.backward and weights == "bf16":
         try:
             out["backward"] = time_backward(L, xd, cfg, K, args.warmup, kept)
