@@ -182,7 +182,11 @@ int moe_combine(const moe_shape* shape, const float* expert_out, const int32_t* 
  * stage_events: NULL, or MOE_STAGE_EVENTS events created by the caller. It
  * records event i before stage i (route, permute, gate|up, down, combine)
  * and the last event after combine, all on `stream`. A NULL entry is
- * skipped (each recorded event costs the stream a few microseconds). */
+ * skipped (each recorded event costs the stream a few microseconds).
+ * The call may be captured in a HIP graph (stage_events NULL): it issues
+ * kernels only, with no memset or copy nodes, every kernel writing what a
+ * later one reads, so each replay gives the eager call's results bit for
+ * bit while ws and the buffers stay allocated. */
 int moe_forward(const moe_shape* shape, const void* x, const void* w_router,
                 const float* logit_bias, const float* select_bias,
                 const void* w_gate, const void* w_up, const void* w_down,
