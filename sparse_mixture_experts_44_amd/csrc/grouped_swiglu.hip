@@ -1023,14 +1023,16 @@ bool tall_tiles(long long rows, int groups) {
 template <int WQ>
 void launch_class(const GroupedParams& p, int phase, hipStream_t stream) {
   if constexpr (WQ == 4) {
-    // int4 weights (a decode format). Gate|up (K = d, a multiple of 256): 32 x 256
-    // tiles with 256 K values per stage, so that each weight row piece a copy
-    // fetches is a whole 128-byte line (a quarter of the L2 requests of 32-byte
-    // pieces): DeepSeek-shaped decode gate|up 0.157 -> 0.142 ms. Down (K = d_ff,
-    // 2048 on that layer: few K steps per tile) and other K: 64 x 256 tiles,
-    // 64 K values per stage, two workgroups per CU.
+    // int4 weights (a decode format). Gate|up (K = d, a multiple of 256): 32 x 512
+    // tiles, 8 waves, 128 K values per stage, three stages (40 KB each). Each
+    // weight row piece a copy fetches is 64 bytes (32 at 64 K values per stage),
+    // and each token row is read once per 256 columns of h instead of 128: at 4
+    // bits per weight the activation rows are a large share of a tile's copies.
+    // DeepSeek-shaped decode gate|up 0.157 ms (64 x 256, 64-K stages) -> 0.142 ms
+    // (32 x 256, 256-K stages) -> 0.133 ms. Down (K = d_ff, 2048 on that layer: few K steps per tile) and
+    // other K: 64 x 256 tiles, 64 K values per stage, two workgroups per CU.
     if (phase == 1 && p.d_model % 256 == 0)
-      launch_mfma<32, 256, 256, 1, 4, 3, 4, false, 1>(p, phase, 1, stream);
+      launch_mfma<32, 512, 128, 1, 8, 3, 4, false, 1>(p, phase, 1, stream);
     else
       launch_mfma<64, 256, 64, 1, 4, 4, 4, false, 2>(p, phase, 2, stream);
   } else if (large_tiles(p.set[0].max_rows, p.set[0].n_groups)) {

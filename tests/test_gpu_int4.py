@@ -114,7 +114,7 @@ def test_int4_small_layers_every_row(kw):
     check_int4(cfg, layer, x, gpu, np.arange(cfg.n_tokens))
 
 
-@pytest.mark.parametrize("d", [128, 512])             # d = 512: gate|up on 32-row tiles with 256-K stages
+@pytest.mark.parametrize("d", [128, 512])             # d = 512: gate|up on 32 x 512 tiles with 128-K stages
 @pytest.mark.parametrize("extra_ws", [0, 64 << 20])   # with room past h, the tail tiles split along K
 @pytest.mark.parametrize("sizes", [
     [0, 1, 255, 256, 257, 0, 513, 2, 300],
